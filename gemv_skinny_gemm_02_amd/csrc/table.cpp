@@ -1,0 +1,336 @@
+// table.cpp -- table file parsing, identity checks, refusals and defaults.
+// Host-only C++ (no HIP calls).
+#include "table.hpp"
+
+#include <cctype>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+#include <sstream>
+
+#include "variants.hpp"
+
+namespace skg {
+
+// ------------------------------------------------------------ a small JSON
+// reader: objects, arrays, strings (with simple escapes), numbers, literals.
+namespace {
+
+struct JVal {
+  enum Kind { NUL, BOOL, NUM, STR, ARR, OBJ } kind = NUL;
+  bool b = false;
+  double num = 0;
+  std::string str;
+  std::vector<JVal> arr;
+  std::vector<std::pair<std::string, JVal>> obj;
+  const JVal* get(const char* key) const {
+    if (kind != OBJ) return nullptr;
+    for (const auto& kv : obj)
+      if (kv.first == key) return &kv.second;
+    return nullptr;
+  }
+};
+
+class JParser {
+ public:
+  explicit JParser(const std::string& s) : s_(s) {}
+  bool parse(JVal* out, std::string* err) {
+    if (!value(out, 0)) {
+      *err = "malformed JSON near byte " + std::to_string(pos_);
+      return false;
+    }
+    ws();
+    if (pos_ != s_.size()) {
+      *err = "trailing bytes after JSON value at byte " + std::to_string(pos_);
+      return false;
+    }
+    return true;
+  }
+
+ private:
+  const std::string& s_;
+  size_t pos_ = 0;
+  void ws() {
+    while (pos_ < s_.size() && std::isspace(static_cast<unsigned char>(s_[pos_]))) ++pos_;
+  }
+  bool lit(const char* t) {
+    const size_t n = std::strlen(t);
+    if (s_.compare(pos_, n, t) != 0) return false;
+    pos_ += n;
+    return true;
+  }
+  bool string(std::string* out) {
+    if (pos_ >= s_.size() || s_[pos_] != '"') return false;
+    ++pos_;
+    while (pos_ < s_.size() && s_[pos_] != '"') {
+      char c = s_[pos_++];
+      if (c == '\\') {
+        if (pos_ >= s_.size()) return false;
+        const char e = s_[pos_++];
+        switch (e) {
+          case '"': c = '"'; break;
+          case '\\': c = '\\'; break;
+          case '/': c = '/'; break;
+          case 'n': c = '\n'; break;
+          case 't': c = '\t'; break;
+          case 'r': c = '\r'; break;
+          case 'b': c = '\b'; break;
+          case 'f': c = '\f'; break;
+          case 'u': {  // keep ASCII only; others become '?'
+            if (pos_ + 4 > s_.size()) return false;
+            const unsigned long cp = std::strtoul(s_.substr(pos_, 4).c_str(), nullptr, 16);
+            pos_ += 4;
+            c = cp < 128 ? static_cast<char>(cp) : '?';
+            break;
+          }
+          default: return false;
+        }
+      }
+      out->push_back(c);
+    }
+    if (pos_ >= s_.size()) return false;
+    ++pos_;
+    return true;
+  }
+  bool value(JVal* v, int depth) {
+    if (depth > 64) return false;
+    ws();
+    if (pos_ >= s_.size()) return false;
+    const char c = s_[pos_];
+    if (c == '{') {
+      v->kind = JVal::OBJ;
+      ++pos_;
+      ws();
+      if (pos_ < s_.size() && s_[pos_] == '}') { ++pos_; return true; }
+      for (;;) {
+        ws();
+        std::string key;
+        if (!string(&key)) return false;
+        ws();
+        if (pos_ >= s_.size() || s_[pos_] != ':') return false;
+        ++pos_;
+        JVal child;
+        if (!value(&child, depth + 1)) return false;
+        v->obj.emplace_back(std::move(key), std::move(child));
+        ws();
+        if (pos_ < s_.size() && s_[pos_] == ',') { ++pos_; continue; }
+        if (pos_ < s_.size() && s_[pos_] == '}') { ++pos_; return true; }
+        return false;
+      }
+    }
+    if (c == '[') {
+      v->kind = JVal::ARR;
+      ++pos_;
+      ws();
+      if (pos_ < s_.size() && s_[pos_] == ']') { ++pos_; return true; }
+      for (;;) {
+        JVal child;
+        if (!value(&child, depth + 1)) return false;
+        v->arr.push_back(std::move(child));
+        ws();
+        if (pos_ < s_.size() && s_[pos_] == ',') { ++pos_; continue; }
+        if (pos_ < s_.size() && s_[pos_] == ']') { ++pos_; return true; }
+        return false;
+      }
+    }
+    if (c == '"') { v->kind = JVal::STR; return string(&v->str); }
+    if (lit("true")) { v->kind = JVal::BOOL; v->b = true; return true; }
+    if (lit("false")) { v->kind = JVal::BOOL; v->b = false; return true; }
+    if (lit("null")) { v->kind = JVal::NUL; return true; }
+    if (c == '-' || std::isdigit(static_cast<unsigned char>(c))) {
+      const char* start = s_.c_str() + pos_;
+      char* end = nullptr;
+      v->num = std::strtod(start, &end);
+      if (end == start) return false;
+      v->kind = JVal::NUM;
+      pos_ += static_cast<size_t>(end - start);
+      return true;
+    }
+    return false;
+  }
+};
+
+bool as_int(const JVal* v, int* out) {
+  if (!v || v->kind != JVal::NUM) return false;
+  const double d = v->num;
+  if (d < -2147483648.0 || d > 2147483647.0 || static_cast<double>(static_cast<int>(d)) != d) return false;
+  *out = static_cast<int>(d);
+  return true;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ identity
+std::string Identity::str() const {
+  return "arch=" + arch + ";hip=" + hip + ";cc=" + cc + ";space=" + space;
+}
+
+bool Identity::parse(const std::string& s, Identity* out) {
+  Identity id;
+  std::stringstream ss(s);
+  std::string item;
+  int seen = 0;
+  while (std::getline(ss, item, ';')) {
+    const size_t eq = item.find('=');
+    if (eq == std::string::npos) return false;
+    const std::string k = item.substr(0, eq), v = item.substr(eq + 1);
+    if (k == "arch") { id.arch = v; seen |= 1; }
+    else if (k == "hip") { id.hip = v; seen |= 2; }
+    else if (k == "cc") { id.cc = v; seen |= 4; }
+    else if (k == "space") { id.space = v; seen |= 8; }
+    else return false;
+  }
+  if (seen != 15) return false;
+  *out = id;
+  return true;
+}
+
+// ----------------------------------------------------------------- names
+const char* op_name(int op) {
+  switch (op) {
+    case OP_BF16: return "bf16";
+    case OP_GATED: return "gated";
+    case OP_FP8T: return "fp8_tensor";
+    case OP_A8W8: return "a8w8_block";
+    default: return nullptr;
+  }
+}
+int op_from_name(const std::string& s) {
+  for (int op = 0; op < NUM_OPS; ++op)
+    if (s == op_name(op)) return op;
+  return -1;
+}
+int variant_from_name(const std::string& s) {
+  for (int i = 0; i < kNumVariants; ++i)
+    if (s == kVariants[i].name) return i;
+  return -1;
+}
+
+int forced_variant() {
+  const char* f = std::getenv("SKINNY_GEMM_FORCE");
+  if (!f || !*f) return -1;
+  return variant_from_name(f);
+}
+
+// ------------------------------------------------------------------ table
+void Table::clear() {
+  map_.clear();
+  engaged_ = false;
+  status_ = "none";
+}
+
+int Table::lookup(int op, int bucket, int N, int K) const {
+  if (!engaged_) return -1;
+  const auto it = map_.find(std::make_tuple(op, bucket, N, K));
+  return it == map_.end() ? -1 : it->second;
+}
+
+int Table::load(const std::string& path, const Identity& self, std::string* err) {
+  clear();
+  std::ifstream f(path, std::ios::binary);
+  if (!f) {
+    *err = "cannot read table " + path;
+    status_ = "none (" + *err + ")";
+    return -1;
+  }
+  std::stringstream buf;
+  buf << f.rdbuf();
+  const std::string text = buf.str();
+  JVal root;
+  if (!JParser(text).parse(&root, err) || root.kind != JVal::OBJ) {
+    if (err->empty()) *err = "table is not a JSON object";
+    *err = path + ": " + *err;
+    status_ = "none (" + *err + ")";
+    return -1;
+  }
+  auto refuse = [&](const std::string& why) {
+    status_ = "refused " + path + ": " + why;
+    std::fprintf(stderr, "skinny_gemm: table %s refused: %s; built-in defaults stay in effect\n",
+                 path.c_str(), why.c_str());
+    return 0;
+  };
+
+  const JVal* id = root.get("identity");
+  if (!id || id->kind != JVal::OBJ) return refuse("no identity header");
+  auto field = [&](const char* k) -> std::string {
+    const JVal* v = id->get(k);
+    return (v && v->kind == JVal::STR) ? v->str : std::string();
+  };
+  const std::string t_arch = field("arch"), t_hip = field("hip"), t_cc = field("cc"), t_space = field("space");
+  if (t_space.empty())
+    return refuse("made before the kernel selection space was tracked - the kernels have changed since: "
+                  "run the tuner again");
+  if (t_space != self.space)
+    return refuse("made for kernel selection space " + t_space + ", this build is " + self.space +
+                  " (the kernels changed): run the tuner again");
+  if (t_arch != self.arch) return refuse("made for " + t_arch + ", this device is " + self.arch);
+  if (t_hip != self.hip)
+    return refuse("tuned on HIP runtime " + t_hip + ", this process loaded " + self.hip +
+                  ": tune and run with the same runtime");
+  if (t_cc != self.cc) return refuse("built by compiler " + t_cc + ", this build is " + self.cc);
+  if (const char* f = std::getenv("SKINNY_GEMM_FORCE"); f && *f)
+    return refuse(std::string("SKINNY_GEMM_FORCE=") + f +
+                  " reroutes the dispatch away from what the table measured");
+
+  const JVal* entries = root.get("entries");
+  if (!entries || entries->kind != JVal::ARR) return refuse("no entries list");
+  std::map<std::tuple<int, int, int, int>, int> map;
+  for (size_t i = 0; i < entries->arr.size(); ++i) {
+    const JVal& e = entries->arr[i];
+    const std::string where = "entry " + std::to_string(i);
+    const JVal* opv = e.get("op");
+    const JVal* ch = e.get("choice");
+    int rows = 0, N = 0, K = 0;
+    if (!opv || opv->kind != JVal::STR || !ch || ch->kind != JVal::STR || !as_int(e.get("rows"), &rows) ||
+        !as_int(e.get("N"), &N) || !as_int(e.get("K"), &K))
+      return refuse(where + " lacks op/rows/N/K/choice");
+    const int op = op_from_name(opv->str);
+    if (op < 0) return refuse(where + " names unknown op '" + opv->str + "'");
+    if (bucket_of(rows) != rows) return refuse(where + ": rows " + std::to_string(rows) + " is not a rows bucket");
+    if (N <= 0 || K <= 0) return refuse(where + ": N and K must be positive");
+    const int v = variant_from_name(ch->str);
+    if (v < 0) return refuse(where + " names variant '" + ch->str + "' that this build does not compile");
+    if (!variant_supports(op, v, rows))
+      return refuse(where + ": variant '" + ch->str + "' is not compiled for " + opv->str + " at rows " +
+                    std::to_string(rows));
+    const auto key = std::make_tuple(op, rows, N, K);
+    if (map.count(key)) return refuse(where + " duplicates an earlier key");
+    map[key] = v;
+  }
+  map_ = std::move(map);
+  engaged_ = true;
+  status_ = "engaged " + std::to_string(map_.size()) + " shapes from " + path + " (" + self.arch +
+            ", runtime " + self.hip + ")";
+  std::fprintf(stderr, "skinny_gemm: table engaged: %zu shapes from %s (%s, runtime %s)\n", map_.size(),
+               path.c_str(), self.arch.c_str(), self.hip.c_str());
+  return 0;
+}
+
+// --------------------------------------------------------------- defaults
+// The untuned entry point: the VALU weight stream below 16 rows, the MFMA
+// tile path from 16 rows, with a shape rule for each.
+int default_variant(int op, int M, int N, int K) {
+  (void)K;
+  const char* name;
+  if (M < 16) {
+    const bool small_n = N <= 2048;
+    if (op == OP_GATED) name = M <= 4 ? "gemv_r1_k4_u2" : "gemv_r2_k4_u1";
+    else if (M <= 2) name = small_n ? "gemv_r1_k4_u2" : "gemv_r2_k4_u2";
+    else if (M <= 8) name = small_n ? "gemv_r2_k4_u2" : "gemv_r4_k4_u1";
+    else name = "gemv_r4_k4_u1";
+  } else {
+    name = (M <= 32) ? "tile_f1_k4_u2" : "tile_f1_k4_u2";
+  }
+  int v = variant_from_name(name);
+  if (v >= 0 && variant_supports(op, v, M)) return v;
+  // first compiled variant of the right family that supports M
+  const int fam = M < 16 ? FAM_GEMV : FAM_TILE;
+  for (int i = 0; i < kNumVariants; ++i)
+    if (kVariants[i].family == fam && variant_supports(op, i, M)) return i;
+  for (int i = 0; i < kNumVariants; ++i)
+    if (variant_supports(op, i, M)) return i;
+  return -1;
+}
+
+}  // namespace skg

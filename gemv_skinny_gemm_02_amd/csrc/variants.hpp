@@ -1,0 +1,126 @@
+// variants.hpp -- compile-time facts about the variant list, shared by the
+// kernels (device) and the dispatch/table code (host).  No HIP dependencies.
+#pragma once
+
+#include <cstdint>
+
+namespace skg {
+
+enum Op : int { OP_BF16 = 0, OP_GATED = 1, OP_FP8T = 2, OP_A8W8 = 3, NUM_OPS = 4 };
+enum Family : int { FAM_GEMV = 0, FAM_TILE = 1 };
+
+// Rows buckets: M is rounded up to the next one (padded-M lookup with no
+// nearest fallback: DeepSeek-V4-flash decode round 3, "Retained change 2";
+// rows 3, 6 and 12 as in mstar PR #1102, "What changed").
+constexpr int kBuckets[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 64, 96, 128};
+constexpr int kNumBuckets = sizeof(kBuckets) / sizeof(kBuckets[0]);
+constexpr int kMaxBucket = 128;
+
+// The GEMV path is compiled for each rows bucket up to 16 (MT = bucket).
+constexpr int kGemvMT[] = {1, 2, 3, 4, 6, 8, 12, 16};
+constexpr int kNumGemvMT = sizeof(kGemvMT) / sizeof(kGemvMT[0]);
+constexpr int kGemvMaxM = 16;
+// The tile path is compiled for 1, 2, 4, 6 and 8 fragments of 16 rows.
+constexpr int kTileFM[] = {1, 2, 4, 6, 8};
+constexpr int kNumTileFM = sizeof(kTileFM) / sizeof(kTileFM[0]);
+
+constexpr int bucket_of(int M) {
+  for (int b : kBuckets)
+    if (M <= b) return b;
+  return 0;  // above the largest bucket
+}
+constexpr int gemv_mt_index(int M) {
+  for (int i = 0; i < kNumGemvMT; ++i)
+    if (M <= kGemvMT[i]) return i;
+  return -1;
+}
+constexpr int tile_fm_index(int M) {  // M rows in one launch row (<= 128)
+  const int f = (M + 15) / 16;
+  for (int i = 0; i < kNumTileFM; ++i)
+    if (f <= kTileFM[i]) return i;
+  return kNumTileFM - 1;
+}
+
+constexpr int op_groups(int op) { return op == OP_GATED ? 2 : 1; }
+constexpr bool op_w_fp8(int op) { return op == OP_FP8T || op == OP_A8W8; }
+constexpr bool op_x_fp8(int op) { return op == OP_A8W8; }
+constexpr int op_w_bytes(int op) { return op_w_fp8(op) ? 1 : 2; }
+constexpr int op_x_bytes(int op) { return op_x_fp8(op) ? 1 : 2; }
+// K elements in one 16-byte weight load of one lane.
+constexpr int op_kc(int op) { return op_w_fp8(op) ? 16 : 8; }
+// dwords of x that pair with one lane's 16-byte weight chunk, per row of x.
+constexpr int op_xd(int op) { return op_kc(op) * op_x_bytes(op) / 4; }
+// K multiple the op requires (one 16-byte load per lane never straddles K).
+constexpr int op_k_multiple(int op) { return op_kc(op); }
+
+// Register budgets that keep a variant compiled for a bucket (per lane).
+constexpr bool gemv_valid(int op, int MT, int R, int KS, int U) {
+  const int G = op_groups(op);
+  return (KS == 1 || KS == 2 || KS == 4) && MT * R * G <= 64 && U * R * G * 4 <= 32 &&
+         U * MT * op_xd(op) <= 96 && (128 % ((4 / KS) * R)) == 0;
+}
+constexpr int tile_red_bytes(int op, int FM, int FN, int KS) {
+  return (4 / KS) * (KS - 1) * op_groups(op) * FN * FM * 4 * 64 * 4;
+}
+constexpr bool tile_valid(int op, int FM, int FN, int KS, int U) {
+  const int G = op_groups(op);
+  return (KS == 1 || KS == 2 || KS == 4) && G * FN * FM * 4 <= 128 &&
+         tile_red_bytes(op, FM, FN, KS) <= 65536 && U >= 1 &&
+         (128 % ((4 / KS) * FN * 16)) == 0;
+}
+
+struct VariantDesc {
+  const char* name;
+  int family;
+  int p0, p1, p2;  // GEMV: R, KS, U.  TILE: FN, KS, U.
+};
+
+constexpr VariantDesc kVariants[] = {
+#define SKG_GEMV(name, R, KS, U) {#name, FAM_GEMV, R, KS, U},
+#define SKG_TILE(name, FN, KS, U) {#name, FAM_TILE, FN, KS, U},
+#include "variants.def"
+#undef SKG_GEMV
+#undef SKG_TILE
+};
+constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+
+constexpr int count_family(int fam) {
+  int n = 0;
+  for (const auto& v : kVariants) n += v.family == fam;
+  return n;
+}
+constexpr int kNumGemv = count_family(FAM_GEMV);
+constexpr int kNumTile = count_family(FAM_TILE);
+// index of variant i inside its family's launch table
+constexpr int family_index(int i) {
+  int n = 0;
+  for (int j = 0; j < i; ++j) n += kVariants[j].family == kVariants[i].family;
+  return n;
+}
+
+// Whether variant i of op can run M rows (M >= 1).
+constexpr bool variant_supports(int op, int i, int M) {
+  const VariantDesc& v = kVariants[i];
+  if (v.family == FAM_GEMV) {
+    const int mi = gemv_mt_index(M);
+    return mi >= 0 && gemv_valid(op, kGemvMT[mi], v.p0, v.p1, v.p2);
+  }
+  const int fm = M > kMaxBucket ? kNumTileFM - 1 : tile_fm_index(M);
+  return tile_valid(op, kTileFM[fm], v.p0, v.p1, v.p2);
+}
+
+// FNV-1a over the list's text: the kernel-selection-space token.
+constexpr uint32_t fnv1a(const char* s, uint32_t h = 2166136261u) {
+  return *s ? fnv1a(s + 1, (h ^ static_cast<uint8_t>(*s)) * 16777619u) : h;
+}
+constexpr const char kSpaceText[] =
+    "buckets=1,2,3,4,6,8,12,16,24,32,64,96,128;gemv_mt=1,2,3,4,6,8,12,16;tile_fm=1,2,4,6,8;"
+#define SKG_GEMV(name, R, KS, U) "G:" #name "," #R "," #KS "," #U ";"
+#define SKG_TILE(name, FN, KS, U) "T:" #name "," #FN "," #KS "," #U ";"
+#include "variants.def"
+#undef SKG_GEMV
+#undef SKG_TILE
+    "kernels=2";  // bump when a kernel's arithmetic or indexing changes
+constexpr uint32_t kSpaceToken = fnv1a(kSpaceText);
+
+}  // namespace skg

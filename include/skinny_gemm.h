@@ -1,0 +1,148 @@
+/*
+ * skinny_gemm.h -- C ABI of the MI355X (gfx950) skinny decode-linear library.
+ *
+ * The operation is the decode-shaped linear
+ *
+ *     y[M, N] = x[M, K] . W[N, K]^T        (M = 1..128 rows, large N and K)
+ *
+ * in the four forms that the decode-linear pages route and tune:
+ *
+ *   skinny_gemm_bf16        bf16 x, bf16 W                     (mstar PR #1104,
+ *                           "Why": decode linears served by skinny GEMM / GEMV)
+ *   skinny_gemm_gated       fused gate/up: silu(x Wg^T) * (x Wu^T)
+ *                           (mstar PR #1104, "Why": decode_gemv_silu_mul, and
+ *                           "What changed": the gate/up's own gated1- entry)
+ *   skinny_gemm_fp8_tensor  bf16 x, fp8 W with one scale for the whole weight
+ *                           (mstar PR #1102, "What changed": the fp8 draft head)
+ *   skinny_gemm_a8w8_block  fp8 x with one scale per row per 128 K-columns, fp8
+ *                           W with one scale per 128 x 128 block (DeepSeek-V4-
+ *                           flash decode round 3, "Retained change 2")
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every tensor argument is a DEVICE pointer to caller-owned memory,
+ *           contiguous and row-major.  bf16 is passed as its 16-bit pattern,
+ *           fp8 as OCP e4m3fn bytes (1 sign, 4 exponent with bias 7, 3 fraction
+ *           bits; largest finite 448; 0x7F/0xFF are NaN), scales as float32.
+ *           x and W must be 16-byte aligned.  y must not overlap any input.
+ *           The library never frees, syncs on or reads caller memory from the
+ *           host; every call is ordered on `stream` (NULL = the null stream).
+ * Sizes.    M, N, K >= 0.  M == 0 or N == 0 is a no-op that returns OK.
+ *           K == 0 writes y = 0 (the empty sum).  K must be a multiple of 8 for
+ *           bf16 weights and of 16 for fp8 weights (one 16-byte load per lane).
+ * Result.   y[M, N] bf16, each element rounded once (round-to-nearest-even)
+ *           from a float32 accumulation.  The same call with the same inputs and
+ *           the same dispatch table gives the same bits every time: reductions
+ *           run in a fixed order and no atomics are used.
+ * Errors.   A status code; nothing is thrown across the ABI.  Arguments are
+ *           checked on the host before any launch.  skinny_gemm_last_error()
+ *           returns the calling thread's text for its last non-OK status.  A
+ *           fault inside a kernel surfaces at the caller's next synchronisation.
+ * Dispatch. Each call rounds M up to its rows bucket {1,2,3,4,6,8,12,16,24,32,
+ *           64,96,128} and looks (op, bucket, N, K) up in the per-device table
+ *           (DeepSeek-V4-flash decode round 3, "Retained change 2": padded-M
+ *           lookup with no nearest fallback; mstar PR #1104, "What changed": one
+ *           per-device table).  A miss, an absent table or a refused table uses
+ *           the built-in default for the op and bucket.  M above 128 uses the
+ *           MFMA tile path in chunks of 128 rows.
+ * Threads.  GEMM calls are reentrant.  skinny_gemm_load_table must not run
+ *           concurrently with other calls.
+ */
+#ifndef SKINNY_GEMM_H
+#define SKINNY_GEMM_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int skg_status;
+#define SKG_OK 0
+#define SKG_EINVAL 1        /* null pointer, negative size, overlap, host memory */
+#define SKG_EUNSUPPORTED 2  /* outside the contract: alignment, K multiple, size */
+#define SKG_ELAUNCH 3       /* the HIP runtime rejected a launch */
+#define SKG_ETABLE 4        /* table file unreadable (the table then stays off) */
+
+/* Operation ids, as used by the query / variant calls. */
+#define SKG_OP_BF16 0
+#define SKG_OP_GATED 1
+#define SKG_OP_FP8_TENSOR 2
+#define SKG_OP_A8W8_BLOCK 3
+
+/* y[M,N] = x[M,K] . W[N,K]^T.  x, W: bf16.  scales: unused, may be NULL. */
+skg_status skinny_gemm_bf16(const void* x, const void* W, const float* scales,
+                            void* y, int M, int N, int K, hipStream_t stream);
+
+/* Fused gate/up.  W is ONE [2N, K] bf16 buffer: rows [0, N) are the gate
+ * weight Wg, rows [N, 2N) the up weight Wu.  y[M, N] = silu(g) * u with
+ * g = x Wg^T and u = x Wu^T kept in float32 (not rounded) before the product;
+ * silu(g) = g / (1 + exp(-g)).  scales: unused, may be NULL. */
+skg_status skinny_gemm_gated(const void* x, const void* W, const float* scales,
+                             void* y, int M, int N, int K, hipStream_t stream);
+
+/* fp8 weight with one per-tensor scale: y = scales[0] * (x . dec(W)^T).
+ * x: bf16 [M, K] (not quantised).  W: e4m3fn [N, K].  scales: device float32[1]. */
+skg_status skinny_gemm_fp8_tensor(const void* x, const void* W, const float* scales,
+                                  void* y, int M, int N, int K, hipStream_t stream);
+
+/* A8W8 block scale.  x: e4m3fn [M, K]; x_scales: float32 [M, ceil(K/128)]
+ * (one per row per 128 K-columns).  W: e4m3fn [N, K]; w_scales: float32
+ * [ceil(N/128), ceil(K/128)] (one per 128 x 128 block).
+ * y[m, n] = sum_k xs[m, k/128] dec(x[m, k]) * ws[n/128, k/128] dec(W[n, k]). */
+skg_status skinny_gemm_a8w8_block(const void* x, const void* W, const float* x_scales,
+                                  const float* w_scales, void* y, int M, int N, int K,
+                                  hipStream_t stream);
+
+/* Text of the calling thread's last non-OK status ("" if none). */
+const char* skinny_gemm_last_error(void);
+
+/* Load the dispatch table.  path NULL: $SKINNY_GEMM_TABLE, else the table
+ * installed beside the library for this device's architecture.  A table whose
+ * identity header does not match this build and device, or one loaded while a
+ * dispatch override ($SKINNY_GEMM_FORCE) is set, is REFUSED: one line on
+ * stderr, built-in defaults stay in effect, and the call returns SKG_OK.  A
+ * missing or malformed file returns SKG_ETABLE (defaults stay in effect).
+ * (Tuned solutions apply only on the stack they were tuned on: mstar PR #1104,
+ * "What changed"; identity, stale and knob refusals: Strata PR #1297, "The
+ * second commit: the seam rework", items 1-2.) */
+skg_status skinny_gemm_load_table(const char* path);
+
+/* Same, with the identity string given instead of read from the device and
+ * runtime: lets the table logic run on a machine without a GPU. */
+skg_status skinny_gemm_load_table_as(const char* path, const char* identity);
+
+/* Identity this build and device give a table:
+ * "arch=<gfx>;hip=<runtime version>;cc=<compiler hash>;space=<selection token>".
+ * Writes a NUL-terminated string into buf[len]. */
+skg_status skinny_gemm_identity(char* buf, int len);
+
+/* 1 if a table is engaged, 0 if defaults are in effect. Also reports, in buf,
+ * the table status line ("engaged ...", "refused ...", "none"). */
+int skinny_gemm_table_status(char* buf, int len);
+
+/* Which variant dispatch picks for (op, M, N, K), as
+ * "<variant> <source>" where source is table|default|force. */
+skg_status skinny_gemm_query(int op, int M, int N, int K, char* buf, int len);
+
+/* Number of compiled variants for an op, and the name of variant i. */
+int skinny_gemm_num_variants(int op);
+skg_status skinny_gemm_variant_name(int op, int variant, char* buf, int len);
+
+/* 1 if variant `variant` of `op` can run M rows (its kernels are compiled for
+ * that rows bucket), else 0. */
+int skinny_gemm_variant_supports(int op, int variant, int M);
+
+/* Run one named variant, bypassing the table (tuner and tests).  s0/s1 are the
+ * op's scale arrays (fp8_tensor: s0 = w_scale; a8w8: s0 = x_scales,
+ * s1 = w_scales; others NULL).  knobs: reserved, pass NULL. */
+skg_status skinny_gemm_run_variant(int op, int variant, const int* knobs,
+                                   const void* x, const void* W, const float* s0,
+                                   const float* s1, void* y, int M, int N, int K,
+                                   hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKINNY_GEMM_H */

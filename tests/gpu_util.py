@@ -1,0 +1,70 @@
+"""Helpers shared by the GPU tests: move generator outputs to the device, run
+the library, compare with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import gemv_skinny_gemm_02_amd as skg
+import oracle
+
+
+def say(*a) -> None:
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_fp8(b: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(b)).view(torch.float8_e4m3fn).cuda()
+
+
+def dev_f32(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def host_bits(y: torch.Tensor) -> np.ndarray:
+    return y.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def to_device(p):
+    """Device tensors (x, W, s0, s1) of a synth.Problem."""
+    if p.kind in ("bf16", "gated"):
+        return dev_bf16(p.x), dev_bf16(p.w), None, None
+    if p.kind == "fp8_tensor":
+        return dev_bf16(p.x), dev_fp8(p.w), dev_f32(p.s0), None
+    return dev_fp8(p.x), dev_fp8(p.w), dev_f32(p.s0), dev_f32(p.s1)
+
+
+def run(p, dev=None, variant=None, y=None):
+    """Run the library on problem p (dispatch, or one variant)."""
+    x, w, s0, s1 = dev if dev is not None else to_device(p)
+    if variant is not None:
+        return skg.skinny_gemm_run_variant(p.kind, variant, x, w, s0, s1, y=y)
+    if p.kind == "bf16":
+        return skg.skinny_gemm_bf16(x, w, y=y)
+    if p.kind == "gated":
+        return skg.skinny_gemm_gated(x, w, y=y)
+    if p.kind == "fp8_tensor":
+        return skg.skinny_gemm_fp8_tensor(x, w, s0, y=y)
+    return skg.skinny_gemm_a8w8_block(x, w, s0, s1, y=y)
+
+
+def reference(p, cols=None) -> np.ndarray:
+    if p.kind == "bf16":
+        return oracle.linear_bf16(p.x, p.w, cols=cols)
+    if p.kind == "gated":
+        return oracle.linear_gated(p.x, p.w, cols=cols)
+    if p.kind == "fp8_tensor":
+        return oracle.linear_fp8_tensor(p.x, p.w, p.s0, cols=cols)
+    return oracle.linear_a8w8_block(p.x, p.s0, p.w, p.s1, cols=cols)
+
+
+def assert_parity(y_bits: np.ndarray, ref: np.ndarray, what: str) -> None:
+    r = oracle.parity(y_bits, ref)
+    assert r.ok, f"{what}: {r.msg}"

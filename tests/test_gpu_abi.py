@@ -1,0 +1,170 @@
+"""The C ABI on the GPU: status codes, edge cases, guard bytes, and the
+determinism of results and of dispatch."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import gemv_skinny_gemm_02_amd as skg
+import synth
+from gpu_util import assert_parity, dev_bf16, dev_f32, dev_fp8, host_bits, reference, run, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    skg.load()
+
+
+def _raw(fn, *args):
+    lib = skg.load()
+    st = getattr(lib, fn)(*args)
+    return st, lib.skinny_gemm_last_error().decode()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def test_empty_is_noop():
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")
+    y = torch.full((4, 8), 7.0, dtype=torch.bfloat16, device="cuda")
+    for M, N in ((0, 8), (4, 0)):
+        st, _ = _raw("skinny_gemm_bf16", x.data_ptr(), w.data_ptr(), None, y.data_ptr(), M, N, 64, _stream())
+        assert st == 0
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+    e = skg.skinny_gemm_bf16(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"), w)
+    assert e.shape == (0, 8)
+
+
+def test_k_zero_writes_zeros():
+    for kind in ("bf16", "gated", "fp8_tensor", "a8w8_block"):
+        p = {"bf16": synth.make_bf16, "gated": synth.make_gated, "fp8_tensor": synth.make_fp8_tensor,
+             "a8w8_block": synth.make_a8w8_block}[kind](3, 40, 16)
+        x, w, s0, s1 = to_device(p)
+        y = torch.full((3, 40), 5.0, dtype=torch.bfloat16, device="cuda")
+        lib = skg.load()
+        if kind == "a8w8_block":
+            st = lib.skinny_gemm_a8w8_block(x.data_ptr(), w.data_ptr(), s0.data_ptr(), s1.data_ptr(), y.data_ptr(),
+                                            3, 40, 0, _stream())
+        else:
+            st = getattr(lib, "skinny_gemm_" + kind)(x.data_ptr(), w.data_ptr(), s0.data_ptr() if s0 is not None else None,
+                                                     y.data_ptr(), 3, 40, 0, _stream())
+        assert st == 0, lib.skinny_gemm_last_error()
+        torch.cuda.synchronize()
+        assert torch.all(y == 0), kind
+
+
+def test_status_codes():
+    x = torch.zeros((2, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros((2, 16), dtype=torch.bfloat16, device="cuda")
+    s = _stream()
+    assert _raw("skinny_gemm_bf16", x.data_ptr(), w.data_ptr(), None, y.data_ptr(), -1, 16, 64, s)[0] == 1
+    assert _raw("skinny_gemm_bf16", None, w.data_ptr(), None, y.data_ptr(), 2, 16, 64, s)[0] == 1
+    st, msg = _raw("skinny_gemm_bf16", x.data_ptr(), w.data_ptr(), None, y.data_ptr(), 2, 16, 60, s)
+    assert st == 2 and "K" in msg
+    st, msg = _raw("skinny_gemm_bf16", x.data_ptr() + 2, w.data_ptr(), None, y.data_ptr(), 2, 16, 56, s)
+    assert st == 2 and "aligned" in msg
+    # y overlapping x
+    st, msg = _raw("skinny_gemm_bf16", x.data_ptr(), w.data_ptr(), None, x.data_ptr(), 2, 16, 64, s)
+    assert st == 1 and "overlap" in msg
+    # host memory is refused on the host, before any launch
+    host = np.zeros((2, 64), np.uint16)
+    st, msg = _raw("skinny_gemm_bf16", host.ctypes.data, w.data_ptr(), None, y.data_ptr(), 2, 16, 64, s)
+    assert st == 1 and "device memory" in msg
+    # fp8 needs K % 16
+    w8 = torch.zeros((16, 64), dtype=torch.uint8, device="cuda")
+    sc = torch.ones(1, dtype=torch.float32, device="cuda")
+    st, _ = _raw("skinny_gemm_fp8_tensor", x.data_ptr(), w8.data_ptr(), sc.data_ptr(), y.data_ptr(), 2, 16, 56, s)
+    assert st == 2
+    # fp8 tensor without its scale
+    st, _ = _raw("skinny_gemm_fp8_tensor", x.data_ptr(), w8.data_ptr(), None, y.data_ptr(), 2, 16, 64, s)
+    assert st == 1
+    # knobs are reserved
+    st, _ = _raw("skinny_gemm_run_variant", 0, 0, ctypes.byref(ctypes.c_int(1)), x.data_ptr(), w.data_ptr(), None,
+                 None, y.data_ptr(), 2, 16, 64, s)
+    assert st == 1
+    # a variant that is not compiled for the rows bucket
+    names = skg.variants("gated")
+    st, _ = _raw("skinny_gemm_run_variant", 1, names.index("gemv_r4_k4_u1"), None, x.data_ptr(), w.data_ptr(),
+                 None, None, y.data_ptr(), 2, 8, 64, s)
+    assert st == 0
+    xw = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
+    yw = torch.zeros((16, 8), dtype=torch.bfloat16, device="cuda")
+    st, _ = _raw("skinny_gemm_run_variant", 1, names.index("gemv_r4_k4_u1"), None, xw.data_ptr(), w.data_ptr(),
+                 None, None, yw.data_ptr(), 16, 8, 64, s)
+    assert st == 2
+
+
+def test_short_allocation_refused():
+    """A W that is shorter than N*K*2 bytes is refused on the host."""
+    hip = ctypes.CDLL("libamdhip64.so")
+    w = torch.empty((4 << 20) // 2, dtype=torch.bfloat16, device="cuda")    # 4 MiB
+    base, size = ctypes.c_void_p(), ctypes.c_size_t()
+    assert hip.hipMemGetAddressRange(ctypes.byref(base), ctypes.byref(size), ctypes.c_void_p(w.data_ptr())) == 0
+    N, K = 1 << 20, 4096                                  # claims 8 GiB
+    need = N * K * 2
+    if base.value + size.value >= w.data_ptr() + need:
+        pytest.skip("allocator segment is unexpectedly large")
+    x = torch.zeros((1, K), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros((1, N), dtype=torch.bfloat16, device="cuda")
+    st, msg = _raw("skinny_gemm_bf16", x.data_ptr(), w.data_ptr(), None, y.data_ptr(), 1, N, K, _stream())
+    assert st == 1 and "W needs" in msg, msg
+
+
+def test_guard_bytes_untouched():
+    """Writes stay inside y: a guard region after y keeps its bytes."""
+    for kind, M, N, K in (("bf16", 3, 77, 264), ("gated", 20, 50, 264), ("fp8_tensor", 2, 77, 272),
+                          ("a8w8_block", 17, 77, 272)):
+        p = {"bf16": synth.make_bf16, "gated": synth.make_gated, "fp8_tensor": synth.make_fp8_tensor,
+             "a8w8_block": synth.make_a8w8_block}[kind](M, N, K, seed=3)
+        dev = to_device(p)
+        buf = torch.full((M * N + 4096,), 12345, dtype=torch.int16, device="cuda")
+        y = buf[:M * N].view(torch.bfloat16).view(M, N)
+        run(p, dev, y=y)
+        torch.cuda.synchronize()
+        assert torch.all(buf[M * N:] == 12345), kind
+        assert_parity(host_bits(y), reference(p), kind)
+
+
+def test_repeat_bit_identical_and_graph_replay():
+    """10 repeats are bit-identical; a captured graph replays the same bits,
+    with eager work and synchronisation between replays."""
+    cases = [synth.make_bf16(8, 4096, 4096), synth.make_gated(6, 1024, 4096),
+             synth.make_fp8_tensor(2, 4096, 4096), synth.make_a8w8_block(32, 8192, 4096),
+             synth.make_bf16(128, 4096, 4096)]
+    for p in cases:
+        say(f"determinism {p.kind} M={p.M} N={p.N} K={p.K}")
+        dev = to_device(p)
+        first = host_bits(run(p, dev))
+        for _ in range(9):
+            assert np.array_equal(host_bits(run(p, dev)), first)
+        y = torch.empty((p.M, p.N), dtype=torch.bfloat16, device="cuda")
+        run(p, dev, y=y)                      # warm-up outside capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(p, dev, y=y)
+        for _ in range(3):
+            y.zero_()
+            junk = torch.randn(1 << 16, device="cuda") * 2   # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(host_bits(y), first), f"graph replay {p.kind}"
+            del junk
+
+
+def test_dispatch_deterministic():
+    a = [skg.skinny_gemm_query(k, M, N, K) for k in skg.OPS for M in (1, 5, 16, 100, 300)
+         for (N, K) in ((4096, 4096), (1024, 1024))]
+    b = [skg.skinny_gemm_query(k, M, N, K) for k in skg.OPS for M in (1, 5, 16, 100, 300)
+         for (N, K) in ((4096, 4096), (1024, 1024))]
+    assert a == b

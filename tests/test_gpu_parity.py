@@ -1,0 +1,167 @@
+"""GPU parity of every form, variant and workload shape against the CPU oracle.
+
+Small shapes span several workgroups and ragged tails in N, K and M and are
+compared element by element.  The full workload shapes run in the launch
+configuration the benchmark times (table dispatch) and are compared on a seeded
+sample of output columns, which the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gemv_skinny_gemm_02_amd as skg
+import oracle
+import synth
+from gpu_util import assert_parity, dev_bf16, dev_f32, dev_fp8, host_bits, reference, run, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+MAKE = {"bf16": synth.make_bf16, "gated": synth.make_gated,
+        "fp8_tensor": synth.make_fp8_tensor, "a8w8_block": synth.make_a8w8_block}
+
+
+def _small_shape(kind):
+    # N and K ragged against every workgroup row count and K round; K % 16 == 0
+    return (257, 1040) if kind in ("fp8_tensor", "a8w8_block") else (257, 1032)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    skg.load()
+    say("device:", torch.cuda.get_device_name(0), "identity:", skg.skinny_gemm_identity())
+    say("table:", skg.skinny_gemm_table_status())
+
+
+def test_config1_full():
+    """bf16 M=1, N=K=4096, seed 0: every output against the oracle."""
+    p = synth.make_bf16(*synth.CONFIG1, seed=0)
+    y = run(p)
+    torch.cuda.synchronize()
+    assert_parity(host_bits(y), reference(p), "config1")
+
+
+@pytest.mark.parametrize("kind", list(MAKE))
+def test_every_variant_small(kind):
+    N, K = _small_shape(kind)
+    names = skg.variants(kind)
+    for M in (1, 2, 3, 5, 8, 12, 16, 17, 40, 128):
+        p = MAKE[kind](M, N, K, seed=1)
+        dev = to_device(p)
+        ref = reference(p)
+        ran = 0
+        for i, name in enumerate(names):
+            if not skg.skinny_gemm_variant_supports(kind, i, M):
+                continue
+            say(f"{kind} M={M} N={N} K={K} variant={name}")
+            y = run(p, dev, variant=name)
+            torch.cuda.synchronize()
+            assert_parity(host_bits(y), ref, f"{kind} {name} M={M}")
+            ran += 1
+        assert ran > 0, f"no variant runs {kind} at M={M}"
+
+
+@pytest.mark.parametrize("kind", list(MAKE))
+def test_dispatch_ragged(kind):
+    """Default dispatch over M buckets and M past 128, ragged N/K."""
+    for (N, K) in [(129, 256), (1000, 2064), (64, 4096)]:
+        for M in (1, 4, 6, 7, 13, 24, 33, 96, 130, 200):
+            p = MAKE[kind](M, N, K, seed=2)
+            say(f"{kind} dispatch M={M} N={N} K={K} -> {skg.skinny_gemm_query(kind, M, N, K)}")
+            y = run(p)
+            torch.cuda.synchronize()
+            assert_parity(host_bits(y), reference(p), f"{kind} dispatch M={M} N={N} K={K}")
+
+
+def _sampled(p, y, count=64):
+    cols = synth.rows_of(p.N, count, seed=p.M)
+    assert_parity(host_bits(y)[:, cols], reference(p, cols=cols), f"{p.kind} M={p.M} N={p.N} K={p.K} (sampled)")
+
+
+def test_sweep_full_shapes():
+    """The bf16 decode-linear sweep at its full shapes, sampled columns."""
+    for (N, K) in synth.SWEEP_NK:
+        for M in synth.SWEEP_M:
+            p = synth.make_bf16(M, N, K, seed=0)
+            say(f"bf16 sweep M={M} N={N} K={K} -> {skg.skinny_gemm_query('bf16', M, N, K)}")
+            y = run(p)
+            torch.cuda.synchronize()
+            _sampled(p, y)
+
+
+def test_gated_full_shapes():
+    N, K = synth.GATED_NK
+    for M in synth.GATED_M:
+        p = synth.make_gated(M, N, K, seed=0)
+        say(f"gated M={M} N={N} K={K} -> {skg.skinny_gemm_query('gated', M, N, K)}")
+        y = run(p)
+        torch.cuda.synchronize()
+        _sampled(p, y)
+
+
+def test_a8w8_full_shapes():
+    for (N, K) in synth.A8W8_NK:
+        for M in synth.A8W8_M:
+            p = synth.make_a8w8_block(M, N, K, seed=0)
+            say(f"a8w8 M={M} N={N} K={K} -> {skg.skinny_gemm_query('a8w8_block', M, N, K)}")
+            y = run(p)
+            torch.cuda.synchronize()
+            _sampled(p, y)
+
+
+def test_fp8_head_full_shape():
+    """The 248320 x 4096 fp8 vocabulary head, one weight copy for all M."""
+    N, K = synth.HEAD_NK
+    base = synth.make_fp8_tensor(max(synth.HEAD_M), N, K, seed=0)
+    w = dev_fp8(base.w)
+    s = dev_f32(base.s0)
+    for M in synth.HEAD_M:
+        # x for M rows: the first M rows of the x stream (seed 0, tensor 1)
+        xM = synth.bf16_bits(synth.normal_f32(0, 1, (M, K)))
+        say(f"fp8 head M={M} -> {skg.skinny_gemm_query('fp8_tensor', M, N, K)}")
+        y = skg.skinny_gemm_fp8_tensor(dev_bf16(xM), w, s)
+        torch.cuda.synchronize()
+        cols = synth.rows_of(N, 256, seed=M)
+        ref = oracle.linear_fp8_tensor(xM, base.w, base.s0, cols=cols)
+        assert_parity(host_bits(y)[:, cols], ref, f"fp8 head M={M}")
+
+
+def test_fp8_one_hot_exact():
+    """x one-hot 1.0 and W holding every finite e4m3fn code: y = the code's
+    value, bit-exactly (every e4m3fn value is a bf16 value)."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    K = 64
+    for M in (1, 3, 16):
+        for k in (0, 37, 63):
+            wq = np.zeros((codes.size, K), np.uint8)
+            wq[:, k] = codes
+            x = np.zeros((M, K), np.uint16)
+            x[:, k] = 0x3F80
+            want = oracle.bf16_rne_bits(np.tile(oracle.dec_e4m3fn(codes), (M, 1)))
+            y = skg.skinny_gemm_fp8_tensor(dev_bf16(x), dev_fp8(wq), dev_f32(np.array([1.0], np.float32)))
+            got = host_bits(y)
+            assert np.array_equal(got & 0x7FFF, want & 0x7FFF), f"fp8 one-hot M={M} k={k}"
+            # zero codes may come back as +0 or -0 from a sum; nonzero signs must match
+            nz = (want & 0x7FFF) != 0
+            assert np.array_equal(got[nz], want[nz])
+            # A8W8: x one-hot 1.0 (0x38) with unit scales
+            xq = np.zeros((M, K), np.uint8)
+            xq[:, k] = 0x38
+            y2 = skg.skinny_gemm_a8w8_block(dev_fp8(xq), dev_fp8(wq), dev_f32(np.ones((M, 1), np.float32)),
+                                            dev_f32(np.ones((2, 1), np.float32)))
+            got2 = host_bits(y2)
+            assert np.array_equal(got2[nz], want[nz]) and np.array_equal(got2 & 0x7FFF, want & 0x7FFF)
+
+
+def test_bf16_one_hot_exact():
+    """One-hot x picks a column of W exactly; gated one-hot gives silu(g)*u."""
+    r = np.random.default_rng(4)
+    N, K = 300, 520
+    w = synth.bf16_bits(r.standard_normal((N, K)).astype(np.float32))
+    for M in (1, 6, 16, 33):
+        ks = r.integers(0, K, size=M)
+        x = np.zeros((M, K), np.uint16)
+        x[np.arange(M), ks] = 0x3F80
+        y = host_bits(skg.skinny_gemm_bf16(dev_bf16(x), dev_bf16(w)))
+        assert np.array_equal(y, w[:, ks].T), f"bf16 one-hot M={M}"
