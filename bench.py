@@ -1,0 +1,342 @@
+#!/usr/bin/env python3
+"""Benchmark of the skinny decode linear on one MI355X.
+
+Workload: the bf16 decode-linear sweep -- M in {1,2,3,4,6,8,12,16,24,32,64,96,
+128} x (N, K) in {(4096,4096), (6144,4096), (4096,12288), (2048,2048),
+(1024,1024)}, x ~ N(0,1), W ~ N(0,0.02), seed 0.  One step is one pass of the
+whole path over that sweep: 65 calls of skinny_gemm_bf16 through the library's
+table dispatch.  Inputs are resident in HBM before timing starts.  Each shape
+cycles through enough copies of W (>= 1 GiB per shape) that every call streams
+its weight from HBM, not from the 256 MB Infinity Cache.  Steps are replayed
+from HIP graphs.  The dominant kernel's launches are grouped in their own graph
+and bracketed by HIP events on the launch stream, which gives its live average
+duration for the roofline figure.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+METRIC = "achieved HBM GB/s and µs/call at M=1/8/128; fraction of MI355X roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def alg_bytes(M, N, K):
+    """Algorithmic bytes of one bf16 call: W once, x once, y once."""
+    return 2 * N * K + 2 * M * K + 2 * M * N
+
+
+def kernel_symbol(variant: str, M: int, op: int = 0) -> str:
+    """The kernel template instance a variant runs for M rows, as rocprofv3
+    prints it."""
+    parts = variant.split("_")
+    a, ks, u = int(parts[1][1:]), int(parts[2][1:]), int(parts[3][1:])   # (R|FN, KS|S, P)
+    if parts[0] == "gemv":
+        mt = next(b for b in (1, 2, 3, 4, 6, 8, 12, 16) if M <= b)
+        return f"void skg::gemv_kernel<{op}, {mt}, {a}, {ks}, {u}>(skg::Args)"
+    f = (min(M, 128) + 15) // 16
+    fm = next(b for b in (1, 2, 4, 6, 8) if f <= b)
+    kind = "tlds" if parts[0] == "tlds" else "tile"
+    return f"void skg::{kind}_kernel<{op}, {fm}, {a}, {ks}, {u}>(skg::Args)"
+
+
+def lib_code_hash() -> str:
+    """Hash of the kernel and dispatch sources the library was built from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gemv_skinny_gemm_02_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_counters(kernel: str, code_hash: str):
+    """HBM traffic per launch of `kernel` from the committed counter summary,
+    if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "bf16_sweep_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv, rows = {}, {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("kernel "):
+                _, rest = line.split(" ", 1)
+                name, fetch, write = rest.rsplit("|", 2)
+                rows[name.strip()] = (float(fetch), float(write))
+            elif "=" in line:
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("code_hash") != code_hash or kernel not in rows:
+        return None
+    ff, wf = float(kv["copy_fetch_factor"]), float(kv["copy_write_factor"])
+    fetch_kib, write_kib = rows[kernel]
+    return (fetch_kib / ff + write_kib / wf) * 1024.0
+
+
+def cpu_baseline(calls, host, seconds: float):
+    """The oracle, as it stands, on a bounded prefix of one step's calls."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    done, nbytes, t0 = [], 0, time.perf_counter()
+    for (M, N, K) in calls:
+        xb, wb = host[(N, K)]
+        oracle.linear_bf16(xb[:M], wb)
+        nbytes += alg_bytes(M, N, K)
+        done.append((M, N, K))
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {len(done)} of the step's {len(calls)} calls in step order "
+                      f"({len(done)} oracle.linear_bf16 calls, float64, {dt:.1f} s)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotation-gib", type=float, default=1.0, help="bytes of W copies per shape")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--per-call-replays", type=int, default=5, help="graph replays per call shape")
+    ap.add_argument("--no-per-call", action="store_true",
+                    help="skip the per-call graph timings (profiling runs: keeps every dispatch of a kernel "
+                         "in the step's shape mix)")
+    ap.add_argument("--per-call-min", type=int, default=64, help="min launches per per-call graph")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the skinny linear is measured on one MI355X "
+              "(a multi-GPU run would shard N with no exchange; see the design notes)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import gemv_skinny_gemm_02_amd as skg
+    import synth
+
+    if not torch.cuda.is_available():
+        log("no GPU")
+        return 1
+    torch.cuda.set_device(0)
+    skg.load()
+    dev_name = torch.cuda.get_device_name(0)
+    log("device", dev_name, "| identity", skg.skinny_gemm_identity())
+
+    shapes = list(synth.SWEEP_NK)
+    Ms = list(synth.SWEEP_M)
+    calls = [(M, N, K) for (N, K) in shapes for M in Ms]
+
+    # ---------------------------------------------------------- inputs
+    host, x_dev, w_dev, y_dev = {}, {}, {}, {}
+    free, _ = torch.cuda.mem_get_info()
+    need = sum(max(2, math.ceil(args.rotation_gib * 2**30 / (2 * N * K))) * 2 * N * K for N, K in shapes)
+    if need > 0.8 * free:
+        log(f"not enough device memory for the rotation copies ({need / 2**30:.1f} GiB needed)")
+        return 1
+    for (N, K) in shapes:
+        p = synth.make_bf16(max(Ms), N, K, seed=0)
+        host[(N, K)] = (p.x, p.w)
+        if K not in x_dev:
+            x_dev[K] = torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).cuda()
+        w0 = torch.from_numpy(p.w.view(np.int16)).view(torch.bfloat16).cuda()
+        R = max(2, math.ceil(args.rotation_gib * 2**30 / (2 * N * K)))
+        w_dev[(N, K)] = [w0] + [w0.clone() for _ in range(R - 1)]
+        for M in Ms:
+            y_dev[(M, N)] = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    log("inputs resident:", {f"{N}x{K}": len(w_dev[(N, K)]) for N, K in shapes}, "copies")
+
+    stream = torch.cuda.current_stream()
+    choice = {c: skg.skinny_gemm_query("bf16", *c) for c in calls}
+    sym = {c: kernel_symbol(choice[c][0], c[0]) for c in calls}
+
+    def launch(c, copy):
+        M, N, K = c
+        ws = w_dev[(N, K)]
+        skg.skinny_gemm_bf16(x_dev[K][:M], ws[copy % len(ws)], y=y_dev[(M, N)])
+
+    for c in calls:                      # eager warm-up (and lazy table load)
+        launch(c, 0)
+    torch.cuda.synchronize()
+
+    # ------------------- which kernel dominates a step (3 eager timings each)
+    rough_us = {}
+    for c in calls:
+        ts = []
+        for i in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch(c, 1 + i)
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        rough_us[c] = min(ts)
+    sym_time = {}
+    for c in calls:
+        sym_time[sym[c]] = sym_time.get(sym[c], 0.0) + rough_us[c]
+    dominant = max(sym_time, key=sym_time.get)
+    dom_calls = [c for c in calls if sym[c] == dominant]
+    rest_calls = [c for c in calls if sym[c] != dominant]
+    log(f"dominant kernel {dominant}: {len(dom_calls)} calls/step, ~{sym_time[dominant]:.1f} us/step")
+
+    # ------------------------------------------ step graphs (4 rotations)
+    NR = 4
+    nM = len(Ms)
+
+    def capture(subset, r):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in subset:
+                launch(c, r * nM + Ms.index(c[0]))
+        return g
+
+    g_rest = [capture(rest_calls, r) for r in range(NR)]
+    g_dom = [capture(dom_calls, r) for r in range(NR)]
+    torch.cuda.synchronize()
+
+    for s in range(args.warmup):
+        g_rest[s % NR].replay()
+        g_dom[s % NR].replay()
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------- timed steps
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.steps):
+        g_rest[s % NR].replay()
+        e0[s].record(stream)
+        g_dom[s % NR].replay()
+        e1[s].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    dom_us = sum(e0[s].elapsed_time(e1[s]) for s in range(args.steps)) * 1e3 / (args.steps * len(dom_calls))
+    step_bytes = sum(alg_bytes(*c) for c in calls)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us ({wall / args.steps * 1e6:.1f} us wall), {value:.1f} GB/s, "
+        f"dominant kernel {dom_us:.2f} us/launch")
+
+    del g_rest, g_dom
+    if args.no_per_call:
+        per_call_us = dict(rough_us)
+    else:
+        # ------------------------------------------- per-call time (graph replay)
+        per_call_us = {}
+        for c in calls:
+            M, N, K = c
+            R = len(w_dev[(N, K)])
+            n = max(args.per_call_min, 2 * R)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    launch(c, i)
+            g.replay()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(max(1, args.per_call_replays)):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+                b.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3 / n)
+            per_call_us[c] = statistics.median(ts)
+            del g
+
+    # --------------------------- a copy of known size (counter calibration)
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+    # ------------------------------------------------------------ report
+    dom_bytes = sum(alg_bytes(*c) for c in dom_calls) / len(dom_calls)
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    code_hash = lib_code_hash()
+    traffic = read_counters(dominant, code_hash)
+    detail = {}
+    for M in (1, 8, 128):
+        row = {}
+        for (N, K) in shapes:
+            c = (M, N, K)
+            us = per_call_us[c]
+            gbs = alg_bytes(*c) / (us * 1e-6) / 1e9
+            tfl = 2 * M * N * K / (us * 1e-6) / 1e12
+            row[f"{N}x{K}"] = {"us": round(us, 2), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
+                               "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4), "variant": choice[c][0]}
+        detail[f"M={M}"] = row
+    all_calls = {f"{M}x{N}x{K}": round(per_call_us[(M, N, K)], 2) for (M, N, K) in calls}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bf16 decode-linear sweep: M in {1,2,3,4,6,8,12,16,24,32,64,96,128} x (N,K) in "
+                               "{(4096,4096),(6144,4096),(4096,12288),(2048,2048),(1024,1024)}, x~N(0,1), "
+                               "W~N(0,0.02), seed 0, 65 calls per step, weights rotated past the Infinity Cache",
+                   "calls_per_step": len(calls), "alg_bytes_per_step": step_bytes, "device": dev_name,
+                   "table": skg.skinny_gemm_table_status()[1]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": round(traffic) if traffic is not None else None,
+                     "kernel": dominant, "launches_per_step": len(dom_calls), "avg_launch_us": round(dom_us, 3),
+                     "alg_bytes_per_launch": round(dom_bytes), "code_hash": code_hash},
+        "per_m": detail,
+        "per_call_us": all_calls,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(calls, host, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -42,8 +42,9 @@ def lib_path() -> str:
     return os.path.join(_PKG, "libskinny_gemm.so")
 
 
-def default_table_path(arch: str = "gfx950", product: str = "mi355x") -> str:
-    return os.path.join(_PKG, "configs", arch, product, "skinny_gemm.json")
+def default_table_path(arch: str = "gfx950") -> str:
+    """Where the library looks for this architecture's dispatch table."""
+    return os.path.join(_PKG, "configs", arch, "skinny_gemm.json")
 
 
 class SkinnyGemmError(RuntimeError):

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <set>
 #include <string>
@@ -110,7 +111,8 @@ void ensure_table_locked() {
   if (!self_identity(&id, &product)) return;
   std::string path;
   if (const char* e = std::getenv("SKINNY_GEMM_TABLE"); e && *e) path = e;
-  else path = self_dir() + "/configs/" + id.arch + "/" + product + "/skinny_gemm.json";
+  else path = self_dir() + "/configs/" + id.arch + "/skinny_gemm.json";
+  (void)product;
   FILE* f = std::fopen(path.c_str(), "rb");
   if (!f) return;  // no table: defaults
   std::fclose(f);
@@ -226,16 +228,89 @@ LaunchFn variant_fn(int op, int v, int M) {
   }
   const int fm = M > kMaxBucket ? kNumTileFM - 1 : tile_fm_index(M);
   const TileRow* t = nullptr;
+  const bool lds = d.family == FAM_TLDS;
   switch (op) {
-    case OP_BF16: t = tile_table<OP_BF16>(); break;
-    case OP_GATED: t = tile_table<OP_GATED>(); break;
-    case OP_FP8T: t = tile_table<OP_FP8T>(); break;
-    case OP_A8W8: t = tile_table<OP_A8W8>(); break;
+    case OP_BF16: t = lds ? tlds_table<OP_BF16>() : tile_table<OP_BF16>(); break;
+    case OP_GATED: t = lds ? tlds_table<OP_GATED>() : tile_table<OP_GATED>(); break;
+    case OP_FP8T: t = lds ? tlds_table<OP_FP8T>() : tile_table<OP_FP8T>(); break;
+    case OP_A8W8: t = lds ? tlds_table<OP_A8W8>() : tile_table<OP_A8W8>(); break;
   }
   return t ? t[fi].f[fm] : nullptr;
 }
 
-skg_status launch(int op, int v, const Args& a, hipStream_t s) {
+// ------------------------------------------------------ split-K workspace
+// fp32 partials of the tlds variants with S > 1: one buffer per device,
+// allocated (kWsInit bytes, or more when a call needs it) by the first call
+// on the device that is not under graph capture, and kept for the life of
+// the process.  Calls on one stream are ordered, so they share it safely;
+// calls that run concurrently on different streams of one device race on it.
+constexpr size_t kWsCap = 256ull << 20;
+constexpr size_t kWsInit = 64ull << 20;
+std::mutex g_ws_mu;
+std::map<int, std::pair<void*, size_t>> g_ws;
+
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return cs != hipStreamCaptureStatusNone;
+}
+
+float* workspace(hipStream_t s, size_t bytes, std::string* why) {
+  if (bytes > kWsCap) {
+    *why = "split-K partials of " + std::to_string(bytes) + " bytes exceed the " + std::to_string(kWsCap) +
+           "-byte workspace cap";
+    return nullptr;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    *why = "no current device";
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  auto& e = g_ws[dev];
+  if (e.first && e.second >= bytes) return static_cast<float*>(e.first);
+  if (capturing(s)) {
+    *why = "the split-K workspace must be allocated outside graph capture (make one call eagerly first)";
+    return nullptr;
+  }
+  if (e.first) {
+    (void)hipDeviceSynchronize();   // the old buffer may still be in use
+    (void)hipFree(e.first);
+    e = {nullptr, 0};
+  }
+  const size_t want = std::max(bytes, kWsInit);
+  void* p = nullptr;
+  if (hipMalloc(&p, want) != hipSuccess) {
+    (void)hipGetLastError();
+    *why = "hipMalloc of the split-K workspace failed";
+    return nullptr;
+  }
+  e = {p, want};
+  return static_cast<float*>(p);
+}
+
+// The first call on a device (outside capture) allocates the workspace so
+// that later captured calls find it.
+void prime_workspace(hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    if (g_ws.count(dev)) return;
+  }
+  std::string why;
+  (void)workspace(s, kWsInit, &why);
+}
+
+skg_status launch(int op, int v, const Args& a_in, hipStream_t s) {
+  Args a = a_in;
   if (a.K == 0) {
     const size_t n = (size_t)a.M * a.N;
     const unsigned grid = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
@@ -244,6 +319,14 @@ skg_status launch(int op, int v, const Args& a, hipStream_t s) {
     return e == hipSuccess ? SKG_OK : fail(SKG_ELAUNCH, "zero fill launch: %s", hipGetErrorString(e));
   }
   const LaunchFn fn = v >= 0 ? variant_fn(op, v, a.M) : nullptr;
+  if (fn && kVariants[v].family == FAM_TLDS) {
+    const size_t need = (size_t)tlds_ws_bytes(op, kVariants[v].p1, a.M, a.N);
+    if (need) {
+      std::string why;
+      a.ws = workspace(s, need, &why);
+      if (!a.ws) return fail(SKG_EUNSUPPORTED, "%s: %s", kVariants[v].name, why.c_str());
+    }
+  }
   if (fn && op == OP_A8W8 && kVariants[v].family == FAM_GEMV) {
     const size_t smem = (size_t)(kGemvMT[gemv_mt_index(a.M)] + 1) * a.kb * sizeof(float);
     if (smem > 64 * 1024)
@@ -260,13 +343,21 @@ skg_status launch(int op, int v, const Args& a, hipStream_t s) {
 
 skg_status run_op(int op, const void* x, const void* w, const float* s0, const float* s1, void* y, int M, int N,
                   int K, hipStream_t s) {
-  Args a{x, w, s0, s1, y, M, N, K, (K + 127) / 128};
+  Args a{x, w, s0, s1, y, M, N, K, (K + 127) / 128, nullptr};
   if (op != OP_FP8T && op != OP_A8W8) a.s0 = nullptr;
   if (op != OP_A8W8) a.s1 = nullptr;
   if (skg_status st = validate(op, a)) return st;
   if (M == 0 || N == 0) return SKG_OK;
+  prime_workspace(s);
   const Decision d = decide(op, M, N, K);
-  return launch(op, d.variant, a, s);
+  skg_status st = launch(op, d.variant, a, s);
+  if (st == SKG_EUNSUPPORTED && d.variant >= 0 && kVariants[d.variant].family == FAM_TLDS) {
+    // no split-K workspace here (e.g. first call under graph capture): the
+    // untuned tile default needs none
+    const int fb = default_variant_no_ws(op, M, N, K);
+    if (fb >= 0 && fb != d.variant) st = launch(op, fb, a, s);
+  }
+  return st;
 }
 
 int copy_out(const std::string& s, char* buf, int len) {
@@ -316,7 +407,7 @@ skg_status skinny_gemm_load_table(const char* path) {
   std::string p;
   if (path && *path) p = path;
   else if (const char* e = std::getenv("SKINNY_GEMM_TABLE"); e && *e) p = e;
-  else p = self_dir() + "/configs/" + id.arch + "/" + product + "/skinny_gemm.json";
+  else p = self_dir() + "/configs/" + id.arch + "/skinny_gemm.json";
   std::string err;
   if (g_table.load(p, id, &err) != 0) return fail(SKG_ETABLE, "%s", err.c_str());
   return SKG_OK;
@@ -377,7 +468,7 @@ skg_status skinny_gemm_run_variant(int op, int variant, const int* knobs, const 
   if (!op_name(op)) return fail(SKG_EINVAL, "unknown op %d", op);
   if (variant < 0 || variant >= kNumVariants) return fail(SKG_EINVAL, "no variant %d", variant);
   if (knobs) return fail(SKG_EINVAL, "knobs are reserved: pass NULL");
-  Args a{x, W, s0, s1, y, M, N, K, (K + 127) / 128};
+  Args a{x, W, s0, s1, y, M, N, K, (K + 127) / 128, nullptr};
   if (op != OP_FP8T && op != OP_A8W8) a.s0 = nullptr;
   if (op != OP_A8W8) a.s1 = nullptr;
   if (skg_status st = validate(op, a)) return st;

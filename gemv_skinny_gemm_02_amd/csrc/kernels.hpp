@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "variants.hpp"
@@ -39,6 +40,7 @@ struct Args {
   void* y;
   int M, N, K;
   int kb;           // ceil(K / 128): scale groups along K
+  float* ws;        // split-K partials [S][G][M][N] fp32 (tlds variants with S > 1)
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -116,12 +118,63 @@ struct ReduceScatter<VC, 0> {
   __device__ __forceinline__ static void run(float*, int, int&) {}
 };
 
+// ======================================================== load pipeline
+// Both kernels stream their operands through a ring of P register buffers:
+// buffer p holds the loads of round j0 + p.  Round j is consumed P rounds
+// after its loads were issued, so P rounds of loads stay in flight while the
+// oldest one is used (vector loads complete in issue order, so waiting for the
+// oldest leaves the younger ones outstanding).  `rounds` is wave-uniform; the
+// load functor clamps a round index past the wave's last to a valid address.
+// The steady-state loop only sees rounds that are full for every lane
+// (compute's second argument false); the drain handles the last P..2P-1
+// rounds, where the final one may reach past K (true).
+template <int P, class Buf, class LoadF, class ComputeF>
+__device__ __forceinline__ void ring_pipeline(Buf (&buf)[P], int rounds, LoadF&& load, ComputeF&& compute) {
+  using Full = std::integral_constant<bool, false>;
+  using Tail = std::integral_constant<bool, true>;
+  // unconditional prologue (load clamps its index): keeps the wait counts exact
+#pragma unroll
+  for (int p = 0; p < P; ++p) load(buf[p], p);
+  int j0 = 0;
+  for (; j0 + 2 * P <= rounds; j0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      compute(buf[p], j0 + p, Full{});
+      // keep each round's loads right after the compute that frees its
+      // buffer: the scheduler would otherwise sink them and shrink the ring
+      __builtin_amdgcn_sched_barrier(0);
+      load(buf[p], j0 + P + p);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int j = j0 + p;
+    if (j < rounds) {
+      compute(buf[p], j, Tail{});
+      if (j + P < rounds) load(buf[p], j + P);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int j = j0 + P + p;
+    if (j < rounds) compute(buf[p], j, Tail{});
+  }
+}
+
 // =================================================================== GEMV
 // One workgroup = 4 waves = (4/KS) row groups x KS K-slices.  Wave (rg, ks)
 // owns rows n0 + rg*R + [0, R) (and the matching up rows N + ... for the gated
 // form) and the K-chunks ((j*KS + ks)*64 + lane) for rounds j = 0, 1, ...; a
-// chunk is one 16-byte load of a W row (8 bf16 or 16 fp8 K-elements).
-template <int OP, int MT, int R, int KS, int U>
+// chunk is one 16-byte load of a W row (8 bf16 or 16 fp8 K-elements).  P
+// rounds are in flight per wave.
+template <int OP, int MT, int R>
+struct GemvRound {
+  u32x4 w[op_groups(OP)][R];
+  u32x4 x[MT][op_xd(OP) / 4];
+};
+
+template <int OP, int MT, int R, int KS, int P>
 __global__ __launch_bounds__(256) void gemv_kernel(const Args a) {
   constexpr int G = op_groups(OP);
   constexpr int V = MT * R * G;
@@ -137,7 +190,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const Args a) {
   extern __shared__ float sc[];      // A8W8: xs rows [MT][kb] then ws row [kb]
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
   const int rg = wave / KS, ks = wave - (wave / KS) * KS;
   const int M = a.M, N = a.N, K = a.K;
   const int wg_row0 = blockIdx.x * RPW;
@@ -153,11 +206,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(const Args a) {
       wp[g][r] = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.w) +
                                                 (size_t)(n + g * N) * K * WB);
     }
-  const u32x4* xp[MT];
+  const u32x4* xp[MT];                // rows past M re-read row M-1: finite data, never stored
 #pragma unroll
   for (int m = 0; m < MT; ++m)
     xp[m] = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.x) +
-                                           (size_t)(m < M ? m : 0) * K * XB);
+                                           (size_t)(m < M ? m : M - 1) * K * XB);
 
   float* xs_l = sc;
   float* ws_l = sc + MT * a.kb;
@@ -176,104 +229,102 @@ __global__ __launch_bounds__(256) void gemv_kernel(const Args a) {
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.0f;
 
-  // Load NU rounds starting at round j0, then accumulate them.
-  auto rounds = [&](int j0, auto nu_tag, auto masked_tag) {
-    constexpr int NU = decltype(nu_tag)::value;
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    u32x4 wv[NU][G][R];
-    u32x4 xv[NU][MT][XV];
-    int cidx[NU];
+  using Round = GemvRound<OP, MT, R>;
+  auto load = [&](Round& b, int j) {
+    const int c = (j * KS + ks) * 64 + lane;
+    const int cc = c < C ? c : C - 1;     // lanes past K re-read a valid chunk; zeroed when used
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int c = ((j0 + u) * KS + ks) * 64 + lane;
-      cidx[u] = c;
-      const bool ok = !MASKED || c < C;
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int r = 0; r < R; ++r) b.w[g][r] = load_nt(wp[g][r] + cc);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int q = 0; q < XV; ++q) b.x[m][q] = xp[m][(size_t)cc * XV + q];
+  };
+
+  auto compute = [&](const Round& b0, int j, auto tail) {
+    const int c = (j * KS + ks) * 64 + lane;
+    Round b;
+    if constexpr (decltype(tail)::value) {     // lanes past K contribute nothing
+      const bool dead = c >= C;
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int r = 0; r < R; ++r) wv[u][g][r] = ok ? load_nt(wp[g][r] + c) : u32x4{0, 0, 0, 0};
+        for (int r = 0; r < R; ++r) b.w[g][r] = dead ? u32x4{0, 0, 0, 0} : b0.w[g][r];
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int q = 0; q < XV; ++q)
-          xv[u][m][q] = (ok && m < M) ? xp[m][(size_t)c * XV + q] : u32x4{0, 0, 0, 0};
+        for (int q = 0; q < XV; ++q) b.x[m][q] = b0.x[m][q];
+    } else {
+      b = b0;
     }
+    if constexpr (OP == OP_BF16 || OP == OP_GATED) {
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      if constexpr (OP == OP_BF16 || OP == OP_GATED) {
+      for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-              float s = acc[(g * MT + m) * R + r];
-#pragma unroll
-              for (int d = 0; d < 4; ++d) s = dot2(xv[u][m][0][d], wv[u][g][r][d], s);
-              acc[(g * MT + m) * R + r] = s;
-            }
-      } else if constexpr (OP == OP_FP8T) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          unsigned wb[8];
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            wb[2 * d] = fp8x2_to_bf16x2<false>(wv[u][0][r][d]);
-            wb[2 * d + 1] = fp8x2_to_bf16x2<true>(wv[u][0][r][d]);
-          }
+        for (int r = 0; r < R; ++r)
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
-            float s = acc[m * R + r];
+            float s = acc[(g * MT + m) * R + r];
 #pragma unroll
-            for (int d = 0; d < 8; ++d) s = dot2(xv[u][m][d >> 2][d & 3], wb[d], s);
-            acc[m * R + r] = s;
+            for (int d = 0; d < 4; ++d) s = dot2(b.x[m][0][d], b.w[g][r][d], s);
+            acc[(g * MT + m) * R + r] = s;
           }
+    } else if constexpr (OP == OP_FP8T) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        unsigned wb[8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          wb[2 * d] = fp8x2_to_bf16x2<false>(b.w[0][r][d]);
+          wb[2 * d + 1] = fp8x2_to_bf16x2<true>(b.w[0][r][d]);
         }
-      } else {  // OP_A8W8
-        const int c = cidx[u];
-        const bool ok = !MASKED || c < C;
-        const int grp = ok ? (c >> 3) : 0;   // 16 K per chunk, 128 K per group
-        const float sw = ws_l[grp];
-        unsigned xb[MT][8];
-        float sxw[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          sxw[m] = xs_l[m * a.kb + grp] * sw;
+          float s = acc[m * R + r];
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            xb[m][2 * d] = fp8x2_to_bf16x2<false>(xv[u][m][0][d]);
-            xb[m][2 * d + 1] = fp8x2_to_bf16x2<true>(xv[u][m][0][d]);
-          }
+          for (int d = 0; d < 8; ++d) s = dot2(b.x[m][d >> 2][d & 3], wb[d], s);
+          acc[m * R + r] = s;
+        }
+      }
+    } else {  // OP_A8W8
+      const int grp = (c < C ? c : C - 1) >> 3;   // 16 K per chunk, 128 K per group
+      const float sw = ws_l[grp];
+      unsigned xb[MT][8];
+      float sxw[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        sxw[m] = xs_l[m * a.kb + grp] * sw;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          xb[m][2 * d] = fp8x2_to_bf16x2<false>(b.x[m][0][d]);
+          xb[m][2 * d + 1] = fp8x2_to_bf16x2<true>(b.x[m][0][d]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        unsigned wb[8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          wb[2 * d] = fp8x2_to_bf16x2<false>(b.w[0][r][d]);
+          wb[2 * d + 1] = fp8x2_to_bf16x2<true>(b.w[0][r][d]);
         }
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          unsigned wb[8];
+        for (int m = 0; m < MT; ++m) {
+          float p = 0.0f;
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            wb[2 * d] = fp8x2_to_bf16x2<false>(wv[u][0][r][d]);
-            wb[2 * d + 1] = fp8x2_to_bf16x2<true>(wv[u][0][r][d]);
-          }
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            float p = 0.0f;
-#pragma unroll
-            for (int d = 0; d < 8; ++d) p = dot2(xb[m][d], wb[d], p);
-            acc[m * R + r] = __builtin_fmaf(p, sxw[m], acc[m * R + r]);
-          }
+          for (int d = 0; d < 8; ++d) p = dot2(xb[m][d], wb[d], p);
+          acc[m * R + r] = __builtin_fmaf(p, sxw[m], acc[m * R + r]);
         }
       }
     }
   };
 
-  using I1 = std::integral_constant<int, 1>;
-  using IU = std::integral_constant<int, U>;
-  using BF = std::integral_constant<bool, false>;
-  using BT = std::integral_constant<bool, true>;
-  const int full = C / (64 * KS);     // rounds in which every lane of every wave has a chunk
-  int j = 0;
-  for (; j + U <= full; j += U) rounds(j, IU{}, BF{});
-  for (; j < full; ++j) rounds(j, I1{}, BF{});
-  if (full * 64 * KS < C) rounds(full, I1{}, BT{});
+  const int first = ks * 64;
+  const int rounds = C > first ? (C - first + 64 * KS - 1) / (64 * KS) : 0;
+  Round buf[P];
+  ring_pipeline<P>(buf, rounds, load, compute);
 
   // ---- combine: lanes (fixed reduce-scatter), then K-slices (LDS, in order)
   using RS = ReduceScatter<V, 32>;
@@ -309,9 +360,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(const Args a) {
 // =================================================================== TILE
 // One workgroup = 4 waves = (4/KS) row groups x KS K-slices.  Wave (ng, ks)
 // owns W rows nb + [0, 16*FN) (plus the up rows for the gated form) and the M
-// rows m_base + [0, 16*FM) of this launch row, and the K-units
-// (j*KS + ks) for rounds j.  A K-unit is 32 K (bf16), 64 K (fp8 weight with
-// bf16 x) or one 128-K scale group (A8W8).
+// rows m_base + [0, 16*FM) of this launch row, and the K-units (j*KS + ks) for
+// rounds j; P units are in flight per wave.  A K-unit is 32 K (bf16), 64 K
+// (fp8 weight with bf16 x) or one 128-K scale group (A8W8).
 //
 // Fragment layout (16x16x32 MFMA): lane l supplies, for its row l%16 of the
 // A operand (W) and its column l%16 of the B operand (x), the 8 K-elements of
@@ -319,12 +370,26 @@ __global__ __launch_bounds__(256) void gemv_kernel(const Args a) {
 // and B agree; the loads below choose them so that the four lanes of one row
 // read 64 contiguous bytes per instruction.  The 16x16 fp32 result sits with
 // C[4*(l/16) + e][l%16] in lane l, register e.
+//
+// x rows past M read row M-1 and lanes past K read a valid K position: both
+// give finite data.  The weight of a lane past K is zeroed before use, so it
+// adds nothing; output columns past M are never stored.  Fragments wholly past
+// M are loaded (clamped) but not multiplied.
 template <int OP>
 struct TileKUnit {
   static constexpr int value = OP == OP_A8W8 ? 128 : (OP == OP_FP8T ? 64 : 32);
 };
+template <int OP, int FM, int FN>
+struct TileRound {
+  static constexpr int WV = OP == OP_A8W8 ? 2 : 1;  // 16-byte W loads per fragment
+  static constexpr int XVN = OP == OP_BF16 || OP == OP_GATED ? 1 : 2;
+  u32x4 w[op_groups(OP)][FN][WV];
+  u32x4 x[FM][XVN];
+  float sx[OP == OP_A8W8 ? FM : 1];
+  float sw[OP == OP_A8W8 ? FN : 1];
+};
 
-template <int OP, int FM, int FN, int KS, int U>
+template <int OP, int FM, int FN, int KS, int P>
 __global__ __launch_bounds__(256) void tile_kernel(const Args a) {
   constexpr int G = op_groups(OP);
   constexpr int NG = 4 / KS;
@@ -333,33 +398,37 @@ __global__ __launch_bounds__(256) void tile_kernel(const Args a) {
   constexpr int WB = op_w_bytes(OP);
   constexpr int XB = op_x_bytes(OP);
   constexpr int NACC = G * FN * FM;
+  using Round = TileRound<OP, FM, FN>;
 
   extern __shared__ float red[];     // KS > 1: [NG][KS-1][NACC*4][64]
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
   const int ng = wave / KS, ks = wave - (wave / KS) * KS;
   const int lr = lane & 15, lq = lane >> 4;
   const int M = a.M, N = a.N, K = a.K;
   const int m_base = blockIdx.y * 16 * FM;
   const int nb = blockIdx.x * RPW + ng * FN * 16;
   const int NU = (K + KU - 1) / KU;
+  const int kb = a.kb;
+  const int fm_live = min(FM, (M - m_base + 15) / 16);   // fragments holding rows < M
 
   const char* wrow[G][FN];
+  int wblk[FN];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+  for (int f = 0; f < FN; ++f) {
+    const int n = min(nb + f * 16 + lr, N - 1);
 #pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      const int n = min(nb + f * 16 + lr, N - 1);
+    for (int g = 0; g < G; ++g)
       wrow[g][f] = static_cast<const char*>(a.w) + (size_t)(n + g * N) * K * WB;
-    }
+    wblk[f] = min(nb + f * 16, N - 1) >> 7;
+  }
   const char* xrow[FM];
-  bool mok[FM];
+  int xm[FM];
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
-    const int m = m_base + j * 16 + lr;
-    mok[j] = m < M;
-    xrow[j] = static_cast<const char*>(a.x) + (size_t)(mok[j] ? m : 0) * K * XB;
+    xm[j] = min(m_base + j * 16 + lr, M - 1);
+    xrow[j] = static_cast<const char*>(a.x) + (size_t)xm[j] * K * XB;
   }
 
   f32x4 acc[G][FN][FM];
@@ -370,110 +439,125 @@ __global__ __launch_bounds__(256) void tile_kernel(const Args a) {
 #pragma unroll
       for (int j = 0; j < FM; ++j) acc[g][f][j] = f32x4{0, 0, 0, 0};
 
-  const int kb = a.kb;
-  const int rounds = (NU + KS - 1) / KS;
-  for (int j0 = 0; j0 < rounds; j0 += U) {
+  // K position of this lane's first element in unit `unit` for load h.
+  auto lane_k = [&](int unit, int h) {
+    if constexpr (OP == OP_A8W8) return unit * KU + h * 64 + lq * 16;
+    else if constexpr (OP == OP_FP8T) return unit * KU + lq * 16;
+    else return unit * KU + lq * 8;
+  };
+  constexpr int LK = OP == OP_BF16 || OP == OP_GATED ? 8 : 16;   // K-elements per 16-byte W load
+
+  auto load = [&](Round& b, int j) {
+    const int unit = min(j * KS + ks, NU - 1);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int unit = (j0 + u) * KS + ks;
-      if (j0 + u >= rounds || unit >= NU) break;   // wave-uniform
-      const int k0 = unit * KU;
-      if constexpr (OP == OP_BF16 || OP == OP_GATED) {
-        const int k = k0 + lq * 8;
-        const bool kok = k < K;
-        bf16x8 wa[G][FN], xb[FM];
+    for (int h = 0; h < Round::WV; ++h) {
+      const int k = min(lane_k(unit, h), K - LK);
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int f = 0; f < FN; ++f) {
-            const u32x4 v = kok ? *reinterpret_cast<const u32x4*>(wrow[g][f] + (size_t)k * 2)
-                                : u32x4{0, 0, 0, 0};
-            wa[g][f] = __builtin_bit_cast(bf16x8, v);
-          }
-#pragma unroll
-        for (int j = 0; j < FM; ++j) {
-          const u32x4 v = (kok && mok[j]) ? *reinterpret_cast<const u32x4*>(xrow[j] + (size_t)k * 2)
-                                          : u32x4{0, 0, 0, 0};
-          xb[j] = __builtin_bit_cast(bf16x8, v);
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int f = 0; f < FN; ++f)
-#pragma unroll
-            for (int j = 0; j < FM; ++j)
-              acc[g][f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[g][f], xb[j], acc[g][f][j], 0, 0, 0);
-      } else if constexpr (OP == OP_FP8T) {
-        // 16 fp8 of a W row per lane (K = k0 + lq*16 + [0,16)): two MFMAs.
-        const int k = k0 + lq * 16;
-        const bool kok = k < K;
-        u32x4 wv[FN];
+      for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int f = 0; f < FN; ++f)
-          wv[f] = kok ? *reinterpret_cast<const u32x4*>(wrow[0][f] + k) : u32x4{0, 0, 0, 0};
-        u32x4 xv[FM][2];
+          b.w[g][f][h] = load_nt(reinterpret_cast<const u32x4*>(wrow[g][f] + (size_t)k * WB));
+    }
+    // every load is unconditional (rows past M are clamped) so the wait
+    // counts stay exact and the ring keeps P units in flight
 #pragma unroll
-        for (int j = 0; j < FM; ++j)
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            xv[j][h] = (kok && mok[j]) ? *reinterpret_cast<const u32x4*>(xrow[j] + (size_t)(k + 8 * h) * 2)
-                                       : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-          for (int f = 0; f < FN; ++f) {
-            u32x4 wb;
-            wb[0] = fp8x2_to_bf16x2<false>(wv[f][2 * h]);
-            wb[1] = fp8x2_to_bf16x2<true>(wv[f][2 * h]);
-            wb[2] = fp8x2_to_bf16x2<false>(wv[f][2 * h + 1]);
-            wb[3] = fp8x2_to_bf16x2<true>(wv[f][2 * h + 1]);
-            const bf16x8 A = __builtin_bit_cast(bf16x8, wb);
-#pragma unroll
-            for (int j = 0; j < FM; ++j)
-              acc[0][f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, xv[j][h]),
-                                                                     acc[0][f][j], 0, 0, 0);
-          }
-        }
-      } else {  // OP_A8W8: one 128-K scale group per unit, four fp8 MFMAs.
-        // lane (row lr, slot lq) holds K = k0 + h*64 + lq*16 + [0,16) for h = 0, 1
-        u32x4 wv[FN][2], xv[FM][2];
+    for (int jj = 0; jj < FM; ++jj) {
+      if constexpr (OP == OP_BF16 || OP == OP_GATED) {
+        const int k = min(lane_k(unit, 0), K - 8);
+        b.x[jj][0] = *reinterpret_cast<const u32x4*>(xrow[jj] + (size_t)k * 2);
+      } else if constexpr (OP == OP_FP8T) {
+        const int k = min(lane_k(unit, 0), K - 16);
+        b.x[jj][0] = *reinterpret_cast<const u32x4*>(xrow[jj] + (size_t)k * 2);
+        b.x[jj][1] = *reinterpret_cast<const u32x4*>(xrow[jj] + (size_t)(k + 8) * 2);
+      } else {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int k = k0 + h * 64 + lq * 16;
-          const bool kok = k < K;
-#pragma unroll
-          for (int f = 0; f < FN; ++f)
-            wv[f][h] = kok ? *reinterpret_cast<const u32x4*>(wrow[0][f] + k) : u32x4{0, 0, 0, 0};
-#pragma unroll
-          for (int j = 0; j < FM; ++j)
-            xv[j][h] = (kok && mok[j]) ? *reinterpret_cast<const u32x4*>(xrow[j] + k) : u32x4{0, 0, 0, 0};
+          const int k = min(lane_k(unit, h), K - 16);
+          b.x[jj][h] = *reinterpret_cast<const u32x4*>(xrow[jj] + k);
         }
-        float sx[FM];
+      }
+    }
+    if constexpr (OP == OP_A8W8) {
 #pragma unroll
-        for (int j = 0; j < FM; ++j)
-          sx[j] = mok[j] ? a.s0[(size_t)(m_base + j * 16 + lr) * kb + unit] : 0.0f;
+      for (int jj = 0; jj < FM; ++jj) b.sx[jj] = a.s0[(size_t)xm[jj] * kb + unit];
+#pragma unroll
+      for (int f = 0; f < FN; ++f) b.sw[f] = a.s1[(size_t)wblk[f] * kb + unit];
+    }
+  };
+
+  auto compute = [&](const Round& b0, int j, auto tail) {
+    const int unit = j * KS + ks;
+    Round b = b0;
+    if constexpr (decltype(tail)::value) {        // lanes past K contribute nothing
+#pragma unroll
+      for (int h = 0; h < Round::WV; ++h) {
+        const bool dead = lane_k(unit, h) >= K;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int f = 0; f < FN; ++f) b.w[g][f][h] = dead ? u32x4{0, 0, 0, 0} : b0.w[g][f][h];
+      }
+    }
+    if constexpr (OP == OP_BF16 || OP == OP_GATED) {
+#pragma unroll
+      for (int jj = 0; jj < FM; ++jj) {
+        if (jj < fm_live) {
+          const bf16x8 B = __builtin_bit_cast(bf16x8, b.x[jj][0]);
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int f = 0; f < FN; ++f)
+              acc[g][f][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.w[g][f][0]), B,
+                                                                      acc[g][f][jj], 0, 0, 0);
+        }
+      }
+    } else if constexpr (OP == OP_FP8T) {
+      // 16 fp8 of a W row per lane: K = unit*64 + lq*16 + [0, 16), two MFMAs.
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
-          const int nrow = min(nb + f * 16, N - 1);
-          const float sw = a.s1[(size_t)(nrow >> 7) * kb + unit];
+          u32x4 wb;
+          wb[0] = fp8x2_to_bf16x2<false>(b.w[0][f][0][2 * h]);
+          wb[1] = fp8x2_to_bf16x2<true>(b.w[0][f][0][2 * h]);
+          wb[2] = fp8x2_to_bf16x2<false>(b.w[0][f][0][2 * h + 1]);
+          wb[3] = fp8x2_to_bf16x2<true>(b.w[0][f][0][2 * h + 1]);
+          const bf16x8 A = __builtin_bit_cast(bf16x8, wb);
 #pragma unroll
-          for (int j = 0; j < FM; ++j) {
+          for (int jj = 0; jj < FM; ++jj)
+            if (jj < fm_live)
+              acc[0][f][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, b.x[jj][h]),
+                                                                      acc[0][f][jj], 0, 0, 0);
+        }
+      }
+    } else {  // OP_A8W8: one 128-K scale group per unit, four fp8 MFMAs
+#pragma unroll
+      for (int f = 0; f < FN; ++f) {
+#pragma unroll
+        for (int jj = 0; jj < FM; ++jj) {
+          if (jj < fm_live) {
             f32x4 t = f32x4{0, 0, 0, 0};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int h = q >> 1, p = (q & 1) * 2;
-              const long A = static_cast<long>((static_cast<unsigned long>(wv[f][h][p + 1]) << 32) | wv[f][h][p]);
-              const long B = static_cast<long>((static_cast<unsigned long>(xv[j][h][p + 1]) << 32) | xv[j][h][p]);
+              const long A = static_cast<long>((static_cast<unsigned long>(b.w[0][f][h][p + 1]) << 32) |
+                                               b.w[0][f][h][p]);
+              const long B = static_cast<long>((static_cast<unsigned long>(b.x[jj][h][p + 1]) << 32) |
+                                               b.x[jj][h][p]);
               t = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(A, B, t, 0, 0, 0);
             }
-            const float s = sx[j] * sw;
+            const float s = b.sx[jj] * b.sw[f];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[0][f][j][e] = __builtin_fmaf(t[e], s, acc[0][f][j][e]);
+            for (int e = 0; e < 4; ++e) acc[0][f][jj][e] = __builtin_fmaf(t[e], s, acc[0][f][jj][e]);
           }
         }
       }
     }
-  }
+  };
+
+  const int rounds = NU > ks ? (NU - ks + KS - 1) / KS : 0;
+  Round buf[P];
+  ring_pipeline<P>(buf, rounds, load, compute);
 
   // ---- combine the K-slices in order through LDS, then the epilogue
   if constexpr (KS > 1) {
@@ -527,55 +611,337 @@ __global__ __launch_bounds__(256) void tile_kernel(const Args a) {
     }
 }
 
+// ============================================================ TILE (LDS x)
+// MFMA tile path for larger M.  The 4 waves of a workgroup split N (each wave
+// owns FN fragments of 16 W rows: 64*FN rows per workgroup) and share one copy
+// of the x chunk in LDS, so x is read from L2 once per 64*FN W rows instead of
+// once per 16.  K is split across S workgroups (grid z) so that the grid still
+// covers every CU; with S > 1 each workgroup writes fp32 partials and
+// splitk_reduce_kernel adds them in a fixed order.  W streams through a ring of
+// P chunks in registers; x chunks pass through registers into a double-
+// buffered LDS tile (one barrier per chunk; on gfx950 the barrier waits only for
+// LDS traffic, so the W loads stay in flight).  A chunk is 64 K (bf16 and fp8
+// weights) or one 128-K scale group (A8W8): 128 bytes of each x row.
+template <int OP>
+struct LdsChunk {
+  static constexpr int value = OP == OP_A8W8 ? 128 : 64;
+};
+constexpr int kLdsRowBytes = 128;          // one x row of a chunk
+constexpr int kLdsRowStride = 144;         // padded: rows start 36 dwords apart
+
+template <int OP, int FM, int FN>
+struct LdsRound {
+  static constexpr int WPF = OP == OP_FP8T ? 1 : 2;          // 16-byte W loads per fragment per chunk
+  static constexpr int XPIECES = 16 * FM * kLdsRowBytes / 16;  // 16-byte pieces of the x chunk
+  static constexpr int XPT = (XPIECES + 255) / 256;           // pieces per thread
+  u32x4 w[op_groups(OP)][FN][WPF];
+  u32x4 x[XPT];
+  float sx[OP == OP_A8W8 ? FM : 1];
+  float sw[OP == OP_A8W8 ? FN : 1];
+};
+
+template <int OP, int FM, int FN, int S, int P>
+__global__ __launch_bounds__(256) void tlds_kernel(const Args a) {
+  constexpr int G = op_groups(OP);
+  constexpr int KCH = LdsChunk<OP>::value;
+  constexpr int WB = op_w_bytes(OP);
+  constexpr int XB = op_x_bytes(OP);
+  using Round = LdsRound<OP, FM, FN>;
+  constexpr int XPIECES = Round::XPIECES;
+  constexpr int XPT = Round::XPT;
+  constexpr int BUFB = 16 * FM * kLdsRowStride;   // bytes of one LDS x buffer
+
+  extern __shared__ __align__(16) unsigned char xl[];   // [2][16*FM][kLdsRowStride]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
+  const int M = a.M, N = a.N, K = a.K;
+  const int m_base = blockIdx.y * 16 * FM;
+  const int nb = blockIdx.x * 64 * FN + wave * 16 * FN;
+  const int split = blockIdx.z;
+  const int kb = a.kb;
+  const int NC = (K + KCH - 1) / KCH;          // chunks along K
+  const int CPS = (NC + S - 1) / S;            // chunks per split
+  const int c_begin = split * CPS;
+  const int rounds = max(0, min(CPS, NC - c_begin));
+
+  const char* wrow[G][FN];
+  int wblk[FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f) {
+    const int n = min(nb + f * 16 + lr, N - 1);
+#pragma unroll
+    for (int g = 0; g < G; ++g) wrow[g][f] = static_cast<const char*>(a.w) + (size_t)(n + g * N) * K * WB;
+    wblk[f] = min(nb + f * 16, N - 1) >> 7;
+  }
+  // x pieces this thread copies into LDS: piece p -> chunk row p/8 (x row
+  // m_base + p/8, clamped to M-1), byte column 16*(p%8)
+  const char* xrowp[XPT];
+  int xcolb[XPT], xdst[XPT];
+  bool xmine[XPT];
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int p = min((int)threadIdx.x + 256 * i, XPIECES - 1);
+    xmine[i] = (int)threadIdx.x + 256 * i < XPIECES;
+    const int r = p >> 3;
+    xcolb[i] = (p & 7) * 16;
+    xrowp[i] = static_cast<const char*>(a.x) + (size_t)min(m_base + r, M - 1) * K * XB;
+    xdst[i] = r * kLdsRowStride + xcolb[i];
+  }
+  int xm[FM];
+#pragma unroll
+  for (int j = 0; j < FM; ++j) xm[j] = min(m_base + j * 16 + lr, M - 1);
+
+  f32x4 acc[G][FN][FM];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) acc[g][f][j] = f32x4{0, 0, 0, 0};
+
+  // K position of this lane's W load h in chunk c (c counts from 0 in this split)
+  auto wk = [&](int c, int h) {
+    const int k0 = (c_begin + c) * KCH;
+    if constexpr (OP == OP_A8W8) return k0 + h * 64 + lq * 16;
+    else if constexpr (OP == OP_FP8T) return k0 + lq * 16;
+    else return k0 + h * 32 + lq * 8;
+  };
+  constexpr int LK = OP == OP_BF16 || OP == OP_GATED ? 8 : 16;   // K per 16-byte W load
+
+  auto load = [&](Round& b, int c) {
+    c = min(c, max(rounds - 1, 0));
+    const int chunk = min(c_begin + c, NC - 1);
+#pragma unroll
+    for (int h = 0; h < Round::WPF; ++h) {
+      const int k = min(wk(c, h), K - LK);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+          b.w[g][f][h] = load_nt(reinterpret_cast<const u32x4*>(wrow[g][f] + (size_t)k * WB));
+    }
+    // x: 16-byte pieces of the 128-byte chunk rows; a piece past K re-reads
+    // the last in-range piece (finite data against zeroed weights)
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int off = min(chunk * KCH * XB + xcolb[i], K * XB - 16);
+      b.x[i] = *reinterpret_cast<const u32x4*>(xrowp[i] + off);
+    }
+    if constexpr (OP == OP_A8W8) {
+#pragma unroll
+      for (int j = 0; j < FM; ++j) b.sx[j] = a.s0[(size_t)xm[j] * kb + chunk];
+#pragma unroll
+      for (int f = 0; f < FN; ++f) b.sw[f] = a.s1[(size_t)wblk[f] * kb + chunk];
+    }
+  };
+
+  auto compute = [&](const Round& b0, int c, auto tail) {
+    Round b = b0;
+    if constexpr (decltype(tail)::value) {        // lanes past K contribute nothing
+#pragma unroll
+      for (int h = 0; h < Round::WPF; ++h) {
+        const bool dead = wk(c, h) >= K;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int f = 0; f < FN; ++f) b.w[g][f][h] = dead ? u32x4{0, 0, 0, 0} : b0.w[g][f][h];
+      }
+    }
+    unsigned char* buf = xl + (c & 1) * BUFB;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i)
+      if (xmine[i]) *reinterpret_cast<u32x4*>(buf + xdst[i]) = b.x[i];
+    __syncthreads();
+    if constexpr (OP == OP_BF16 || OP == OP_GATED) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          const bf16x8 B = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(buf + (j * 16 + lr) * kLdsRowStride + u * 64 + lq * 16));
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int f = 0; f < FN; ++f)
+              acc[g][f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.w[g][f][u]), B,
+                                                                     acc[g][f][j], 0, 0, 0);
+        }
+      }
+    } else if constexpr (OP == OP_FP8T) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 A[FN];
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          u32x4 wb;
+          wb[0] = fp8x2_to_bf16x2<false>(b.w[0][f][0][2 * h]);
+          wb[1] = fp8x2_to_bf16x2<true>(b.w[0][f][0][2 * h]);
+          wb[2] = fp8x2_to_bf16x2<false>(b.w[0][f][0][2 * h + 1]);
+          wb[3] = fp8x2_to_bf16x2<true>(b.w[0][f][0][2 * h + 1]);
+          A[f] = __builtin_bit_cast(bf16x8, wb);
+        }
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          const bf16x8 B = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(buf + (j * 16 + lr) * kLdsRowStride + lq * 32 + h * 16));
+#pragma unroll
+          for (int f = 0; f < FN; ++f)
+            acc[0][f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[f], B, acc[0][f][j], 0, 0, 0);
+        }
+      }
+    } else {  // OP_A8W8: the chunk is one 128-K scale group
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        u32x4 B16[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          B16[h] = *reinterpret_cast<const u32x4*>(buf + (j * 16 + lr) * kLdsRowStride + h * 64 + lq * 16);
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          f32x4 t = f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int h = q >> 1, p = (q & 1) * 2;
+            const long A = static_cast<long>((static_cast<unsigned long>(b.w[0][f][h][p + 1]) << 32) |
+                                             b.w[0][f][h][p]);
+            const long Bv = static_cast<long>((static_cast<unsigned long>(B16[h][p + 1]) << 32) | B16[h][p]);
+            t = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(A, Bv, t, 0, 0, 0);
+          }
+          const float sc = b.sx[j] * b.sw[f];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[0][f][j][e] = __builtin_fmaf(t[e], sc, acc[0][f][j][e]);
+        }
+      }
+    }
+  };
+
+  Round ring[P];
+  ring_pipeline<P>(ring, rounds, load, compute);
+
+  unsigned short* y = static_cast<unsigned short*>(a.y);
+  float scale = 1.0f;
+  if constexpr (OP == OP_FP8T) scale = a.s0[0];
+#pragma unroll
+  for (int f = 0; f < FN; ++f)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int m = m_base + j * 16 + lr;
+      if (m >= M) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n = nb + f * 16 + lq * 4 + e;
+        if (n >= N) continue;
+        if constexpr (S == 1) {
+          float v = acc[0][f][j][e];
+          if constexpr (OP == OP_GATED) v = silu_f32(v) * acc[G - 1][f][j][e];
+          if constexpr (OP == OP_FP8T) v *= scale;
+          y[(size_t)m * N + n] = f32_to_bf16(v);
+        } else {
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            a.ws[(((size_t)split * G + g) * M + m) * N + n] = acc[g][f][j][e];
+        }
+      }
+    }
+}
+
+// Sum of the S split-K partials in a fixed order, then the epilogue.
+template <int OP>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const Args a, int S) {
+  constexpr int G = op_groups(OP);
+  const size_t MN = (size_t)a.M * a.N;
+  float scale = 1.0f;
+  if constexpr (OP == OP_FP8T) scale = a.s0[0];
+  unsigned short* y = static_cast<unsigned short*>(a.y);
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < MN; i += (size_t)gridDim.x * 256) {
+    float v = 0.0f, u = 0.0f;
+    for (int s = 0; s < S; ++s) {
+      v += a.ws[((size_t)s * G) * MN + i];
+      if constexpr (G == 2) u += a.ws[((size_t)s * G + 1) * MN + i];
+    }
+    if constexpr (OP == OP_GATED) v = silu_f32(v) * u;
+    if constexpr (OP == OP_FP8T) v *= scale;
+    y[i] = f32_to_bf16(v);
+  }
+}
+
 // y = 0 (the empty sum, K == 0).
 __global__ void zero_kernel(unsigned short* y, size_t n);
 
 // ------------------------------------------------------------- launch tables
 typedef hipError_t (*LaunchFn)(const Args&, hipStream_t);
 
-template <int OP, int MT, int R, int KS, int U>
+template <int OP, int MT, int R, int KS, int P>
 hipError_t launch_gemv(const Args& a, hipStream_t s) {
   constexpr int RPW = (4 / KS) * R;
   const unsigned grid = (unsigned)((a.N + RPW - 1) / RPW);
   const size_t smem = OP == OP_A8W8 ? (size_t)(MT + 1) * a.kb * sizeof(float) : 0;
-  hipLaunchKernelGGL((gemv_kernel<OP, MT, R, KS, U>), dim3(grid), dim3(256), smem, s, a);
+  hipLaunchKernelGGL((gemv_kernel<OP, MT, R, KS, P>), dim3(grid), dim3(256), smem, s, a);
   return hipGetLastError();
 }
 
-template <int OP, int FM, int FN, int KS, int U>
+template <int OP, int FM, int FN, int KS, int P>
 hipError_t launch_tile(const Args& a, hipStream_t s) {
   constexpr int RPW = (4 / KS) * FN * 16;
   const unsigned gx = (unsigned)((a.N + RPW - 1) / RPW);
   const unsigned gy = (unsigned)((a.M + 16 * FM - 1) / (16 * FM));
   const size_t smem = (size_t)tile_red_bytes(OP, FM, FN, KS);
-  hipLaunchKernelGGL((tile_kernel<OP, FM, FN, KS, U>), dim3(gx, gy), dim3(256), smem, s, a);
+  hipLaunchKernelGGL((tile_kernel<OP, FM, FN, KS, P>), dim3(gx, gy), dim3(256), smem, s, a);
   return hipGetLastError();
 }
 
-template <int OP, int MT, int R, int KS, int U>
+template <int OP, int FM, int FN, int S, int P>
+hipError_t launch_tlds(const Args& a, hipStream_t s) {
+  const unsigned gx = (unsigned)((a.N + 64 * FN - 1) / (64 * FN));
+  const unsigned gy = (unsigned)((a.M + 16 * FM - 1) / (16 * FM));
+  const size_t smem = (size_t)2 * 16 * FM * kLdsRowStride;
+  hipLaunchKernelGGL((tlds_kernel<OP, FM, FN, S, P>), dim3(gx, gy, S), dim3(256), smem, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  const size_t mn = (size_t)a.M * a.N;
+  const unsigned rg = (unsigned)std::min<size_t>((mn + 255) / 256, 2048);
+  hipLaunchKernelGGL((splitk_reduce_kernel<OP>), dim3(rg), dim3(256), 0, s, a, S);
+  return hipGetLastError();
+}
+
+template <int OP, int MT, int R, int KS, int P>
 constexpr LaunchFn gemv_fn() {
-  if constexpr (gemv_valid(OP, MT, R, KS, U)) return &launch_gemv<OP, MT, R, KS, U>;
+  if constexpr (gemv_valid(OP, MT, R, KS, P)) return &launch_gemv<OP, MT, R, KS, P>;
   else return nullptr;
 }
-template <int OP, int FM, int FN, int KS, int U>
+template <int OP, int FM, int FN, int KS, int P>
 constexpr LaunchFn tile_fn() {
-  if constexpr (tile_valid(OP, FM, FN, KS, U)) return &launch_tile<OP, FM, FN, KS, U>;
+  if constexpr (tile_valid(OP, FM, FN, KS, P)) return &launch_tile<OP, FM, FN, KS, P>;
+  else return nullptr;
+}
+
+template <int OP, int FM, int FN, int S, int P>
+constexpr LaunchFn tlds_fn() {
+  if constexpr (tlds_valid(OP, FM, FN, S, P)) return &launch_tlds<OP, FM, FN, S, P>;
   else return nullptr;
 }
 
 struct GemvRow { LaunchFn f[kNumGemvMT]; };
 struct TileRow { LaunchFn f[kNumTileFM]; };
 
-template <int OP, int R, int KS, int U>
+template <int OP, int R, int KS, int P>
 constexpr GemvRow gemv_row() {
-  return GemvRow{{gemv_fn<OP, 1, R, KS, U>(), gemv_fn<OP, 2, R, KS, U>(), gemv_fn<OP, 3, R, KS, U>(),
-                  gemv_fn<OP, 4, R, KS, U>(), gemv_fn<OP, 6, R, KS, U>(), gemv_fn<OP, 8, R, KS, U>(),
-                  gemv_fn<OP, 12, R, KS, U>(), gemv_fn<OP, 16, R, KS, U>()}};
+  return GemvRow{{gemv_fn<OP, 1, R, KS, P>(), gemv_fn<OP, 2, R, KS, P>(), gemv_fn<OP, 3, R, KS, P>(),
+                  gemv_fn<OP, 4, R, KS, P>(), gemv_fn<OP, 6, R, KS, P>(), gemv_fn<OP, 8, R, KS, P>(),
+                  gemv_fn<OP, 12, R, KS, P>(), gemv_fn<OP, 16, R, KS, P>()}};
 }
-template <int OP, int FN, int KS, int U>
+template <int OP, int FN, int KS, int P>
 constexpr TileRow tile_row() {
-  return TileRow{{tile_fn<OP, 1, FN, KS, U>(), tile_fn<OP, 2, FN, KS, U>(), tile_fn<OP, 4, FN, KS, U>(),
-                  tile_fn<OP, 6, FN, KS, U>(), tile_fn<OP, 8, FN, KS, U>()}};
+  return TileRow{{tile_fn<OP, 1, FN, KS, P>(), tile_fn<OP, 2, FN, KS, P>(), tile_fn<OP, 4, FN, KS, P>(),
+                  tile_fn<OP, 6, FN, KS, P>(), tile_fn<OP, 8, FN, KS, P>()}};
+}
+
+template <int OP, int FN, int S, int P>
+constexpr TileRow tlds_row() {
+  return TileRow{{tlds_fn<OP, 1, FN, S, P>(), tlds_fn<OP, 2, FN, S, P>(), tlds_fn<OP, 4, FN, S, P>(),
+                  tlds_fn<OP, 6, FN, S, P>(), tlds_fn<OP, 8, FN, S, P>()}};
 }
 
 // Launch tables, one pair per op, defined in ops_<op>.hip:
@@ -590,5 +956,10 @@ template <> const TileRow* tile_table<OP_BF16>();
 template <> const TileRow* tile_table<OP_GATED>();
 template <> const TileRow* tile_table<OP_FP8T>();
 template <> const TileRow* tile_table<OP_A8W8>();
+template <int OP> const TileRow* tlds_table();
+template <> const TileRow* tlds_table<OP_BF16>();
+template <> const TileRow* tlds_table<OP_GATED>();
+template <> const TileRow* tlds_table<OP_FP8T>();
+template <> const TileRow* tlds_table<OP_A8W8>();
 
 }  // namespace skg

@@ -7,20 +7,34 @@ namespace {
 constexpr GemvRow kGemv[kNumGemv] = {
 #define SKG_GEMV(name, R, KS, U) gemv_row<OP_A8W8, R, KS, U>(),
 #define SKG_TILE(name, FN, KS, U)
+#define SKG_TLDS(name, FN, S, P)
 #include "variants.def"
 #undef SKG_GEMV
 #undef SKG_TILE
+#undef SKG_TLDS
 };
 constexpr TileRow kTile[kNumTile] = {
 #define SKG_GEMV(name, R, KS, U)
 #define SKG_TILE(name, FN, KS, U) tile_row<OP_A8W8, FN, KS, U>(),
+#define SKG_TLDS(name, FN, S, P)
 #include "variants.def"
 #undef SKG_GEMV
 #undef SKG_TILE
+#undef SKG_TLDS
+};
+constexpr TileRow kTlds[kNumTlds] = {
+#define SKG_GEMV(name, R, KS, U)
+#define SKG_TILE(name, FN, KS, U)
+#define SKG_TLDS(name, FN, S, P) tlds_row<OP_A8W8, FN, S, P>(),
+#include "variants.def"
+#undef SKG_GEMV
+#undef SKG_TILE
+#undef SKG_TLDS
 };
 }  // namespace
 
 template <> const GemvRow* gemv_table<OP_A8W8>() { return kGemv; }
 template <> const TileRow* tile_table<OP_A8W8>() { return kTile; }
+template <> const TileRow* tlds_table<OP_A8W8>() { return kTlds; }
 
 }  // namespace skg

@@ -310,22 +310,33 @@ int Table::load(const std::string& path, const Identity& self, std::string* err)
 // --------------------------------------------------------------- defaults
 // The untuned entry point: the VALU weight stream below 16 rows, the MFMA
 // tile path from 16 rows, with a shape rule for each.
+int default_variant_no_ws(int op, int M, int N, int K) {
+  (void)N;
+  (void)K;
+  for (int i = 0; i < kNumVariants; ++i)
+    if (kVariants[i].family == FAM_TILE && variant_supports(op, i, M)) return i;
+  for (int i = 0; i < kNumVariants; ++i)
+    if (kVariants[i].family == FAM_GEMV && variant_supports(op, i, M)) return i;
+  return -1;
+}
+
 int default_variant(int op, int M, int N, int K) {
   (void)K;
-  const char* name;
-  if (M < 16) {
-    const bool small_n = N <= 2048;
-    if (op == OP_GATED) name = M <= 4 ? "gemv_r1_k4_u2" : "gemv_r2_k4_u1";
-    else if (M <= 2) name = small_n ? "gemv_r1_k4_u2" : "gemv_r2_k4_u2";
-    else if (M <= 8) name = small_n ? "gemv_r2_k4_u2" : "gemv_r4_k4_u1";
-    else name = "gemv_r4_k4_u1";
-  } else {
-    name = (M <= 32) ? "tile_f1_k4_u2" : "tile_f1_k4_u2";
+  (void)N;
+  // Preference lists: the first variant compiled for (op, M) wins.
+  static const char* const kGemvPref[] = {"gemv_r2_k4_p4", "gemv_r2_k4_p2", "gemv_r4_k4_p2", "gemv_r4_k4_p1",
+                                          "gemv_r2_k4_p1", "gemv_r1_k4_p2"};
+  static const char* const kGemvPrefLarge[] = {"gemv_r4_k4_p2", "gemv_r4_k4_p1", "gemv_r2_k4_p2", "gemv_r2_k4_p1",
+                                               "gemv_r1_k4_p2"};
+  static const char* const kTilePref[] = {"tile_f1_k4_p16", "tile_f1_k4_p8", "tile_f1_k4_p4", "tile_f1_k4_p2"};
+  const bool gemv = !tile_rows(M);
+  const char* const* pref = gemv ? (M <= 2 ? kGemvPref : kGemvPrefLarge) : kTilePref;
+  const int npref = gemv ? (M <= 2 ? 6 : 5) : 4;
+  for (int i = 0; i < npref; ++i) {
+    const int v = variant_from_name(pref[i]);
+    if (v >= 0 && variant_supports(op, v, M)) return v;
   }
-  int v = variant_from_name(name);
-  if (v >= 0 && variant_supports(op, v, M)) return v;
-  // first compiled variant of the right family that supports M
-  const int fam = M < 16 ? FAM_GEMV : FAM_TILE;
+  const int fam = gemv ? FAM_GEMV : FAM_TILE;
   for (int i = 0; i < kNumVariants; ++i)
     if (kVariants[i].family == fam && variant_supports(op, i, M)) return i;
   for (int i = 0; i < kNumVariants; ++i)

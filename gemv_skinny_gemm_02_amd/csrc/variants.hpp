@@ -7,7 +7,7 @@
 namespace skg {
 
 enum Op : int { OP_BF16 = 0, OP_GATED = 1, OP_FP8T = 2, OP_A8W8 = 3, NUM_OPS = 4 };
-enum Family : int { FAM_GEMV = 0, FAM_TILE = 1 };
+enum Family : int { FAM_GEMV = 0, FAM_TILE = 1, FAM_TLDS = 2 };
 
 // Rows buckets: M is rounded up to the next one (padded-M lookup with no
 // nearest fallback: DeepSeek-V4-flash decode round 3, "Retained change 2";
@@ -53,21 +53,57 @@ constexpr int op_xd(int op) { return op_kc(op) * op_x_bytes(op) / 4; }
 // K multiple the op requires (one 16-byte load per lane never straddles K).
 constexpr int op_k_multiple(int op) { return op_kc(op); }
 
-// Register budgets that keep a variant compiled for a bucket (per lane).
-constexpr bool gemv_valid(int op, int MT, int R, int KS, int U) {
+// Register budgets that keep a variant compiled for a bucket (per lane, in
+// 32-bit registers): accumulators plus P rounds of weight and x loads.
+constexpr int kRegBudget = 200;
+constexpr int gemv_regs(int op, int MT, int R, int P) {
   const int G = op_groups(op);
-  return (KS == 1 || KS == 2 || KS == 4) && MT * R * G <= 64 && U * R * G * 4 <= 32 &&
-         U * MT * op_xd(op) <= 96 && (128 % ((4 / KS) * R)) == 0;
+  return P * (R * G * 4 + MT * op_xd(op)) + MT * R * G;
+}
+constexpr bool gemv_valid(int op, int MT, int R, int KS, int P) {
+  const int G = op_groups(op);
+  return (KS == 1 || KS == 2 || KS == 4) && P >= 1 && MT * R * G <= 64 &&
+         gemv_regs(op, MT, R, P) <= kRegBudget && (128 % ((4 / KS) * R)) == 0;
 }
 constexpr int tile_red_bytes(int op, int FM, int FN, int KS) {
   return (4 / KS) * (KS - 1) * op_groups(op) * FN * FM * 4 * 64 * 4;
 }
-constexpr bool tile_valid(int op, int FM, int FN, int KS, int U) {
+constexpr int tile_regs(int op, int FM, int FN, int P) {
   const int G = op_groups(op);
-  return (KS == 1 || KS == 2 || KS == 4) && G * FN * FM * 4 <= 128 &&
-         tile_red_bytes(op, FM, FN, KS) <= 65536 && U >= 1 &&
+  const int per_unit = op == OP_A8W8 ? FN * 8 + FM * 8 + FM + FN
+                                     : (op == OP_FP8T ? FN * 4 + FM * 8 : G * FN * 4 + FM * 4);
+  return P * per_unit + G * FN * FM * 4;
+}
+constexpr bool tile_valid(int op, int FM, int FN, int KS, int P) {
+  const int G = op_groups(op);
+  return (KS == 1 || KS == 2 || KS == 4) && P >= 1 && G * FN * FM * 4 <= 128 &&
+         tile_regs(op, FM, FN, P) <= kRegBudget && tile_red_bytes(op, FM, FN, KS) <= 65536 &&
          (128 % ((4 / KS) * FN * 16)) == 0;
 }
+// LDS-shared-x tile path (tlds): 64*FN W rows per workgroup, S-way split-K.
+constexpr int tlds_xpt(int FM) { return (16 * FM * 8 + 255) / 256; }
+constexpr int tlds_regs(int op, int FM, int FN, int P) {
+  const int G = op_groups(op);
+  const int wpf = op == OP_FP8T ? 1 : 2;
+  const int per_chunk = G * FN * wpf * 4 + tlds_xpt(FM) * 4 + (op == OP_A8W8 ? FM + FN : 0);
+  const int acc = G * FN * FM * 4;
+  return P * per_chunk + acc * (op == OP_A8W8 ? 2 : 1) + FM * 4;
+}
+constexpr bool tlds_valid(int op, int FM, int FN, int S, int P) {
+  const int G = op_groups(op);
+  return (S == 1 || S == 2 || S == 4 || S == 8) && P >= 1 && G * FN * FM * 4 <= 128 &&
+         tlds_regs(op, FM, FN, P) <= 224 && (128 % (64 * FN)) == 0;
+}
+// Bytes of split-K partials a tlds launch with S > 1 needs.
+constexpr unsigned long long tlds_ws_bytes(int op, int S, int M, int N) {
+  return S > 1 ? (unsigned long long)S * op_groups(op) * M * N * 4ull : 0ull;
+}
+
+// The MFMA tile path serves the rows buckets from 16 up (M = 13..128, and any M
+// above 128): below that the problem is a weight stream with too few rows to
+// fill a 16-wide fragment, and the VALU path serves it.
+constexpr int kTileMinBucket = 16;
+constexpr bool tile_rows(int M) { return M > kMaxBucket || bucket_of(M) >= kTileMinBucket; }
 
 struct VariantDesc {
   const char* name;
@@ -78,9 +114,11 @@ struct VariantDesc {
 constexpr VariantDesc kVariants[] = {
 #define SKG_GEMV(name, R, KS, U) {#name, FAM_GEMV, R, KS, U},
 #define SKG_TILE(name, FN, KS, U) {#name, FAM_TILE, FN, KS, U},
+#define SKG_TLDS(name, FN, S, P) {#name, FAM_TLDS, FN, S, P},
 #include "variants.def"
 #undef SKG_GEMV
 #undef SKG_TILE
+#undef SKG_TLDS
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -91,6 +129,7 @@ constexpr int count_family(int fam) {
 }
 constexpr int kNumGemv = count_family(FAM_GEMV);
 constexpr int kNumTile = count_family(FAM_TILE);
+constexpr int kNumTlds = count_family(FAM_TLDS);
 // index of variant i inside its family's launch table
 constexpr int family_index(int i) {
   int n = 0;
@@ -105,22 +144,27 @@ constexpr bool variant_supports(int op, int i, int M) {
     const int mi = gemv_mt_index(M);
     return mi >= 0 && gemv_valid(op, kGemvMT[mi], v.p0, v.p1, v.p2);
   }
+  if (!tile_rows(M)) return false;
   const int fm = M > kMaxBucket ? kNumTileFM - 1 : tile_fm_index(M);
+  if (v.family == FAM_TLDS) return tlds_valid(op, kTileFM[fm], v.p0, v.p1, v.p2);
   return tile_valid(op, kTileFM[fm], v.p0, v.p1, v.p2);
 }
 
 // FNV-1a over the list's text: the kernel-selection-space token.
 constexpr uint32_t fnv1a(const char* s, uint32_t h = 2166136261u) {
-  return *s ? fnv1a(s + 1, (h ^ static_cast<uint8_t>(*s)) * 16777619u) : h;
+  for (; *s; ++s) h = (h ^ static_cast<uint8_t>(*s)) * 16777619u;
+  return h;
 }
 constexpr const char kSpaceText[] =
     "buckets=1,2,3,4,6,8,12,16,24,32,64,96,128;gemv_mt=1,2,3,4,6,8,12,16;tile_fm=1,2,4,6,8;"
 #define SKG_GEMV(name, R, KS, U) "G:" #name "," #R "," #KS "," #U ";"
 #define SKG_TILE(name, FN, KS, U) "T:" #name "," #FN "," #KS "," #U ";"
+#define SKG_TLDS(name, FN, S, P) "L:" #name "," #FN "," #S "," #P ";"
 #include "variants.def"
 #undef SKG_GEMV
 #undef SKG_TILE
-    "kernels=2";  // bump when a kernel's arithmetic or indexing changes
+#undef SKG_TLDS
+    "kernels=4";  // bump when a kernel's arithmetic or indexing changes
 constexpr uint32_t kSpaceToken = fnv1a(kSpaceText);
 
 }  // namespace skg

@@ -1,0 +1,95 @@
+"""Summaries of rocprofv3 output for this library's kernels.
+
+    python -m gemv_skinny_gemm_02_amd.profsum trace KERNEL_STATS.csv [--cmd CMD]
+    python -m gemv_skinny_gemm_02_amd.profsum counters --fetch FETCH.csv --write WRITE.csv \
+        --code-hash HASH [--cmd CMD]
+
+`trace` prints the per-kernel call count and average/min/max duration from a
+`--kernel-trace --stats` run.  `counters` turns two `--pmc FETCH_SIZE` and
+`--pmc WRITE_SIZE` runs into KiB per dispatch for each kernel, and calibrates
+both counters on the run's 256 MiB device-to-device copy (a copy of known size
+reads and writes 262144 KiB): the factor is what the counter reads for that
+copy divided by 262144.  HBM bytes per launch = FETCH/fetch_factor +
+WRITE/write_factor, in KiB.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import statistics
+import sys
+from collections import defaultdict
+
+COPY_KIB = 256 * 1024
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def trace_summary(path: str, cmd: str | None) -> str:
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = []
+    if cmd:
+        out.append(f"# command: {cmd}")
+    out.append("# kernel | calls | avg_us | min_us | max_us | total_ms | percent")
+    for r in rows:
+        out.append(f"{r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | {float(r['MinNs']) / 1e3:.3f} | "
+                   f"{float(r['MaxNs']) / 1e3:.3f} | {float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f}")
+    return "\n".join(out) + "\n"
+
+
+def _per_kernel(path: str, counter: str):
+    vals = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return vals
+
+
+def _copy_factor(vals) -> float:
+    cand = [v for v in vals.get(COPY_KERNEL, []) if 0.5 * COPY_KIB <= v <= 2.0 * COPY_KIB]
+    if not cand:
+        raise SystemExit("no 256 MiB copy dispatch found for calibration")
+    return statistics.median(cand) / COPY_KIB
+
+
+def counters_summary(fetch: str, write: str, code_hash: str, cmd: str | None) -> str:
+    fv, wv = _per_kernel(fetch, "FETCH_SIZE"), _per_kernel(write, "WRITE_SIZE")
+    ff, wf = _copy_factor(fv), _copy_factor(wv)
+    out = []
+    if cmd:
+        out.append(f"# command: {cmd}")
+    out.append("# FETCH_SIZE and WRITE_SIZE in KiB per dispatch (mean over the kernel's dispatches);")
+    out.append("# HBM bytes per launch = (FETCH/copy_fetch_factor + WRITE/copy_write_factor) * 1024")
+    out.append(f"code_hash={code_hash}")
+    out.append(f"copy_fetch_factor={ff:.6f}")
+    out.append(f"copy_write_factor={wf:.6f}")
+    for name in sorted(set(fv) | set(wv)):
+        if not name.startswith("void skg::"):
+            continue
+        f = statistics.fmean(fv[name]) if fv.get(name) else float("nan")
+        w = statistics.fmean(wv[name]) if wv.get(name) else float("nan")
+        out.append(f"kernel {name} | {f:.3f} | {w:.3f}")
+    return "\n".join(out) + "\n"
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("stats")
+    t.add_argument("--cmd")
+    c = sub.add_parser("counters")
+    c.add_argument("--fetch", required=True)
+    c.add_argument("--write", required=True)
+    c.add_argument("--code-hash", required=True)
+    c.add_argument("--cmd")
+    a = ap.parse_args(argv)
+    if a.mode == "trace":
+        sys.stdout.write(trace_summary(a.stats, a.cmd))
+    else:
+        sys.stdout.write(counters_summary(a.fetch, a.write, a.code_hash, a.cmd))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -47,6 +47,14 @@
  *           MFMA tile path in chunks of 128 rows.
  * Threads.  GEMM calls are reentrant.  skinny_gemm_load_table must not run
  *           concurrently with other calls.
+ * Workspace. Variants that split K across workgroups keep fp32 partials in a
+ *           per-device buffer the library allocates once (64 MiB, more if a
+ *           call needs it, at most 256 MiB) on the first call on the device
+ *           that is not under graph capture; it lives until the process
+ *           ends.  Calls on one stream share it safely.  Calls that run
+ *           concurrently on different streams of one device race on it.  A
+ *           call that would need to allocate it while the stream is being
+ *           captured uses a variant that needs no workspace instead.
  */
 #ifndef SKINNY_GEMM_H
 #define SKINNY_GEMM_H

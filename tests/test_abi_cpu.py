@@ -53,9 +53,9 @@ def _write(tmp_path, ident, entries, name="t.json", drop=()):
     return str(path)
 
 
-E1 = [{"op": "bf16", "rows": 8, "N": 4096, "K": 4096, "choice": "gemv_r1_k4_u2",
-       "candidates": {"gemv_r1_k4_u2": {"us": 5.0}, "gemv_r4_k4_u1": {"us": 6.0}}},
-      {"op": "gated", "rows": 16, "N": 12288, "K": 4096, "choice": "tile_f2_k4_u1"}]
+E1 = [{"op": "bf16", "rows": 8, "N": 4096, "K": 4096, "choice": "gemv_r1_k4_p2",
+       "candidates": {"gemv_r1_k4_p2": {"us": 5.0}, "gemv_r4_k4_p1": {"us": 6.0}}},
+      {"op": "gated", "rows": 16, "N": 12288, "K": 4096, "choice": "tile_f2_k4_p4"}]
 
 
 def test_variants_and_buckets():
@@ -66,10 +66,14 @@ def test_variants_and_buckets():
     for op in skg.OPS:
         for M in range(1, 301):
             assert any(skg.skinny_gemm_variant_supports(op, i, M) for i in range(len(names))), (op, M)
-    # GEMV variants never claim rows above 16
+    # GEMV variants never claim rows above 16; tile variants start at the
+    # rows-16 bucket (M = 13)
     for i, n in enumerate(names):
         if n.startswith("gemv_"):
             assert not skg.skinny_gemm_variant_supports("bf16", i, 17)
+        else:
+            assert not skg.skinny_gemm_variant_supports("bf16", i, 12)
+            assert skg.skinny_gemm_variant_supports("bf16", i, 13)
 
 
 def test_table_engaged_lookup_and_buckets(tmp_path):
@@ -80,11 +84,11 @@ def test_table_engaged_lookup_and_buckets(tmp_path):
     assert engaged and status.startswith("engaged 2 shapes")
     # M in (6, 8] rounds up to the rows-8 bucket; no nearest fallback outside it
     for M in (7, 8):
-        assert skg.skinny_gemm_query("bf16", M, 4096, 4096) == ("gemv_r1_k4_u2", "table")
+        assert skg.skinny_gemm_query("bf16", M, 4096, 4096) == ("gemv_r1_k4_p2", "table")
     for M in (6, 9, 12):
         assert skg.skinny_gemm_query("bf16", M, 4096, 4096)[1] == "default"
     assert skg.skinny_gemm_query("bf16", 8, 4096, 4095)[1] == "default"
-    assert skg.skinny_gemm_query("gated", 13, 12288, 4096) == ("tile_f2_k4_u1", "table")
+    assert skg.skinny_gemm_query("gated", 13, 12288, 4096) == ("tile_f2_k4_p4", "table")
     assert skg.skinny_gemm_query("fp8_tensor", 8, 4096, 4096)[1] == "default"
 
 
@@ -118,7 +122,7 @@ def test_table_refusals(tmp_path, case, needle):
     elif case == "bucket":
         entries[0]["rows"] = 5
     elif case == "unsupported":
-        entries[1]["choice"] = "gemv_r8_k4_u1"
+        entries[1]["choice"] = "gemv_r8_k4_p1"
     p = _write(tmp_path, table_ident, entries, drop=drop)
     code = f"""
 import gemv_skinny_gemm_02_amd as skg
@@ -141,14 +145,14 @@ def test_force_knob_refuses_table(tmp_path):
 import gemv_skinny_gemm_02_amd as skg
 skg.skinny_gemm_load_table_as({p!r}, {ident!r})
 assert not skg.skinny_gemm_table_status()[0]
-assert skg.skinny_gemm_query('bf16', 3, 4096, 4096) == ('gemv_r4_k1_u1', 'force')
+assert skg.skinny_gemm_query('bf16', 3, 4096, 4096) == ('gemv_r4_k1_p2', 'force')
 # a forced variant that cannot run the rows falls back to the default
 assert skg.skinny_gemm_query('bf16', 40, 4096, 4096)[1] == 'default'
 """
-    env = dict(os.environ, SKINNY_GEMM_FORCE="gemv_r4_k1_u1")
+    env = dict(os.environ, SKINNY_GEMM_FORCE="gemv_r4_k1_p2")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, env=env)
     assert r.returncode == 0, r.stderr
-    assert "SKINNY_GEMM_FORCE=gemv_r4_k1_u1 reroutes the dispatch" in r.stderr
+    assert "SKINNY_GEMM_FORCE=gemv_r4_k1_p2 reroutes the dispatch" in r.stderr
 
 
 def test_malformed_and_missing(tmp_path):
@@ -172,5 +176,5 @@ def test_defaults_follow_the_rows_rule():
     for op in skg.OPS:
         for M in (1, 2, 3, 4, 6, 8, 12):
             assert skg.skinny_gemm_query(op, M, 4096, 4096)[0].startswith("gemv_"), (op, M)
-        for M in (16, 24, 32, 64, 96, 128, 129, 1000):
+        for M in (13, 16, 24, 32, 64, 96, 128, 129, 1000):
             assert skg.skinny_gemm_query(op, M, 4096, 4096)[0].startswith("tile_"), (op, M)

@@ -93,12 +93,12 @@ def test_status_codes():
     assert st == 1
     # a variant that is not compiled for the rows bucket
     names = skg.variants("gated")
-    st, _ = _raw("skinny_gemm_run_variant", 1, names.index("gemv_r4_k4_u1"), None, x.data_ptr(), w.data_ptr(),
+    st, _ = _raw("skinny_gemm_run_variant", 1, names.index("gemv_r4_k4_p1"), None, x.data_ptr(), w.data_ptr(),
                  None, None, y.data_ptr(), 2, 8, 64, s)
     assert st == 0
     xw = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
     yw = torch.zeros((16, 8), dtype=torch.bfloat16, device="cuda")
-    st, _ = _raw("skinny_gemm_run_variant", 1, names.index("gemv_r4_k4_u1"), None, xw.data_ptr(), w.data_ptr(),
+    st, _ = _raw("skinny_gemm_run_variant", 1, names.index("gemv_r4_k4_p1"), None, xw.data_ptr(), w.data_ptr(),
                  None, None, yw.data_ptr(), 16, 8, 64, s)
     assert st == 2
 
