@@ -246,6 +246,7 @@ LaunchFn variant_fn(int op, int v, int M) {
 // calls that run concurrently on different streams of one device race on it.
 constexpr size_t kWsCap = 256ull << 20;
 constexpr size_t kWsInit = 64ull << 20;
+constexpr size_t kCntBytes = (size_t)kSplitCounters * sizeof(unsigned);  // counters precede the partials
 std::mutex g_ws_mu;
 std::map<int, std::pair<void*, size_t>> g_ws;
 
@@ -272,7 +273,7 @@ float* workspace(hipStream_t s, size_t bytes, std::string* why) {
   }
   std::lock_guard<std::mutex> lk(g_ws_mu);
   auto& e = g_ws[dev];
-  if (e.first && e.second >= bytes) return static_cast<float*>(e.first);
+  if (e.first && e.second >= bytes + kCntBytes) return static_cast<float*>(e.first);
   if (capturing(s)) {
     *why = "the split-K workspace must be allocated outside graph capture (make one call eagerly first)";
     return nullptr;
@@ -282,11 +283,18 @@ float* workspace(hipStream_t s, size_t bytes, std::string* why) {
     (void)hipFree(e.first);
     e = {nullptr, 0};
   }
-  const size_t want = std::max(bytes, kWsInit);
+  const size_t want = std::max(bytes + kCntBytes, kWsInit);
   void* p = nullptr;
   if (hipMalloc(&p, want) != hipSuccess) {
     (void)hipGetLastError();
     *why = "hipMalloc of the split-K workspace failed";
+    return nullptr;
+  }
+  // the arrival counters start at zero; each launch leaves them at zero
+  if (hipMemset(p, 0, kCntBytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(p);
+    *why = "clearing the split-K counters failed";
     return nullptr;
   }
   e = {p, want};
@@ -322,9 +330,13 @@ skg_status launch(int op, int v, const Args& a_in, hipStream_t s) {
   if (fn && kVariants[v].family == FAM_TLDS) {
     const size_t need = (size_t)tlds_ws_bytes(op, kVariants[v].p1, a.M, a.N);
     if (need) {
+      if (tlds_tiles(kVariants[v].p0, a.M, a.N) > (unsigned long long)kSplitCounters)
+        return fail(SKG_EUNSUPPORTED, "%s: more output tiles than split-K counters", kVariants[v].name);
       std::string why;
-      a.ws = workspace(s, need, &why);
-      if (!a.ws) return fail(SKG_EUNSUPPORTED, "%s: %s", kVariants[v].name, why.c_str());
+      float* base = workspace(s, need, &why);
+      if (!base) return fail(SKG_EUNSUPPORTED, "%s: %s", kVariants[v].name, why.c_str());
+      a.cnt = reinterpret_cast<unsigned*>(base);
+      a.ws = reinterpret_cast<float*>(reinterpret_cast<char*>(base) + kCntBytes);
     }
   }
   if (fn && op == OP_A8W8 && kVariants[v].family == FAM_GEMV) {
@@ -343,7 +355,7 @@ skg_status launch(int op, int v, const Args& a_in, hipStream_t s) {
 
 skg_status run_op(int op, const void* x, const void* w, const float* s0, const float* s1, void* y, int M, int N,
                   int K, hipStream_t s) {
-  Args a{x, w, s0, s1, y, M, N, K, (K + 127) / 128, nullptr};
+  Args a{x, w, s0, s1, y, M, N, K, (K + 127) / 128, nullptr, nullptr};
   if (op != OP_FP8T && op != OP_A8W8) a.s0 = nullptr;
   if (op != OP_A8W8) a.s1 = nullptr;
   if (skg_status st = validate(op, a)) return st;
@@ -468,7 +480,7 @@ skg_status skinny_gemm_run_variant(int op, int variant, const int* knobs, const 
   if (!op_name(op)) return fail(SKG_EINVAL, "unknown op %d", op);
   if (variant < 0 || variant >= kNumVariants) return fail(SKG_EINVAL, "no variant %d", variant);
   if (knobs) return fail(SKG_EINVAL, "knobs are reserved: pass NULL");
-  Args a{x, W, s0, s1, y, M, N, K, (K + 127) / 128, nullptr};
+  Args a{x, W, s0, s1, y, M, N, K, (K + 127) / 128, nullptr, nullptr};
   if (op != OP_FP8T && op != OP_A8W8) a.s0 = nullptr;
   if (op != OP_A8W8) a.s1 = nullptr;
   if (skg_status st = validate(op, a)) return st;

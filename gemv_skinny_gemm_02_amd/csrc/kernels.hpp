@@ -41,6 +41,7 @@ struct Args {
   int M, N, K;
   int kb;           // ceil(K / 128): scale groups along K
   float* ws;        // split-K partials [S][G][M][N] fp32 (tlds variants with S > 1)
+  unsigned* cnt;    // split-K arrival counters, one per output tile, zero between calls
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -78,6 +79,13 @@ __device__ __forceinline__ float silu_f32(float g) {
 }
 
 __device__ __forceinline__ u32x4 load_nt(const u32x4* p) { return __builtin_nontemporal_load(p); }
+
+// Buffer resource over [p, p + bytes) for raw buffer loads/stores; cache
+// policy bit 4 (sc1) makes an access device-coherent across the XCDs' L2s.
+constexpr int kCoherent = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
 
 // ------------------------------------------- fixed-order cross-lane reduction
 // Reduce-scatter of VC per-lane values over the 64 lanes of a wave.  While the
@@ -616,12 +624,22 @@ __global__ __launch_bounds__(256) void tile_kernel(const Args a) {
 // owns FN fragments of 16 W rows: 64*FN rows per workgroup) and share one copy
 // of the x chunk in LDS, so x is read from L2 once per 64*FN W rows instead of
 // once per 16.  K is split across S workgroups (grid z) so that the grid still
-// covers every CU; with S > 1 each workgroup writes fp32 partials and
-// splitk_reduce_kernel adds them in a fixed order.  W streams through a ring of
+// covers every CU; with S > 1 the workgroups of a tile combine their fp32
+// partials as described below.  W streams through a ring of
 // P chunks in registers; x chunks pass through registers into a double-
 // buffered LDS tile (one barrier per chunk; on gfx950 the barrier waits only for
 // LDS traffic, so the W loads stay in flight).  A chunk is 64 K (bf16 and fp8
 // weights) or one 128-K scale group (A8W8): 128 bytes of each x row.
+//
+// Split-K (S > 1): every workgroup stores its fp32 partial tile with device-
+// coherent stores, waits for them to complete, and counts itself in the
+// tile's arrival counter.  The workgroup that arrives last reads the S
+// partials of the tile with device-coherent loads, adds them in split order
+// 0..S-1 -- the same order whichever workgroup is last, so the result is
+// reproducible -- applies the epilogue, stores y and resets the counter for the
+// next call.  Nothing waits on another workgroup.  (Device-coherent accesses
+// pass the per-XCD L2 coherently; a device-scope fence would instead write back
+// and invalidate the whole L2 under every co-resident workgroup.)
 template <int OP>
 struct LdsChunk {
   static constexpr int value = OP == OP_A8W8 ? 128 : 64;
@@ -823,47 +841,124 @@ __global__ __launch_bounds__(256) void tlds_kernel(const Args a) {
   unsigned short* y = static_cast<unsigned short*>(a.y);
   float scale = 1.0f;
   if constexpr (OP == OP_FP8T) scale = a.s0[0];
+  if constexpr (S == 1) {
 #pragma unroll
-  for (int f = 0; f < FN; ++f)
+    for (int f = 0; f < FN; ++f)
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int m = m_base + j * 16 + lr;
-      if (m >= M) continue;
+      for (int j = 0; j < FM; ++j) {
+        const int m = m_base + j * 16 + lr;
+        if (m >= M) continue;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int n = nb + f * 16 + lq * 4 + e;
-        if (n >= N) continue;
-        if constexpr (S == 1) {
+        for (int e = 0; e < 4; ++e) {
+          const int n = nb + f * 16 + lq * 4 + e;
+          if (n >= N) continue;
           float v = acc[0][f][j][e];
           if constexpr (OP == OP_GATED) v = silu_f32(v) * acc[G - 1][f][j][e];
           if constexpr (OP == OP_FP8T) v *= scale;
           y[(size_t)m * N + n] = f32_to_bf16(v);
-        } else {
-#pragma unroll
-          for (int g = 0; g < G; ++g)
-            a.ws[(((size_t)split * G + g) * M + m) * N + n] = acc[g][f][j][e];
         }
       }
+  } else {
+    // ---- split-K: store this split's partials (device-coherent), count in,
+    // and let the last workgroup of the tile combine them
+    const size_t MN = (size_t)M * N;
+    const auto ws = buffer_rsrc(a.ws, (unsigned)((size_t)S * G * MN * 4));
+    const bool vec = (N & 3) == 0;                // 16-byte partial rows
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int m = m_base + j * 16 + lr;
+        if (m >= M) continue;
+        const int n = nb + f * 16 + lq * 4;       // this lane's 4 consecutive outputs
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const size_t base = ((size_t)split * G + g) * MN + (size_t)m * N + n;
+          if (vec && n + 3 < N) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[g][f][j]), ws,
+                                                   (unsigned)(base * 4), 0, kCoherent);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N)
+                __hip_atomic_store(a.ws + base + e, acc[g][f][j][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      }
+    __shared__ unsigned last;
+    __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0): this thread's partial stores are done
+    __syncthreads();
+    const unsigned tile = blockIdx.y * gridDim.x + blockIdx.x;
+    if (threadIdx.x == 0)
+      last = __hip_atomic_fetch_add(a.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (unsigned)(S - 1);
+    __syncthreads();
+    if (last) {                                   // workgroup-uniform
+      constexpr int TW = 64 * FN, TH = 16 * FM;
+      const int n0 = blockIdx.x * TW;
+      if (vec) {
+        // quads of 4 outputs: thread t takes quads t, t + 256, ...; every load
+        // is issued before the sums
+        constexpr int QPR = TW / 4;               // quads per tile row
+        constexpr int T = TH * QPR / 256;         // quads per thread (TH*QPR is a multiple of 256)
+        constexpr int TB0 = 32 / (S * G);         // quads per batch: at most 128 registers in flight
+        constexpr int TB = TB0 < 1 ? 1 : (TB0 > T ? T : TB0);
+#pragma unroll
+        for (int t0 = 0; t0 < T; t0 += TB) {
+          f32x4 pv[TB][S][G];
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb) {
+            const int q = threadIdx.x + 256 * min(t0 + tb, T - 1);
+            const int m = min(m_base + q / QPR, M - 1), n = min(n0 + 4 * (q % QPR), N - 4);
+#pragma unroll
+            for (int sp = 0; sp < S; ++sp)
+#pragma unroll
+              for (int g = 0; g < G; ++g)
+                pv[tb][sp][g] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               ws, (unsigned)((((size_t)sp * G + g) * MN + (size_t)m * N + n) * 4), 0, kCoherent));
+          }
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb) {
+            if (t0 + tb >= T) continue;
+            const int q = threadIdx.x + 256 * (t0 + tb);
+            const int m = m_base + q / QPR, n = n0 + 4 * (q % QPR);
+            if (m >= M || n >= N) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float v = 0.0f, u = 0.0f;
+#pragma unroll
+              for (int sp = 0; sp < S; ++sp) {
+                v += pv[tb][sp][0][e];
+                if constexpr (G == 2) u += pv[tb][sp][G - 1][e];
+              }
+              if constexpr (OP == OP_GATED) v = silu_f32(v) * u;
+              if constexpr (OP == OP_FP8T) v *= scale;
+              y[(size_t)m * N + n + e] = f32_to_bf16(v);
+            }
+          }
+        }
+      } else {
+        for (int e = threadIdx.x; e < TW * TH; e += 256) {
+          const int r = e / TW, cc = e - (e / TW) * TW;
+          const int m = m_base + r, n = n0 + cc;
+          if (m >= M || n >= N) continue;
+          const size_t i = (size_t)m * N + n;
+          float v = 0.0f, u = 0.0f;
+#pragma unroll
+          for (int sp = 0; sp < S; ++sp) {
+            v += __hip_atomic_load(a.ws + (size_t)sp * G * MN + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if constexpr (G == 2)
+              u += __hip_atomic_load(a.ws + ((size_t)sp * G + 1) * MN + i, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+          }
+          if constexpr (OP == OP_GATED) v = silu_f32(v) * u;
+          if constexpr (OP == OP_FP8T) v *= scale;
+          y[i] = f32_to_bf16(v);
+        }
+      }
+      if (threadIdx.x == 0) __hip_atomic_store(a.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-}
-
-// Sum of the S split-K partials in a fixed order, then the epilogue.
-template <int OP>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const Args a, int S) {
-  constexpr int G = op_groups(OP);
-  const size_t MN = (size_t)a.M * a.N;
-  float scale = 1.0f;
-  if constexpr (OP == OP_FP8T) scale = a.s0[0];
-  unsigned short* y = static_cast<unsigned short*>(a.y);
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < MN; i += (size_t)gridDim.x * 256) {
-    float v = 0.0f, u = 0.0f;
-    for (int s = 0; s < S; ++s) {
-      v += a.ws[((size_t)s * G) * MN + i];
-      if constexpr (G == 2) u += a.ws[((size_t)s * G + 1) * MN + i];
-    }
-    if constexpr (OP == OP_GATED) v = silu_f32(v) * u;
-    if constexpr (OP == OP_FP8T) v *= scale;
-    y[i] = f32_to_bf16(v);
   }
 }
 
@@ -898,11 +993,6 @@ hipError_t launch_tlds(const Args& a, hipStream_t s) {
   const unsigned gy = (unsigned)((a.M + 16 * FM - 1) / (16 * FM));
   const size_t smem = (size_t)2 * 16 * FM * kLdsRowStride;
   hipLaunchKernelGGL((tlds_kernel<OP, FM, FN, S, P>), dim3(gx, gy, S), dim3(256), smem, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || S == 1) return e;
-  const size_t mn = (size_t)a.M * a.N;
-  const unsigned rg = (unsigned)std::min<size_t>((mn + 255) / 256, 2048);
-  hipLaunchKernelGGL((splitk_reduce_kernel<OP>), dim3(rg), dim3(256), 0, s, a, S);
   return hipGetLastError();
 }
 

@@ -94,10 +94,15 @@ constexpr bool tlds_valid(int op, int FM, int FN, int S, int P) {
   return (S == 1 || S == 2 || S == 4 || S == 8) && P >= 1 && G * FN * FM * 4 <= 128 &&
          tlds_regs(op, FM, FN, P) <= 224 && (128 % (64 * FN)) == 0;
 }
-// Bytes of split-K partials a tlds launch with S > 1 needs.
+// Bytes of split-K partials a tlds launch with S > 1 needs, and the number of
+// output tiles (one arrival counter each) its grid has.
 constexpr unsigned long long tlds_ws_bytes(int op, int S, int M, int N) {
   return S > 1 ? (unsigned long long)S * op_groups(op) * M * N * 4ull : 0ull;
 }
+constexpr unsigned long long tlds_tiles(int FN, int M, int N) {
+  return (unsigned long long)((N + 64 * FN - 1) / (64 * FN)) * (unsigned long long)((M + 127) / 128 + 1);
+}
+constexpr int kSplitCounters = 65536;   // arrival counters kept in the workspace
 
 // The MFMA tile path serves the rows buckets from 16 up (M = 13..128, and any M
 // above 128): below that the problem is a weight stream with too few rows to
@@ -164,7 +169,7 @@ constexpr const char kSpaceText[] =
 #undef SKG_GEMV
 #undef SKG_TILE
 #undef SKG_TLDS
-    "kernels=4";  // bump when a kernel's arithmetic or indexing changes
+    "kernels=7";  // bump when a kernel's arithmetic or indexing changes
 constexpr uint32_t kSpaceToken = fnv1a(kSpaceText);
 
 }  // namespace skg

@@ -168,3 +168,47 @@ def test_dispatch_deterministic():
     b = [skg.skinny_gemm_query(k, M, N, K) for k in skg.OPS for M in (1, 5, 16, 100, 300)
          for (N, K) in ((4096, 4096), (1024, 1024))]
     assert a == b
+
+
+def test_split_k_counters_and_graph_replay():
+    """Split-K variants combine partials through per-tile arrival counters that
+    each launch leaves at zero: repeated calls, calls on other shapes in
+    between, and graph replays all give the eager bits."""
+    names = skg.variants("bf16")
+    split = [n for n in names if n.startswith("tlds_") and "_s1_" not in n]
+    assert split
+    cases = [(64, 4096, 4096), (24, 1000, 2064), (128, 2048, 1024), (17, 4096, 512)]
+    first = {}
+    for (M, N, K) in cases:
+        p = synth.make_bf16(M, N, K, seed=5)
+        dev = to_device(p)
+        ref = reference(p)
+        for v in split:
+            if not skg.skinny_gemm_variant_supports("bf16", names.index(v), M):
+                continue
+            y = run(p, dev, variant=v)
+            torch.cuda.synchronize()
+            bits = host_bits(y)
+            assert_parity(bits, ref, f"{v} M={M} N={N} K={K}")
+            first[(M, N, K, v)] = (p, dev, bits)
+    # interleave shapes and variants, then repeat: same bits every time
+    for _ in range(2):
+        for (M, N, K, v), (p, dev, bits) in first.items():
+            assert np.array_equal(host_bits(run(p, dev, variant=v)), bits), (M, N, K, v)
+    # graph replay of a split-K variant, eager work in between
+    (M, N, K, v), (p, dev, bits) = next(iter(first.items()))
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    run(p, dev, variant=v, y=y)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(3):
+            run(p, dev, variant=v, y=y)
+    for _ in range(3):
+        y.zero_()
+        junk = torch.randn(1 << 16, device="cuda") * 2
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(y), bits), f"graph replay {v}"
+        del junk
