@@ -8,9 +8,9 @@ whole path over that sweep: 65 calls of skinny_gemm_bf16 through the library's
 table dispatch.  Inputs are resident in HBM before timing starts.  Each shape
 cycles through enough copies of W (>= 1 GiB per shape) that every call streams
 its weight from HBM, not from the 256 MB Infinity Cache.  Steps are replayed
-from HIP graphs.  The dominant kernel's launches are grouped in their own graph
-and bracketed by HIP events on the launch stream, which gives its live average
-duration for the roofline figure.
+from HIP graphs, eight steps per graph.  The dominant kernel's launches of
+those steps are grouped in their own graph and bracketed by HIP events on the
+launch stream, which gives its live average duration for the roofline figure.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -97,25 +97,30 @@ def read_counters(kernel: str, code_hash: str):
 
 
 def cpu_baseline(calls, host, seconds: float):
-    """The oracle, as it stands, on a bounded prefix of one step's calls."""
+    """The oracle, as it stands, run over the step's calls in step order,
+    pass after pass, until `seconds` of CPU time have been spent (the last pass
+    may stop part-way); reported as algorithmic bytes per second."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
-    done, nbytes, t0 = [], 0, time.perf_counter()
-    for (M, N, K) in calls:
-        xb, wb = host[(N, K)]
-        oracle.linear_bf16(xb[:M], wb)
-        nbytes += alg_bytes(M, N, K)
-        done.append((M, N, K))
+    ncalls, nbytes, t0 = 0, 0, time.perf_counter()
+    while True:
+        for (M, N, K) in calls:
+            xb, wb = host[(N, K)]
+            oracle.linear_bf16(xb[:M], wb)
+            nbytes += alg_bytes(M, N, K)
+            ncalls += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {len(done)} of the step's {len(calls)} calls in step order "
-                      f"({len(done)} oracle.linear_bf16 calls, float64, {dt:.1f} s)"}
+            "sample": f"{ncalls} oracle.linear_bf16 calls ({ncalls / len(calls):.2f} passes over the step's "
+                      f"{len(calls)} calls in step order), float64, {dt:.1f} s"}
 
 
 def main() -> int:
@@ -124,7 +129,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rotation-gib", type=float, default=1.0, help="bytes of W copies per shape")
-    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-call-replays", type=int, default=5, help="graph replays per call shape")
     ap.add_argument("--no-per-call", action="store_true",
@@ -148,7 +153,8 @@ def main() -> int:
         return 1
     torch.cuda.set_device(0)
     skg.load()
-    dev_name = torch.cuda.get_device_name(0)
+    props = torch.cuda.get_device_properties(0)
+    dev_name = f"{props.gcnArchName.split(':')[0]} ({props.multi_processor_count} CUs)"
     log("device", dev_name, "| identity", skg.skinny_gemm_identity())
 
     shapes = list(synth.SWEEP_NK)
@@ -208,49 +214,64 @@ def main() -> int:
     rest_calls = [c for c in calls if sym[c] != dominant]
     log(f"dominant kernel {dominant}: {len(dom_calls)} calls/step, ~{sym_time[dominant]:.1f} us/step")
 
-    # ------------------------------------------ step graphs (4 rotations)
-    NR = 4
+    # ---------------------------------------------------------- step graphs
+    # Steps are replayed in blocks of B: one graph holds the non-dominant calls
+    # of B steps, another the dominant kernel's calls of the same B steps, so
+    # each HIP event pair brackets B * len(dom_calls) back-to-back launches and
+    # the graph-launch boundary is amortised.  Step s of a block uses weight
+    # copy (s * len(Ms) + i) for the i-th M of a shape.
+    B = max(1, min(8, args.steps))
     nM = len(Ms)
 
-    def capture(subset, r):
+    def capture(subset, steps):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for c in subset:
-                launch(c, r * nM + Ms.index(c[0]))
+            for s_ in steps:
+                for c in subset:
+                    launch(c, s_ * nM + Ms.index(c[0]))
         return g
 
-    g_rest = [capture(rest_calls, r) for r in range(NR)]
-    g_dom = [capture(dom_calls, r) for r in range(NR)]
+    g_rest = capture(rest_calls, range(B))
+    g_dom = capture(dom_calls, range(B))
+    rem = args.steps % B
+    g_rest_r = capture(rest_calls, range(rem)) if rem else None
+    g_dom_r = capture(dom_calls, range(rem)) if rem else None
     torch.cuda.synchronize()
 
-    for s in range(args.warmup):
-        g_rest[s % NR].replay()
-        g_dom[s % NR].replay()
+    for _ in range(max(1, args.warmup // B)):
+        g_rest.replay()
+        g_dom.replay()
     torch.cuda.synchronize()
 
     # ------------------------------------------------------- timed steps
-    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    blocks = args.steps // B
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(blocks + (1 if rem else 0))]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for s in range(args.steps):
-        g_rest[s % NR].replay()
-        e0[s].record(stream)
-        g_dom[s % NR].replay()
-        e1[s].record(stream)
+    for bi in range(blocks):
+        g_rest.replay()
+        pairs[bi][0].record(stream)
+        g_dom.replay()
+        pairs[bi][1].record(stream)
+    if rem:
+        g_rest_r.replay()
+        pairs[-1][0].record(stream)
+        g_dom_r.replay()
+        pairs[-1][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    dom_us = sum(e0[s].elapsed_time(e1[s]) for s in range(args.steps)) * 1e3 / (args.steps * len(dom_calls))
+    dom_us = sum(e0.elapsed_time(e1) for e0, e1 in pairs) * 1e3 / (args.steps * len(dom_calls))
     step_bytes = sum(alg_bytes(*c) for c in calls)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"step {ms_step * 1e3:.1f} us ({wall / args.steps * 1e6:.1f} us wall), {value:.1f} GB/s, "
         f"dominant kernel {dom_us:.2f} us/launch")
 
-    del g_rest, g_dom
+    del g_rest, g_dom, g_rest_r, g_dom_r
     if args.no_per_call:
         per_call_us = dict(rough_us)
     else:
