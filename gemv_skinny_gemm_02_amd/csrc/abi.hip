@@ -365,7 +365,7 @@ skg_status run_op(int op, const void* x, const void* w, const float* s0, const f
   skg_status st = launch(op, d.variant, a, s);
   if (st == SKG_EUNSUPPORTED && d.variant >= 0 && kVariants[d.variant].family == FAM_TLDS) {
     // no split-K workspace here (e.g. first call under graph capture): the
-    // untuned tile default needs none
+    // untuned default without a K split needs none
     const int fb = default_variant_no_ws(op, M, N, K);
     if (fb >= 0 && fb != d.variant) st = launch(op, fb, a, s);
   }

@@ -658,18 +658,35 @@ struct LdsRound {
   float sw[OP == OP_A8W8 ? FN : 1];
 };
 
+// W rows move as 128-byte row segments (8 rows per wave instruction, whole
+// cache lines) and pass through a per-wave LDS stage into the MFMA fragment
+// layout: the fragment layout itself would read 16 rows x 64 bytes per
+// instruction, and that load pattern is limited by the vector L1 (its address
+// stage stalls on the cache), not by HBM.  fp8 weights with bf16 x keep the
+// direct fragment loads.
+template <int OP>
+struct TldsSeg {
+  static constexpr bool value = OP != OP_FP8T;
+};
+constexpr int tlds_wstage_bytes(int op, int FN) { return op == OP_FP8T ? 0 : op_groups(op) * FN * 16 * kLdsRowStride; }
+constexpr int tlds_lds_bytes(int op, int FM, int FN) {
+  return 2 * 16 * FM * kLdsRowStride + 4 * tlds_wstage_bytes(op, FN);
+}
+
 template <int OP, int FM, int FN, int S, int P>
 __global__ __launch_bounds__(256) void tlds_kernel(const Args a) {
   constexpr int G = op_groups(OP);
   constexpr int KCH = LdsChunk<OP>::value;
   constexpr int WB = op_w_bytes(OP);
   constexpr int XB = op_x_bytes(OP);
+  constexpr bool SEG = TldsSeg<OP>::value;
   using Round = LdsRound<OP, FM, FN>;
   constexpr int XPIECES = Round::XPIECES;
   constexpr int XPT = Round::XPT;
   constexpr int BUFB = 16 * FM * kLdsRowStride;   // bytes of one LDS x buffer
+  constexpr int WSTB = tlds_wstage_bytes(OP, FN);  // bytes of one wave's W stage
 
-  extern __shared__ __align__(16) unsigned char xl[];   // [2][16*FM][kLdsRowStride]
+  extern __shared__ __align__(16) unsigned char xl[];   // [2][16*FM][stride] x, then [4][G*FN*16][stride] W
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -684,15 +701,22 @@ __global__ __launch_bounds__(256) void tlds_kernel(const Args a) {
   const int c_begin = split * CPS;
   const int rounds = max(0, min(CPS, NC - c_begin));
 
-  const char* wrow[G][FN];
+  // W row pointers: fragment layout (row lr), or for the 128-byte segments
+  // the row of load h (8h + lane/8) with this lane's 16-byte column lane%8
+  const char* wrow[G][FN][2];
   int wblk[FN];
 #pragma unroll
   for (int f = 0; f < FN; ++f) {
-    const int n = min(nb + f * 16 + lr, N - 1);
 #pragma unroll
-    for (int g = 0; g < G; ++g) wrow[g][f] = static_cast<const char*>(a.w) + (size_t)(n + g * N) * K * WB;
+    for (int h = 0; h < 2; ++h) {
+      const int n = SEG ? min(nb + f * 16 + 8 * h + (lane >> 3), N - 1) : min(nb + f * 16 + lr, N - 1);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        wrow[g][f][h] = static_cast<const char*>(a.w) + (size_t)(n + g * N) * K * WB + (SEG ? (lane & 7) * 16 : 0);
+    }
     wblk[f] = min(nb + f * 16, N - 1) >> 7;
   }
+  unsigned char* wst = xl + 2 * BUFB + wave * WSTB;   // this wave's W stage
   // x pieces this thread copies into LDS: piece p -> chunk row p/8 (x row
   // m_base + p/8, clamped to M-1), byte column 16*(p%8)
   const char* xrowp[XPT];
@@ -731,14 +755,27 @@ __global__ __launch_bounds__(256) void tlds_kernel(const Args a) {
   auto load = [&](Round& b, int c) {
     c = min(c, max(rounds - 1, 0));
     const int chunk = min(c_begin + c, NC - 1);
+    if constexpr (SEG) {
+      // segment h of every fragment: 128 bytes of 8 rows; a segment piece past
+      // K re-reads the last in-range piece (its weights are zeroed when used)
+      const int off = min(chunk * KCH * WB, K * WB - 16 - (lane & 7) * 16);
 #pragma unroll
-    for (int h = 0; h < Round::WPF; ++h) {
-      const int k = min(wk(c, h), K - LK);
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int f = 0; f < FN; ++f)
-          b.w[g][f][h] = load_nt(reinterpret_cast<const u32x4*>(wrow[g][f] + (size_t)k * WB));
+          for (int f = 0; f < FN; ++f)
+            b.w[g][f][h] = load_nt(reinterpret_cast<const u32x4*>(wrow[g][f][h] + off));
+    } else {
+#pragma unroll
+      for (int h = 0; h < Round::WPF; ++h) {
+        const int k = min(wk(c, h), K - LK);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int f = 0; f < FN; ++f)
+            b.w[g][f][h] = load_nt(reinterpret_cast<const u32x4*>(wrow[g][f][0] + (size_t)k * WB));
+      }
     }
     // x: 16-byte pieces of the 128-byte chunk rows; a piece past K re-reads
     // the last in-range piece (finite data against zeroed weights)
@@ -757,6 +794,34 @@ __global__ __launch_bounds__(256) void tlds_kernel(const Args a) {
 
   auto compute = [&](const Round& b0, int c, auto tail) {
     Round b = b0;
+    unsigned char* buf = xl + (c & 1) * BUFB;
+    if constexpr (SEG) {
+      // stage the 128-byte segments (row 8h + lane/8, column lane%8) ...
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            *reinterpret_cast<u32x4*>(wst + ((g * FN + f) * 16 + 8 * h + (lane >> 3)) * kLdsRowStride +
+                                      (lane & 7) * 16) = b0.w[g][f][h];
+    }
+#pragma unroll
+    for (int i = 0; i < XPT; ++i)
+      if (xmine[i]) *reinterpret_cast<u32x4*>(buf + xdst[i]) = b.x[i];
+    __syncthreads();
+    if constexpr (SEG) {
+      // ... and read them back in fragment layout: row lr, the 16 bytes of
+      // K-slot lq for MFMA step / half h
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            b.w[g][f][h] = *reinterpret_cast<const u32x4*>(wst + ((g * FN + f) * 16 + lr) * kLdsRowStride + h * 64 +
+                                                           lq * 16);
+    }
     if constexpr (decltype(tail)::value) {        // lanes past K contribute nothing
 #pragma unroll
       for (int h = 0; h < Round::WPF; ++h) {
@@ -764,14 +829,9 @@ __global__ __launch_bounds__(256) void tlds_kernel(const Args a) {
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
-          for (int f = 0; f < FN; ++f) b.w[g][f][h] = dead ? u32x4{0, 0, 0, 0} : b0.w[g][f][h];
+          for (int f = 0; f < FN; ++f) b.w[g][f][h] = dead ? u32x4{0, 0, 0, 0} : b.w[g][f][h];
       }
     }
-    unsigned char* buf = xl + (c & 1) * BUFB;
-#pragma unroll
-    for (int i = 0; i < XPT; ++i)
-      if (xmine[i]) *reinterpret_cast<u32x4*>(buf + xdst[i]) = b.x[i];
-    __syncthreads();
     if constexpr (OP == OP_BF16 || OP == OP_GATED) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -991,7 +1051,7 @@ template <int OP, int FM, int FN, int S, int P>
 hipError_t launch_tlds(const Args& a, hipStream_t s) {
   const unsigned gx = (unsigned)((a.N + 64 * FN - 1) / (64 * FN));
   const unsigned gy = (unsigned)((a.M + 16 * FM - 1) / (16 * FM));
-  const size_t smem = (size_t)2 * 16 * FM * kLdsRowStride;
+  const size_t smem = (size_t)tlds_lds_bytes(OP, FM, FN);
   hipLaunchKernelGGL((tlds_kernel<OP, FM, FN, S, P>), dim3(gx, gy, S), dim3(256), smem, s, a);
   return hipGetLastError();
 }

@@ -7,6 +7,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <fstream>
+#include <initializer_list>
 #include <sstream>
 
 #include "variants.hpp"
@@ -308,40 +309,68 @@ int Table::load(const std::string& path, const Identity& self, std::string* err)
 }
 
 // --------------------------------------------------------------- defaults
-// The untuned entry point: the VALU weight stream below 16 rows, the MFMA
-// tile path from 16 rows, with a shape rule for each.
-int default_variant_no_ws(int op, int M, int N, int K) {
-  (void)N;
-  (void)K;
-  for (int i = 0; i < kNumVariants; ++i)
-    if (kVariants[i].family == FAM_TILE && variant_supports(op, i, M)) return i;
-  for (int i = 0; i < kNumVariants; ++i)
-    if (kVariants[i].family == FAM_GEMV && variant_supports(op, i, M)) return i;
+// The untuned entry point: what runs with no table, and the incumbent a table
+// entry has to beat.  A shape rule fitted to gfx950 measurements of the whole
+// variant list over the decode shapes:
+//  * rows 1..3, rows 4 unless both operands are fp8, and rows up to 12 when
+//    the weight is under 16 MiB or is fp8 with bf16 x: the VALU weight
+//    stream.  Two weight rows per wave for one row of x, four for more, eight
+//    for a vocabulary-sized N (>= 65536) with more than one row of x; K split
+//    over the 4 waves of a workgroup unless a weight row is under 2 KiB, where
+//    the 4 waves take different rows instead.
+//  * small weights (<= 4 MiB) at rows 16..32: the register MFMA tile.
+//  * otherwise the LDS-shared MFMA tile, with K split S ways so that the
+//    64-row output tiles times S come to about 256 workgroups or more: S = 4
+//    up to 8192 weight rows (gate and up rows counted), 2 up to 16384, else 1;
+//    two chunks in flight from the rows-96 bucket, four below.
+// `allow_ws` false keeps to variants that need no split-K workspace.
+namespace {
+
+int first_supported(int op, int M, std::initializer_list<const char*> names) {
+  for (const char* n : names) {
+    const int v = variant_from_name(n);
+    if (v >= 0 && variant_supports(op, v, M)) return v;
+  }
   return -1;
 }
 
-int default_variant(int op, int M, int N, int K) {
-  (void)K;
-  (void)N;
-  // Preference lists: the first variant compiled for (op, M) wins.
-  static const char* const kGemvPref[] = {"gemv_r2_k4_p4", "gemv_r2_k4_p2", "gemv_r4_k4_p2", "gemv_r4_k4_p1",
-                                          "gemv_r2_k4_p1", "gemv_r1_k4_p2"};
-  static const char* const kGemvPrefLarge[] = {"gemv_r4_k4_p2", "gemv_r4_k4_p1", "gemv_r2_k4_p2", "gemv_r2_k4_p1",
-                                               "gemv_r1_k4_p2"};
-  static const char* const kTilePref[] = {"tile_f1_k4_p16", "tile_f1_k4_p8", "tile_f1_k4_p4", "tile_f1_k4_p2"};
-  const bool gemv = !tile_rows(M);
-  const char* const* pref = gemv ? (M <= 2 ? kGemvPref : kGemvPrefLarge) : kTilePref;
-  const int npref = gemv ? (M <= 2 ? 6 : 5) : 4;
-  for (int i = 0; i < npref; ++i) {
-    const int v = variant_from_name(pref[i]);
-    if (v >= 0 && variant_supports(op, v, M)) return v;
-  }
-  const int fam = gemv ? FAM_GEMV : FAM_TILE;
+int first_of_family(int op, int M, int fam) {
   for (int i = 0; i < kNumVariants; ++i)
     if (kVariants[i].family == fam && variant_supports(op, i, M)) return i;
-  for (int i = 0; i < kNumVariants; ++i)
-    if (variant_supports(op, i, M)) return i;
   return -1;
 }
+
+int default_pick(int op, int M, int N, int K, bool allow_ws) {
+  const int b = M > kMaxBucket ? kMaxBucket : bucket_of(M);
+  const double wbytes = (double)N * K * op_w_bytes(op) * op_groups(op);
+  const double wrows = (double)N * op_groups(op);
+  const double MiB = 1024.0 * 1024.0;
+  const bool gemv = b <= 3 || (b == 4 && op != OP_A8W8) || (b <= 12 && (wbytes < 16 * MiB || op == OP_FP8T));
+  int v = -1;
+  if (gemv) {
+    if ((double)K * op_w_bytes(op) < 2048) v = first_supported(op, M, {"gemv_r4_k1_p2", "gemv_r4_k2_p2"});
+    else if (M == 1) v = first_supported(op, M, {"gemv_r2_k4_p1", "gemv_r4_k4_p1"});
+    else if (N >= 65536) v = first_supported(op, M, {"gemv_r8_k4_p1", "gemv_r4_k4_p1", "gemv_r2_k4_p1"});
+    else v = first_supported(op, M, {"gemv_r4_k4_p1", "gemv_r2_k4_p1", "gemv_r1_k4_p2"});
+    if (v < 0) v = first_of_family(op, M, FAM_GEMV);
+  } else if (wbytes <= 4 * MiB && b <= 32) {
+    v = first_supported(op, M, {"tile_f1_k4_p4", "tile_f1_k4_p2"});
+  } else {
+    const int S = !allow_ws ? 1 : wrows <= 8192 ? 4 : wrows <= 16384 ? 2 : 1;
+    if (S == 4) v = first_supported(op, M, {b >= 96 ? "tlds_f1_s4_p2" : "tlds_f1_s4_p4", "tlds_f1_s4_p2"});
+    else if (S == 2) v = first_supported(op, M, {"tlds_f1_s2_p4", "tlds_f1_s2_p8"});
+    else v = first_supported(op, M, {"tlds_f1_s1_p4"});
+  }
+  if (v < 0) v = first_supported(op, M, {"tile_f1_k4_p4", "tile_f1_k4_p2"});
+  if (v < 0) v = first_of_family(op, M, FAM_TILE);
+  if (v < 0) v = first_of_family(op, M, FAM_GEMV);
+  return v;
+}
+
+}  // namespace
+
+int default_variant(int op, int M, int N, int K) { return default_pick(op, M, N, K, true); }
+
+int default_variant_no_ws(int op, int M, int N, int K) { return default_pick(op, M, N, K, false); }
 
 }  // namespace skg

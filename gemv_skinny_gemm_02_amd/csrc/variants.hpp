@@ -104,11 +104,9 @@ constexpr unsigned long long tlds_tiles(int FN, int M, int N) {
 }
 constexpr int kSplitCounters = 65536;   // arrival counters kept in the workspace
 
-// The MFMA tile path serves the rows buckets from 16 up (M = 13..128, and any M
-// above 128): below that the problem is a weight stream with too few rows to
-// fill a 16-wide fragment, and the VALU path serves it.
-constexpr int kTileMinBucket = 16;
-constexpr bool tile_rows(int M) { return M > kMaxBucket || bucket_of(M) >= kTileMinBucket; }
+// The MFMA tile path serves every rows bucket: rows past M inside a 16-row
+// fragment re-read row M-1 and are never stored, so a table may pick it
+// wherever it streams the weight faster than the VALU path, even for one row.
 
 struct VariantDesc {
   const char* name;
@@ -149,7 +147,6 @@ constexpr bool variant_supports(int op, int i, int M) {
     const int mi = gemv_mt_index(M);
     return mi >= 0 && gemv_valid(op, kGemvMT[mi], v.p0, v.p1, v.p2);
   }
-  if (!tile_rows(M)) return false;
   const int fm = M > kMaxBucket ? kNumTileFM - 1 : tile_fm_index(M);
   if (v.family == FAM_TLDS) return tlds_valid(op, kTileFM[fm], v.p0, v.p1, v.p2);
   return tile_valid(op, kTileFM[fm], v.p0, v.p1, v.p2);
@@ -161,7 +158,7 @@ constexpr uint32_t fnv1a(const char* s, uint32_t h = 2166136261u) {
   return h;
 }
 constexpr const char kSpaceText[] =
-    "buckets=1,2,3,4,6,8,12,16,24,32,64,96,128;gemv_mt=1,2,3,4,6,8,12,16;tile_fm=1,2,4,6,8;"
+    "buckets=1,2,3,4,6,8,12,16,24,32,64,96,128;gemv_mt=1,2,3,4,6,8,12,16;tile_fm=1,2,4,6,8;tile_min=1;"
 #define SKG_GEMV(name, R, KS, U) "G:" #name "," #R "," #KS "," #U ";"
 #define SKG_TILE(name, FN, KS, U) "T:" #name "," #FN "," #KS "," #U ";"
 #define SKG_TLDS(name, FN, S, P) "L:" #name "," #FN "," #S "," #P ";"
@@ -169,7 +166,7 @@ constexpr const char kSpaceText[] =
 #undef SKG_GEMV
 #undef SKG_TILE
 #undef SKG_TLDS
-    "kernels=7";  // bump when a kernel's arithmetic or indexing changes
+    "kernels=8";  // bump when a kernel's arithmetic or indexing changes
 constexpr uint32_t kSpaceToken = fnv1a(kSpaceText);
 
 }  // namespace skg

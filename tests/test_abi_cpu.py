@@ -66,14 +66,13 @@ def test_variants_and_buckets():
     for op in skg.OPS:
         for M in range(1, 301):
             assert any(skg.skinny_gemm_variant_supports(op, i, M) for i in range(len(names))), (op, M)
-    # GEMV variants never claim rows above 16; tile variants start at the
-    # rows-16 bucket (M = 13)
+    # GEMV variants never claim rows above 16; the bf16 tile variants serve
+    # every bucket from one row
     for i, n in enumerate(names):
         if n.startswith("gemv_"):
             assert not skg.skinny_gemm_variant_supports("bf16", i, 17)
         else:
-            assert not skg.skinny_gemm_variant_supports("bf16", i, 12)
-            assert skg.skinny_gemm_variant_supports("bf16", i, 13)
+            assert skg.skinny_gemm_variant_supports("bf16", i, 1)
 
 
 def test_table_engaged_lookup_and_buckets(tmp_path):
@@ -172,9 +171,33 @@ def test_malformed_and_missing(tmp_path):
 
 
 def test_defaults_follow_the_rows_rule():
+    """The untuned rule: VALU weight stream for few rows (up to 12 for small or
+    fp8-with-bf16-x weights), register tile for small weights at 16..32 rows,
+    LDS tile with a K split sized by N otherwise."""
     skg.skinny_gemm_load_table_as(None, _identity())
+    q = lambda op, M, N, K: skg.skinny_gemm_query(op, M, N, K)[0]
     for op in skg.OPS:
-        for M in (1, 2, 3, 4, 6, 8, 12):
-            assert skg.skinny_gemm_query(op, M, 4096, 4096)[0].startswith("gemv_"), (op, M)
-        for M in (13, 16, 24, 32, 64, 96, 128, 129, 1000):
-            assert skg.skinny_gemm_query(op, M, 4096, 4096)[0].startswith("tile_"), (op, M)
+        for M in (1, 2, 3):
+            assert q(op, M, 4096, 4096).startswith("gemv_"), (op, M)
+        for M in (16, 24, 32, 64, 96, 128, 129, 1000):
+            assert q(op, M, 4096, 4096).startswith("tlds_"), (op, M)
+    for M in (4, 6, 8, 12):     # bf16 4096x4096 is 32 MiB: LDS tile from 6 rows
+        assert q("bf16", M, 4096, 4096).startswith("gemv_" if M == 4 else "tlds_"), M
+        assert q("bf16", M, 1024, 1024).startswith("gemv_"), M
+        assert q("fp8_tensor", M, 4096, 4096).startswith("gemv_"), M
+    assert q("a8w8_block", 4, 8192, 4096).startswith("tlds_")
+    for M in (16, 32):
+        assert q("bf16", M, 1024, 1024).startswith("tile_"), M
+    assert q("bf16", 64, 1024, 1024).startswith("tlds_")
+    # GEMV shape: two rows per wave for one x row, eight for a vocabulary N,
+    # one wave per row (no K split) for rows under 2 KiB
+    assert q("bf16", 1, 4096, 4096) == "gemv_r2_k4_p1"
+    assert q("bf16", 3, 4096, 4096) == "gemv_r4_k4_p1"
+    assert q("fp8_tensor", 2, 248320, 4096) == "gemv_r8_k4_p1"
+    assert q("a8w8_block", 1, 32768, 1024) == "gemv_r4_k1_p2"
+    # K split: 4 up to 8192 weight rows, 2 up to 16384, else 1 (gated counts both halves)
+    assert q("bf16", 16, 4096, 12288) == "tlds_f1_s4_p4"
+    assert q("bf16", 128, 4096, 12288) == "tlds_f1_s4_p2"
+    assert q("bf16", 16, 12288, 4096) == "tlds_f1_s2_p4"
+    assert q("gated", 16, 12288, 4096) == "tlds_f1_s1_p4"
+    assert q("a8w8_block", 16, 32768, 1024) == "tlds_f1_s1_p4"
