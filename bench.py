@@ -48,16 +48,21 @@ def alg_bytes(M, N, K):
 
 def kernel_symbol(variant: str, M: int, op: int = 0) -> str:
     """The kernel template instance a variant runs for M rows, as rocprofv3
-    prints it."""
+    prints it.  Variant names are the family followed by one-letter fields:
+    gemv_r<R>_k<KS>_p<P>, tile_f<FN>_k<KS>_p<P>, and
+    tlds[_w<NW>]_f<FN>_s<S>_p<P>[_m<MC>] (NW waves, default 4; at most MC
+    16-row fragments per workgroup, default 8)."""
     parts = variant.split("_")
-    a, ks, u = int(parts[1][1:]), int(parts[2][1:]), int(parts[3][1:])   # (R|FN, KS|S, P)
+    kv = {p[0]: int(p[1:]) for p in parts[1:]}
     if parts[0] == "gemv":
         mt = next(b for b in (1, 2, 3, 4, 6, 8, 12, 16) if M <= b)
-        return f"void skg::gemv_kernel<{op}, {mt}, {a}, {ks}, {u}>(skg::Args)"
+        return f"void skg::gemv_kernel<{op}, {mt}, {kv['r']}, {kv['k']}, {kv['p']}>(skg::Args)"
     f = (min(M, 128) + 15) // 16
     fm = next(b for b in (1, 2, 4, 6, 8) if f <= b)
-    kind = "tlds" if parts[0] == "tlds" else "tile"
-    return f"void skg::{kind}_kernel<{op}, {fm}, {a}, {ks}, {u}>(skg::Args)"
+    if parts[0] == "tile":
+        return f"void skg::tile_kernel<{op}, {fm}, {kv['f']}, {kv['k']}, {kv['p']}>(skg::Args)"
+    fm = min(fm, kv.get("m", 8))
+    return f"void skg::tlds_kernel<{op}, {fm}, {kv['f']}, {kv['s']}, {kv['p']}, {kv.get('w', 4)}>(skg::Args)"
 
 
 def lib_code_hash() -> str:

@@ -647,11 +647,11 @@ struct LdsChunk {
 constexpr int kLdsRowBytes = 128;          // one x row of a chunk
 constexpr int kLdsRowStride = 144;         // padded: rows start 36 dwords apart
 
-template <int OP, int FM, int FN>
+template <int OP, int FM, int FN, int NW>
 struct LdsRound {
   static constexpr int WPF = OP == OP_FP8T ? 1 : 2;          // 16-byte W loads per fragment per chunk
   static constexpr int XPIECES = 16 * FM * kLdsRowBytes / 16;  // 16-byte pieces of the x chunk
-  static constexpr int XPT = (XPIECES + 255) / 256;           // pieces per thread
+  static constexpr int XPT = (XPIECES + 64 * NW - 1) / (64 * NW);  // pieces per thread
   u32x4 w[op_groups(OP)][FN][WPF];
   u32x4 x[XPT];
   float sx[OP == OP_A8W8 ? FM : 1];
@@ -669,18 +669,19 @@ struct TldsSeg {
   static constexpr bool value = OP != OP_FP8T;
 };
 constexpr int tlds_wstage_bytes(int op, int FN) { return op == OP_FP8T ? 0 : op_groups(op) * FN * 16 * kLdsRowStride; }
-constexpr int tlds_lds_bytes(int op, int FM, int FN) {
-  return 2 * 16 * FM * kLdsRowStride + 4 * tlds_wstage_bytes(op, FN);
+constexpr int tlds_lds_bytes(int op, int FM, int FN, int NW) {
+  return 2 * 16 * FM * kLdsRowStride + NW * tlds_wstage_bytes(op, FN);
 }
 
-template <int OP, int FM, int FN, int S, int P>
-__global__ __launch_bounds__(256) void tlds_kernel(const Args a) {
+template <int OP, int FM, int FN, int S, int P, int NW>
+__global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
+  constexpr int NT = 64 * NW;                     // threads of the workgroup
   constexpr int G = op_groups(OP);
   constexpr int KCH = LdsChunk<OP>::value;
   constexpr int WB = op_w_bytes(OP);
   constexpr int XB = op_x_bytes(OP);
   constexpr bool SEG = TldsSeg<OP>::value;
-  using Round = LdsRound<OP, FM, FN>;
+  using Round = LdsRound<OP, FM, FN, NW>;
   constexpr int XPIECES = Round::XPIECES;
   constexpr int XPT = Round::XPT;
   constexpr int BUFB = 16 * FM * kLdsRowStride;   // bytes of one LDS x buffer
@@ -693,7 +694,7 @@ __global__ __launch_bounds__(256) void tlds_kernel(const Args a) {
   const int lr = lane & 15, lq = lane >> 4;
   const int M = a.M, N = a.N, K = a.K;
   const int m_base = blockIdx.y * 16 * FM;
-  const int nb = blockIdx.x * 64 * FN + wave * 16 * FN;
+  const int nb = blockIdx.x * 16 * FN * NW + wave * 16 * FN;
   const int split = blockIdx.z;
   const int kb = a.kb;
   const int NC = (K + KCH - 1) / KCH;          // chunks along K
@@ -724,8 +725,8 @@ __global__ __launch_bounds__(256) void tlds_kernel(const Args a) {
   bool xmine[XPT];
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
-    const int p = min((int)threadIdx.x + 256 * i, XPIECES - 1);
-    xmine[i] = (int)threadIdx.x + 256 * i < XPIECES;
+    const int p = min((int)threadIdx.x + NT * i, XPIECES - 1);
+    xmine[i] = (int)threadIdx.x + NT * i < XPIECES;
     const int r = p >> 3;
     xcolb[i] = (p & 7) * 16;
     xrowp[i] = static_cast<const char*>(a.x) + (size_t)min(m_base + r, M - 1) * K * XB;
@@ -808,7 +809,7 @@ __global__ __launch_bounds__(256) void tlds_kernel(const Args a) {
     }
 #pragma unroll
     for (int i = 0; i < XPT; ++i)
-      if (xmine[i]) *reinterpret_cast<u32x4*>(buf + xdst[i]) = b.x[i];
+      if (XPIECES % NT == 0 || xmine[i]) *reinterpret_cast<u32x4*>(buf + xdst[i]) = b.x[i];
     __syncthreads();
     if constexpr (SEG) {
       // ... and read them back in fragment layout: row lr, the 16 bytes of
@@ -833,20 +834,26 @@ __global__ __launch_bounds__(256) void tlds_kernel(const Args a) {
       }
     }
     if constexpr (OP == OP_BF16 || OP == OP_GATED) {
+      // every x fragment of the chunk is read before the first MFMA: with one
+      // wave per SIMD nothing else hides an LDS read's latency, so the reads
+      // go out back to back and the MFMAs consume them in issue order
+      u32x4 B[2][FM];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int j = 0; j < FM; ++j) {
-          const bf16x8 B = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(buf + (j * 16 + lr) * kLdsRowStride + u * 64 + lq * 16));
+        for (int j = 0; j < FM; ++j)
+          B[u][j] = *reinterpret_cast<const u32x4*>(buf + (j * 16 + lr) * kLdsRowStride + u * 64 + lq * 16);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
 #pragma unroll
           for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int f = 0; f < FN; ++f)
-              acc[g][f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.w[g][f][u]), B,
-                                                                     acc[g][f][j], 0, 0, 0);
-        }
-      }
+              acc[g][f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, b.w[g][f][u]), __builtin_bit_cast(bf16x8, B[u][j]), acc[g][f][j], 0, 0, 0);
     } else if constexpr (OP == OP_FP8T) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -954,13 +961,13 @@ __global__ __launch_bounds__(256) void tlds_kernel(const Args a) {
              (unsigned)(S - 1);
     __syncthreads();
     if (last) {                                   // workgroup-uniform
-      constexpr int TW = 64 * FN, TH = 16 * FM;
+      constexpr int TW = 16 * FN * NW, TH = 16 * FM;
       const int n0 = blockIdx.x * TW;
       if (vec) {
-        // quads of 4 outputs: thread t takes quads t, t + 256, ...; every load
+        // quads of 4 outputs: thread t takes quads t, t + NT, ...; every load
         // is issued before the sums
         constexpr int QPR = TW / 4;               // quads per tile row
-        constexpr int T = TH * QPR / 256;         // quads per thread (TH*QPR is a multiple of 256)
+        constexpr int T = TH * QPR / NT;          // quads per thread (TH*QPR is a multiple of NT)
         constexpr int TB0 = 32 / (S * G);         // quads per batch: at most 128 registers in flight
         constexpr int TB = TB0 < 1 ? 1 : (TB0 > T ? T : TB0);
 #pragma unroll
@@ -968,7 +975,7 @@ __global__ __launch_bounds__(256) void tlds_kernel(const Args a) {
           f32x4 pv[TB][S][G];
 #pragma unroll
           for (int tb = 0; tb < TB; ++tb) {
-            const int q = threadIdx.x + 256 * min(t0 + tb, T - 1);
+            const int q = threadIdx.x + NT * min(t0 + tb, T - 1);
             const int m = min(m_base + q / QPR, M - 1), n = min(n0 + 4 * (q % QPR), N - 4);
 #pragma unroll
             for (int sp = 0; sp < S; ++sp)
@@ -981,7 +988,7 @@ __global__ __launch_bounds__(256) void tlds_kernel(const Args a) {
 #pragma unroll
           for (int tb = 0; tb < TB; ++tb) {
             if (t0 + tb >= T) continue;
-            const int q = threadIdx.x + 256 * (t0 + tb);
+            const int q = threadIdx.x + NT * (t0 + tb);
             const int m = m_base + q / QPR, n = n0 + 4 * (q % QPR);
             if (m >= M || n >= N) continue;
 #pragma unroll
@@ -999,7 +1006,7 @@ __global__ __launch_bounds__(256) void tlds_kernel(const Args a) {
           }
         }
       } else {
-        for (int e = threadIdx.x; e < TW * TH; e += 256) {
+        for (int e = threadIdx.x; e < TW * TH; e += NT) {
           const int r = e / TW, cc = e - (e / TW) * TW;
           const int m = m_base + r, n = n0 + cc;
           if (m >= M || n >= N) continue;
@@ -1047,12 +1054,12 @@ hipError_t launch_tile(const Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int OP, int FM, int FN, int S, int P>
+template <int OP, int FM, int FN, int S, int P, int NW>
 hipError_t launch_tlds(const Args& a, hipStream_t s) {
-  const unsigned gx = (unsigned)((a.N + 64 * FN - 1) / (64 * FN));
+  const unsigned gx = (unsigned)((a.N + 16 * FN * NW - 1) / (16 * FN * NW));
   const unsigned gy = (unsigned)((a.M + 16 * FM - 1) / (16 * FM));
-  const size_t smem = (size_t)tlds_lds_bytes(OP, FM, FN);
-  hipLaunchKernelGGL((tlds_kernel<OP, FM, FN, S, P>), dim3(gx, gy, S), dim3(256), smem, s, a);
+  const size_t smem = (size_t)tlds_lds_bytes(OP, FM, FN, NW);
+  hipLaunchKernelGGL((tlds_kernel<OP, FM, FN, S, P, NW>), dim3(gx, gy, S), dim3(64 * NW), smem, s, a);
   return hipGetLastError();
 }
 
@@ -1067,9 +1074,9 @@ constexpr LaunchFn tile_fn() {
   else return nullptr;
 }
 
-template <int OP, int FM, int FN, int S, int P>
+template <int OP, int FM, int FN, int S, int P, int NW>
 constexpr LaunchFn tlds_fn() {
-  if constexpr (tlds_valid(OP, FM, FN, S, P)) return &launch_tlds<OP, FM, FN, S, P>;
+  if constexpr (tlds_valid(OP, FM, FN, S, P, NW)) return &launch_tlds<OP, FM, FN, S, P, NW>;
   else return nullptr;
 }
 
@@ -1088,10 +1095,12 @@ constexpr TileRow tile_row() {
                   tile_fn<OP, 6, FN, KS, P>(), tile_fn<OP, 8, FN, KS, P>()}};
 }
 
-template <int OP, int FN, int S, int P>
+// Buckets above MC fragments launch the MC-fragment kernel over more grid rows.
+template <int OP, int FN, int S, int P, int MC, int NW>
 constexpr TileRow tlds_row() {
-  return TileRow{{tlds_fn<OP, 1, FN, S, P>(), tlds_fn<OP, 2, FN, S, P>(), tlds_fn<OP, 4, FN, S, P>(),
-                  tlds_fn<OP, 6, FN, S, P>(), tlds_fn<OP, 8, FN, S, P>()}};
+  return TileRow{{tlds_fn<OP, tlds_fm(1, MC), FN, S, P, NW>(), tlds_fn<OP, tlds_fm(2, MC), FN, S, P, NW>(),
+                  tlds_fn<OP, tlds_fm(4, MC), FN, S, P, NW>(), tlds_fn<OP, tlds_fm(6, MC), FN, S, P, NW>(),
+                  tlds_fn<OP, tlds_fm(8, MC), FN, S, P, NW>()}};
 }
 
 // Launch tables, one pair per op, defined in ops_<op>.hip:

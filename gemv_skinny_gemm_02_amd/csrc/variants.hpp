@@ -81,27 +81,31 @@ constexpr bool tile_valid(int op, int FM, int FN, int KS, int P) {
          (128 % ((4 / KS) * FN * 16)) == 0;
 }
 // LDS-shared-x tile path (tlds): 64*FN W rows per workgroup, S-way split-K.
-constexpr int tlds_xpt(int FM) { return (16 * FM * 8 + 255) / 256; }
-constexpr int tlds_regs(int op, int FM, int FN, int P) {
+constexpr int tlds_xpt(int FM, int NW) { return (16 * FM * 8 + 64 * NW - 1) / (64 * NW); }
+constexpr int tlds_regs(int op, int FM, int FN, int P, int NW) {
   const int G = op_groups(op);
   const int wpf = op == OP_FP8T ? 1 : 2;
-  const int per_chunk = G * FN * wpf * 4 + tlds_xpt(FM) * 4 + (op == OP_A8W8 ? FM + FN : 0);
+  const int per_chunk = G * FN * wpf * 4 + tlds_xpt(FM, NW) * 4 + (op == OP_A8W8 ? FM + FN : 0);
   const int acc = G * FN * FM * 4;
-  return P * per_chunk + acc * (op == OP_A8W8 ? 2 : 1) + FM * 4;
+  const int xfrag = op == OP_BF16 || op == OP_GATED ? 8 * FM : 0;   // a chunk's x fragments
+  return P * per_chunk + acc * (op == OP_A8W8 ? 2 : 1) + FM * 4 + xfrag;
 }
-constexpr bool tlds_valid(int op, int FM, int FN, int S, int P) {
+constexpr bool tlds_valid(int op, int FM, int FN, int S, int P, int NW) {
   const int G = op_groups(op);
-  return (S == 1 || S == 2 || S == 4 || S == 8) && P >= 1 && G * FN * FM * 4 <= 128 &&
-         tlds_regs(op, FM, FN, P) <= 224 && (128 % (64 * FN)) == 0;
+  return (S == 1 || S == 2 || S == 4 || S == 8) && (NW == 4 || NW == 8) && P >= 1 && G * FN * FM * 4 <= 128 &&
+         tlds_regs(op, FM, FN, P, NW) <= 224 && (128 % (64 * FN)) == 0;
 }
 // Bytes of split-K partials a tlds launch with S > 1 needs, and the number of
 // output tiles (one arrival counter each) its grid has.
 constexpr unsigned long long tlds_ws_bytes(int op, int S, int M, int N) {
   return S > 1 ? (unsigned long long)S * op_groups(op) * M * N * 4ull : 0ull;
 }
-constexpr unsigned long long tlds_tiles(int FN, int M, int N) {
-  return (unsigned long long)((N + 64 * FN - 1) / (64 * FN)) * (unsigned long long)((M + 127) / 128 + 1);
+constexpr unsigned long long tlds_tiles(int FN, int NW, int FM, int M, int N) {
+  return (unsigned long long)((N + 16 * FN * NW - 1) / (16 * FN * NW)) *
+         (unsigned long long)((M + 16 * FM - 1) / (16 * FM));
 }
+// M fragments a tlds workgroup takes: the bucket's count, capped at MC.
+constexpr int tlds_fm(int FM, int MC) { return FM < MC ? FM : MC; }
 constexpr int kSplitCounters = 65536;   // arrival counters kept in the workspace
 
 // The MFMA tile path serves every rows bucket: rows past M inside a 16-row
@@ -111,13 +115,13 @@ constexpr int kSplitCounters = 65536;   // arrival counters kept in the workspac
 struct VariantDesc {
   const char* name;
   int family;
-  int p0, p1, p2;  // GEMV: R, KS, U.  TILE: FN, KS, U.
+  int p0, p1, p2, p3, p4;  // GEMV: R, KS, U.  TILE: FN, KS, U.  TLDS: FN, S, P, MC, NW.
 };
 
 constexpr VariantDesc kVariants[] = {
-#define SKG_GEMV(name, R, KS, U) {#name, FAM_GEMV, R, KS, U},
-#define SKG_TILE(name, FN, KS, U) {#name, FAM_TILE, FN, KS, U},
-#define SKG_TLDS(name, FN, S, P) {#name, FAM_TLDS, FN, S, P},
+#define SKG_GEMV(name, R, KS, U) {#name, FAM_GEMV, R, KS, U, 0, 0},
+#define SKG_TILE(name, FN, KS, U) {#name, FAM_TILE, FN, KS, U, 0, 0},
+#define SKG_TLDS(name, FN, S, P, MC, NW) {#name, FAM_TLDS, FN, S, P, MC, NW},
 #include "variants.def"
 #undef SKG_GEMV
 #undef SKG_TILE
@@ -148,7 +152,7 @@ constexpr bool variant_supports(int op, int i, int M) {
     return mi >= 0 && gemv_valid(op, kGemvMT[mi], v.p0, v.p1, v.p2);
   }
   const int fm = M > kMaxBucket ? kNumTileFM - 1 : tile_fm_index(M);
-  if (v.family == FAM_TLDS) return tlds_valid(op, kTileFM[fm], v.p0, v.p1, v.p2);
+  if (v.family == FAM_TLDS) return tlds_valid(op, tlds_fm(kTileFM[fm], v.p3), v.p0, v.p1, v.p2, v.p4);
   return tile_valid(op, kTileFM[fm], v.p0, v.p1, v.p2);
 }
 
@@ -161,12 +165,12 @@ constexpr const char kSpaceText[] =
     "buckets=1,2,3,4,6,8,12,16,24,32,64,96,128;gemv_mt=1,2,3,4,6,8,12,16;tile_fm=1,2,4,6,8;tile_min=1;"
 #define SKG_GEMV(name, R, KS, U) "G:" #name "," #R "," #KS "," #U ";"
 #define SKG_TILE(name, FN, KS, U) "T:" #name "," #FN "," #KS "," #U ";"
-#define SKG_TLDS(name, FN, S, P) "L:" #name "," #FN "," #S "," #P ";"
+#define SKG_TLDS(name, FN, S, P, MC, NW) "L:" #name "," #FN "," #S "," #P "," #MC "," #NW ";"
 #include "variants.def"
 #undef SKG_GEMV
 #undef SKG_TILE
 #undef SKG_TLDS
-    "kernels=8";  // bump when a kernel's arithmetic or indexing changes
+    "kernels=10";  // bump when a kernel's arithmetic or indexing changes
 constexpr uint32_t kSpaceToken = fnv1a(kSpaceText);
 
 }  // namespace skg
