@@ -640,18 +640,22 @@ __global__ __launch_bounds__(256) void tile_kernel(const Args a) {
 // next call.  Nothing waits on another workgroup.  (Device-coherent accesses
 // pass the per-XCD L2 coherently; a device-scope fence would instead write back
 // and invalidate the whole L2 under every co-resident workgroup.)
+// A chunk is 128 bytes of every W row: 64 K for bf16 weights, 128 K for fp8
+// weights (for A8W8 also one 128-K scale group).  Its x rows are 128 bytes
+// (bf16 and fp8 x with 128-byte W rows) or 256 bytes (bf16 x with fp8 W).
 template <int OP>
 struct LdsChunk {
-  static constexpr int value = OP == OP_A8W8 ? 128 : 64;
+  static constexpr int value = op_w_fp8(OP) ? 128 : 64;
 };
-constexpr int kLdsRowBytes = 128;          // one x row of a chunk
-constexpr int kLdsRowStride = 144;         // padded: rows start 36 dwords apart
+constexpr int tlds_xrow_bytes(int op) { return (op_w_fp8(op) ? 128 : 64) * op_x_bytes(op); }
+constexpr int tlds_xrow_stride(int op) { return tlds_xrow_bytes(op) + 16; }   // rows start 4 banks apart
+constexpr int kWRowStride = 144;           // W stage rows: 128 bytes + 16 of padding
 
 template <int OP, int FM, int FN, int NW>
 struct LdsRound {
-  static constexpr int WPF = OP == OP_FP8T ? 1 : 2;          // 16-byte W loads per fragment per chunk
-  static constexpr int XPIECES = 16 * FM * kLdsRowBytes / 16;  // 16-byte pieces of the x chunk
-  static constexpr int XPT = (XPIECES + 64 * NW - 1) / (64 * NW);  // pieces per thread
+  static constexpr int WPF = 2;                                         // 16-byte W loads per fragment per chunk
+  static constexpr int XPIECES = 16 * FM * tlds_xrow_bytes(OP) / 16;   // 16-byte pieces of the x chunk
+  static constexpr int XPT = (XPIECES + 64 * NW - 1) / (64 * NW);      // pieces per thread
   u32x4 w[op_groups(OP)][FN][WPF];
   u32x4 x[XPT];
   float sx[OP == OP_A8W8 ? FM : 1];
@@ -662,15 +666,10 @@ struct LdsRound {
 // cache lines) and pass through a per-wave LDS stage into the MFMA fragment
 // layout: the fragment layout itself would read 16 rows x 64 bytes per
 // instruction, and that load pattern is limited by the vector L1 (its address
-// stage stalls on the cache), not by HBM.  fp8 weights with bf16 x keep the
-// direct fragment loads.
-template <int OP>
-struct TldsSeg {
-  static constexpr bool value = OP != OP_FP8T;
-};
-constexpr int tlds_wstage_bytes(int op, int FN) { return op == OP_FP8T ? 0 : op_groups(op) * FN * 16 * kLdsRowStride; }
+// stage stalls on the cache), not by HBM.
+constexpr int tlds_wstage_bytes(int op, int FN) { return op_groups(op) * FN * 16 * kWRowStride; }
 constexpr int tlds_lds_bytes(int op, int FM, int FN, int NW) {
-  return 2 * 16 * FM * kLdsRowStride + NW * tlds_wstage_bytes(op, FN);
+  return 2 * 16 * FM * tlds_xrow_stride(op) + NW * tlds_wstage_bytes(op, FN);
 }
 
 template <int OP, int FM, int FN, int S, int P, int NW>
@@ -680,11 +679,12 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   constexpr int KCH = LdsChunk<OP>::value;
   constexpr int WB = op_w_bytes(OP);
   constexpr int XB = op_x_bytes(OP);
-  constexpr bool SEG = TldsSeg<OP>::value;
   using Round = LdsRound<OP, FM, FN, NW>;
   constexpr int XPIECES = Round::XPIECES;
   constexpr int XPT = Round::XPT;
-  constexpr int BUFB = 16 * FM * kLdsRowStride;   // bytes of one LDS x buffer
+  constexpr int XS = tlds_xrow_stride(OP);        // LDS x row stride
+  constexpr int PPR = tlds_xrow_bytes(OP) / 16;   // 16-byte x pieces per chunk row
+  constexpr int BUFB = 16 * FM * XS;              // bytes of one LDS x buffer
   constexpr int WSTB = tlds_wstage_bytes(OP, FN);  // bytes of one wave's W stage
 
   extern __shared__ __align__(16) unsigned char xl[];   // [2][16*FM][stride] x, then [4][G*FN*16][stride] W
@@ -702,24 +702,24 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   const int c_begin = split * CPS;
   const int rounds = max(0, min(CPS, NC - c_begin));
 
-  // W row pointers: fragment layout (row lr), or for the 128-byte segments
-  // the row of load h (8h + lane/8) with this lane's 16-byte column lane%8
+  // W row pointers of the 128-byte segments: load h of a fragment reads row
+  // 8h + lane/8 at this lane's 16-byte column lane%8
   const char* wrow[G][FN][2];
   int wblk[FN];
 #pragma unroll
   for (int f = 0; f < FN; ++f) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int n = SEG ? min(nb + f * 16 + 8 * h + (lane >> 3), N - 1) : min(nb + f * 16 + lr, N - 1);
+      const int n = min(nb + f * 16 + 8 * h + (lane >> 3), N - 1);
 #pragma unroll
       for (int g = 0; g < G; ++g)
-        wrow[g][f][h] = static_cast<const char*>(a.w) + (size_t)(n + g * N) * K * WB + (SEG ? (lane & 7) * 16 : 0);
+        wrow[g][f][h] = static_cast<const char*>(a.w) + (size_t)(n + g * N) * K * WB + (lane & 7) * 16;
     }
     wblk[f] = min(nb + f * 16, N - 1) >> 7;
   }
   unsigned char* wst = xl + 2 * BUFB + wave * WSTB;   // this wave's W stage
-  // x pieces this thread copies into LDS: piece p -> chunk row p/8 (x row
-  // m_base + p/8, clamped to M-1), byte column 16*(p%8)
+  // x pieces this thread copies into LDS: piece p -> chunk row p/PPR (x row
+  // m_base + p/PPR, clamped to M-1), byte column 16*(p%PPR)
   const char* xrowp[XPT];
   int xcolb[XPT], xdst[XPT];
   bool xmine[XPT];
@@ -727,10 +727,10 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   for (int i = 0; i < XPT; ++i) {
     const int p = min((int)threadIdx.x + NT * i, XPIECES - 1);
     xmine[i] = (int)threadIdx.x + NT * i < XPIECES;
-    const int r = p >> 3;
-    xcolb[i] = (p & 7) * 16;
+    const int r = p / PPR;
+    xcolb[i] = (p % PPR) * 16;
     xrowp[i] = static_cast<const char*>(a.x) + (size_t)min(m_base + r, M - 1) * K * XB;
-    xdst[i] = r * kLdsRowStride + xcolb[i];
+    xdst[i] = r * XS + xcolb[i];
   }
   int xm[FM];
 #pragma unroll
@@ -744,11 +744,12 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
 #pragma unroll
       for (int j = 0; j < FM; ++j) acc[g][f][j] = f32x4{0, 0, 0, 0};
 
-  // K position of this lane's W load h in chunk c (c counts from 0 in this split)
+  // First K of this lane's 16-byte W piece h (fragment layout) in chunk c
+  // (c counts from 0 in this split)
   auto wk = [&](int c, int h) {
     const int k0 = (c_begin + c) * KCH;
     if constexpr (OP == OP_A8W8) return k0 + h * 64 + lq * 16;
-    else if constexpr (OP == OP_FP8T) return k0 + lq * 16;
+    else if constexpr (OP == OP_FP8T) return k0 + lq * 32 + h * 16;
     else return k0 + h * 32 + lq * 8;
   };
   constexpr int LK = OP == OP_BF16 || OP == OP_GATED ? 8 : 16;   // K per 16-byte W load
@@ -756,7 +757,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   auto load = [&](Round& b, int c) {
     c = min(c, max(rounds - 1, 0));
     const int chunk = min(c_begin + c, NC - 1);
-    if constexpr (SEG) {
+    {
       // segment h of every fragment: 128 bytes of 8 rows; a segment piece past
       // K re-reads the last in-range piece (its weights are zeroed when used)
       const int off = min(chunk * KCH * WB, K * WB - 16 - (lane & 7) * 16);
@@ -767,18 +768,8 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
 #pragma unroll
           for (int f = 0; f < FN; ++f)
             b.w[g][f][h] = load_nt(reinterpret_cast<const u32x4*>(wrow[g][f][h] + off));
-    } else {
-#pragma unroll
-      for (int h = 0; h < Round::WPF; ++h) {
-        const int k = min(wk(c, h), K - LK);
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int f = 0; f < FN; ++f)
-            b.w[g][f][h] = load_nt(reinterpret_cast<const u32x4*>(wrow[g][f][0] + (size_t)k * WB));
-      }
     }
-    // x: 16-byte pieces of the 128-byte chunk rows; a piece past K re-reads
+    // x: 16-byte pieces of the chunk rows; a piece past K re-reads
     // the last in-range piece (finite data against zeroed weights)
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
@@ -796,7 +787,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   auto compute = [&](const Round& b0, int c, auto tail) {
     Round b = b0;
     unsigned char* buf = xl + (c & 1) * BUFB;
-    if constexpr (SEG) {
+    {
       // stage the 128-byte segments (row 8h + lane/8, column lane%8) ...
 #pragma unroll
       for (int g = 0; g < G; ++g)
@@ -804,24 +795,25 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
         for (int f = 0; f < FN; ++f)
 #pragma unroll
           for (int h = 0; h < 2; ++h)
-            *reinterpret_cast<u32x4*>(wst + ((g * FN + f) * 16 + 8 * h + (lane >> 3)) * kLdsRowStride +
+            *reinterpret_cast<u32x4*>(wst + ((g * FN + f) * 16 + 8 * h + (lane >> 3)) * kWRowStride +
                                       (lane & 7) * 16) = b0.w[g][f][h];
     }
 #pragma unroll
     for (int i = 0; i < XPT; ++i)
       if (XPIECES % NT == 0 || xmine[i]) *reinterpret_cast<u32x4*>(buf + xdst[i]) = b.x[i];
     __syncthreads();
-    if constexpr (SEG) {
-      // ... and read them back in fragment layout: row lr, the 16 bytes of
-      // K-slot lq for MFMA step / half h
+    {
+      // ... and read them back in fragment layout: row lr, the 16-byte piece h
+      // of K-slot lq (fp8 weights with bf16 x: lane slot lq owns the 32
+      // contiguous K of bytes 32*lq.., for W and x alike)
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int f = 0; f < FN; ++f)
 #pragma unroll
           for (int h = 0; h < 2; ++h)
-            b.w[g][f][h] = *reinterpret_cast<const u32x4*>(wst + ((g * FN + f) * 16 + lr) * kLdsRowStride + h * 64 +
-                                                           lq * 16);
+            b.w[g][f][h] = *reinterpret_cast<const u32x4*>(
+                wst + ((g * FN + f) * 16 + lr) * kWRowStride + (OP == OP_FP8T ? lq * 32 + h * 16 : h * 64 + lq * 16));
     }
     if constexpr (decltype(tail)::value) {        // lanes past K contribute nothing
 #pragma unroll
@@ -842,7 +834,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
-          B[u][j] = *reinterpret_cast<const u32x4*>(buf + (j * 16 + lr) * kLdsRowStride + u * 64 + lq * 16);
+          B[u][j] = *reinterpret_cast<const u32x4*>(buf + (j * 16 + lr) * XS + u * 64 + lq * 16);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -855,26 +847,34 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
               acc[g][f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                   __builtin_bit_cast(bf16x8, b.w[g][f][u]), __builtin_bit_cast(bf16x8, B[u][j]), acc[g][f][j], 0, 0, 0);
     } else if constexpr (OP == OP_FP8T) {
+      // four MFMA steps of 8 K per lane slot: step u takes K 32*lq + 8u .. +7
+      // of the chunk from W (fp8, converted exactly to bf16) and x alike
+      u32x4 B[4][FM];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+          B[u][j] = *reinterpret_cast<const u32x4*>(buf + (j * 16 + lr) * XS + lq * 64 + u * 16);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
         bf16x8 A[FN];
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
+          const unsigned lo = b.w[0][f][u >> 1][(u & 1) * 2], hi = b.w[0][f][u >> 1][(u & 1) * 2 + 1];
           u32x4 wb;
-          wb[0] = fp8x2_to_bf16x2<false>(b.w[0][f][0][2 * h]);
-          wb[1] = fp8x2_to_bf16x2<true>(b.w[0][f][0][2 * h]);
-          wb[2] = fp8x2_to_bf16x2<false>(b.w[0][f][0][2 * h + 1]);
-          wb[3] = fp8x2_to_bf16x2<true>(b.w[0][f][0][2 * h + 1]);
+          wb[0] = fp8x2_to_bf16x2<false>(lo);
+          wb[1] = fp8x2_to_bf16x2<true>(lo);
+          wb[2] = fp8x2_to_bf16x2<false>(hi);
+          wb[3] = fp8x2_to_bf16x2<true>(hi);
           A[f] = __builtin_bit_cast(bf16x8, wb);
         }
 #pragma unroll
-        for (int j = 0; j < FM; ++j) {
-          const bf16x8 B = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(buf + (j * 16 + lr) * kLdsRowStride + lq * 32 + h * 16));
+        for (int j = 0; j < FM; ++j)
 #pragma unroll
           for (int f = 0; f < FN; ++f)
-            acc[0][f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[f], B, acc[0][f][j], 0, 0, 0);
-        }
+            acc[0][f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[f], __builtin_bit_cast(bf16x8, B[u][j]),
+                                                                   acc[0][f][j], 0, 0, 0);
       }
     } else {  // OP_A8W8: the chunk is one 128-K scale group
 #pragma unroll
@@ -882,7 +882,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
         u32x4 B16[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          B16[h] = *reinterpret_cast<const u32x4*>(buf + (j * 16 + lr) * kLdsRowStride + h * 64 + lq * 16);
+          B16[h] = *reinterpret_cast<const u32x4*>(buf + (j * 16 + lr) * XS + h * 64 + lq * 16);
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
           f32x4 t = f32x4{0, 0, 0, 0};

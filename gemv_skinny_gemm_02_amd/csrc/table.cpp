@@ -357,9 +357,15 @@ int default_pick(int op, int M, int N, int K, bool allow_ws) {
     v = first_supported(op, M, {"tile_f1_k4_p4", "tile_f1_k4_p2"});
   } else {
     const int S = !allow_ws ? 1 : wrows <= 8192 ? 4 : wrows <= 16384 ? 2 : 1;
-    if (S == 4) v = first_supported(op, M, {b >= 96 ? "tlds_f1_s4_p2" : "tlds_f1_s4_p4", "tlds_f1_s4_p2"});
-    else if (S == 2) v = first_supported(op, M, {"tlds_f1_s2_p4", "tlds_f1_s2_p8"});
-    else v = first_supported(op, M, {"tlds_f1_s1_p4"});
+    // the capped variants (at most 4 or 2 fragments of x rows per workgroup)
+    // serve forms whose full-height tile does not fit the register budget
+    if (S == 4)
+      v = first_supported(op, M, {b >= 96 ? "tlds_f1_s4_p2" : "tlds_f1_s4_p4", "tlds_f1_s4_p2", "tlds_f1_s4_p4_m4",
+                                  "tlds_f1_s4_p4_m2"});
+    else if (S == 2)
+      v = first_supported(op, M, {"tlds_f1_s2_p4", "tlds_f1_s2_p8", "tlds_f1_s2_p4_m4", "tlds_f1_s2_p4_m2"});
+    else
+      v = first_supported(op, M, {"tlds_f1_s1_p4", "tlds_f1_s1_p4_m4", "tlds_f1_s1_p4_m2"});
   }
   if (v < 0) v = first_supported(op, M, {"tile_f1_k4_p4", "tile_f1_k4_p2"});
   if (v < 0) v = first_of_family(op, M, FAM_TILE);

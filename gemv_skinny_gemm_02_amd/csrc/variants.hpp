@@ -81,13 +81,15 @@ constexpr bool tile_valid(int op, int FM, int FN, int KS, int P) {
          (128 % ((4 / KS) * FN * 16)) == 0;
 }
 // LDS-shared-x tile path (tlds): 64*FN W rows per workgroup, S-way split-K.
-constexpr int tlds_xpt(int FM, int NW) { return (16 * FM * 8 + 64 * NW - 1) / (64 * NW); }
+constexpr int tlds_xpt(int op, int FM, int NW) {
+  const int ppr = op == OP_FP8T ? 16 : 8;   // 16-byte x pieces per chunk row
+  return (16 * FM * ppr + 64 * NW - 1) / (64 * NW);
+}
 constexpr int tlds_regs(int op, int FM, int FN, int P, int NW) {
   const int G = op_groups(op);
-  const int wpf = op == OP_FP8T ? 1 : 2;
-  const int per_chunk = G * FN * wpf * 4 + tlds_xpt(FM, NW) * 4 + (op == OP_A8W8 ? FM + FN : 0);
+  const int per_chunk = G * FN * 2 * 4 + tlds_xpt(op, FM, NW) * 4 + (op == OP_A8W8 ? FM + FN : 0);
   const int acc = G * FN * FM * 4;
-  const int xfrag = op == OP_BF16 || op == OP_GATED ? 8 * FM : 0;   // a chunk's x fragments
+  const int xfrag = op == OP_FP8T ? 16 * FM : (op == OP_BF16 || op == OP_GATED ? 8 * FM : 0);   // a chunk's x fragments
   return P * per_chunk + acc * (op == OP_A8W8 ? 2 : 1) + FM * 4 + xfrag;
 }
 constexpr bool tlds_valid(int op, int FM, int FN, int S, int P, int NW) {
@@ -170,7 +172,7 @@ constexpr const char kSpaceText[] =
 #undef SKG_GEMV
 #undef SKG_TILE
 #undef SKG_TLDS
-    "kernels=10";  // bump when a kernel's arithmetic or indexing changes
+    "kernels=11";  // bump when a kernel's arithmetic or indexing changes
 constexpr uint32_t kSpaceToken = fnv1a(kSpaceText);
 
 }  // namespace skg
