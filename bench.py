@@ -50,8 +50,9 @@ def kernel_symbol(variant: str, M: int, op: int = 0) -> str:
     """The kernel template instance a variant runs for M rows, as rocprofv3
     prints it.  Variant names are the family followed by one-letter fields:
     gemv_r<R>_k<KS>_p<P>, tile_f<FN>_k<KS>_p<P>, and
-    tlds[_w<NW>]_f<FN>_s<S>_p<P>[_m<MC>] (NW waves, default 4; at most MC
-    16-row fragments per workgroup, default 8)."""
+    tlds[_w<NW>][_k<KW>]_f<FN>_s<S>_p<P>[_m<MC>] (NW waves, default 4, of
+    which KW split K inside the workgroup, default 1; at most MC 16-row
+    fragments per workgroup, default 8)."""
     parts = variant.split("_")
     kv = {p[0]: int(p[1:]) for p in parts[1:]}
     if parts[0] == "gemv":
@@ -62,7 +63,8 @@ def kernel_symbol(variant: str, M: int, op: int = 0) -> str:
     if parts[0] == "tile":
         return f"void skg::tile_kernel<{op}, {fm}, {kv['f']}, {kv['k']}, {kv['p']}>(skg::Args)"
     fm = min(fm, kv.get("m", 8))
-    return f"void skg::tlds_kernel<{op}, {fm}, {kv['f']}, {kv['s']}, {kv['p']}, {kv.get('w', 4)}>(skg::Args)"
+    return (f"void skg::tlds_kernel<{op}, {fm}, {kv['f']}, {kv['s']}, {kv['p']}, {kv.get('w', 4)}, "
+            f"{kv.get('k', 1)}>(skg::Args)")
 
 
 def lib_code_hash() -> str:

@@ -331,7 +331,8 @@ skg_status launch(int op, int v, const Args& a_in, hipStream_t s) {
     const size_t need = (size_t)tlds_ws_bytes(op, kVariants[v].p1, a.M, a.N);
     if (need) {
       const int fm = a.M > kMaxBucket ? kNumTileFM - 1 : tile_fm_index(a.M);
-      if (tlds_tiles(kVariants[v].p0, kVariants[v].p4, tlds_fm(kTileFM[fm], kVariants[v].p3), a.M, a.N) >
+      if (tlds_tiles(kVariants[v].p0, kVariants[v].p4 / kVariants[v].p5, tlds_fm(kTileFM[fm], kVariants[v].p3), a.M,
+                     a.N) >
           (unsigned long long)kSplitCounters)
         return fail(SKG_EUNSUPPORTED, "%s: more output tiles than split-K counters", kVariants[v].name);
       std::string why;

@@ -651,10 +651,10 @@ constexpr int tlds_xrow_bytes(int op) { return (op_w_fp8(op) ? 128 : 64) * op_x_
 constexpr int tlds_xrow_stride(int op) { return tlds_xrow_bytes(op) + 16; }   // rows start 4 banks apart
 constexpr int kWRowStride = 144;           // W stage rows: 128 bytes + 16 of padding
 
-template <int OP, int FM, int FN, int NW>
+template <int OP, int FM, int FN, int NW, int KW>
 struct LdsRound {
-  static constexpr int WPF = 2;                                         // 16-byte W loads per fragment per chunk
-  static constexpr int XPIECES = 16 * FM * tlds_xrow_bytes(OP) / 16;   // 16-byte pieces of the x chunk
+  static constexpr int WPF = 2;                                              // 16-byte W loads per fragment per chunk
+  static constexpr int XPIECES = KW * 16 * FM * tlds_xrow_bytes(OP) / 16;   // 16-byte pieces of the round's x chunks
   static constexpr int XPT = (XPIECES + 64 * NW - 1) / (64 * NW);      // pieces per thread
   u32x4 w[op_groups(OP)][FN][WPF];
   u32x4 x[XPT];
@@ -668,39 +668,51 @@ struct LdsRound {
 // instruction, and that load pattern is limited by the vector L1 (its address
 // stage stalls on the cache), not by HBM.
 constexpr int tlds_wstage_bytes(int op, int FN) { return op_groups(op) * FN * 16 * kWRowStride; }
-constexpr int tlds_lds_bytes(int op, int FM, int FN, int NW) {
-  return 2 * 16 * FM * tlds_xrow_stride(op) + NW * tlds_wstage_bytes(op, FN);
+// LDS of a workgroup: the double-buffered x chunks (KW per round), reused
+// after the loop for the K-group partials, then one W stage per wave.
+constexpr int tlds_red_bytes(int op, int FM, int FN, int NW, int KW) {
+  return (KW - 1) * (NW / KW) * 64 * op_groups(op) * FN * FM * 4 * 4;
+}
+constexpr int tlds_lds_bytes(int op, int FM, int FN, int NW, int KW) {
+  const int xb = 2 * KW * 16 * FM * tlds_xrow_stride(op), rb = tlds_red_bytes(op, FM, FN, NW, KW);
+  return (xb > rb ? xb : rb) + NW * tlds_wstage_bytes(op, FN);
 }
 
-template <int OP, int FM, int FN, int S, int P, int NW>
+template <int OP, int FM, int FN, int S, int P, int NW, int KW>
 __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   constexpr int NT = 64 * NW;                     // threads of the workgroup
+  constexpr int NG = NW / KW;                     // wave groups along N (KW waves each split K)
   constexpr int G = op_groups(OP);
   constexpr int KCH = LdsChunk<OP>::value;
   constexpr int WB = op_w_bytes(OP);
   constexpr int XB = op_x_bytes(OP);
-  using Round = LdsRound<OP, FM, FN, NW>;
+  using Round = LdsRound<OP, FM, FN, NW, KW>;
   constexpr int XPIECES = Round::XPIECES;
   constexpr int XPT = Round::XPT;
   constexpr int XS = tlds_xrow_stride(OP);        // LDS x row stride
   constexpr int PPR = tlds_xrow_bytes(OP) / 16;   // 16-byte x pieces per chunk row
-  constexpr int BUFB = 16 * FM * XS;              // bytes of one LDS x buffer
+  constexpr int SUBB = 16 * FM * XS;              // bytes of one x chunk in LDS
+  constexpr int BUFB = KW * SUBB;                 // bytes of one LDS x buffer (a round's KW chunks)
+  constexpr int XBUF = 2 * BUFB > tlds_red_bytes(OP, FM, FN, NW, KW) ? 2 * BUFB : tlds_red_bytes(OP, FM, FN, NW, KW);
   constexpr int WSTB = tlds_wstage_bytes(OP, FN);  // bytes of one wave's W stage
 
   extern __shared__ __align__(16) unsigned char xl[];   // [2][16*FM][stride] x, then [4][G*FN*16][stride] W
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ng = wave % NG, kw = wave / NG;   // wave-uniform
   const int lr = lane & 15, lq = lane >> 4;
   const int M = a.M, N = a.N, K = a.K;
   const int m_base = blockIdx.y * 16 * FM;
-  const int nb = blockIdx.x * 16 * FN * NW + wave * 16 * FN;
+  const int nb = blockIdx.x * 16 * FN * NG + ng * 16 * FN;
   const int split = blockIdx.z;
   const int kb = a.kb;
   const int NC = (K + KCH - 1) / KCH;          // chunks along K
   const int CPS = (NC + S - 1) / S;            // chunks per split
   const int c_begin = split * CPS;
-  const int rounds = max(0, min(CPS, NC - c_begin));
+  const int c_end = min(c_begin + CPS, NC);    // this split's chunks: [c_begin, c_end)
+  // round r covers chunks c_begin + r*KW + [0, KW); K-group kw takes the kw-th
+  const int rounds = max(0, (c_end - c_begin + KW - 1) / KW);
 
   // W row pointers of the 128-byte segments: load h of a fragment reads row
   // 8h + lane/8 at this lane's 16-byte column lane%8
@@ -717,20 +729,22 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
     }
     wblk[f] = min(nb + f * 16, N - 1) >> 7;
   }
-  unsigned char* wst = xl + 2 * BUFB + wave * WSTB;   // this wave's W stage
-  // x pieces this thread copies into LDS: piece p -> chunk row p/PPR (x row
-  // m_base + p/PPR, clamped to M-1), byte column 16*(p%PPR)
+  unsigned char* wst = xl + XBUF + wave * WSTB;   // this wave's W stage
+  // x pieces this thread copies into LDS: piece p -> the round's chunk
+  // p / (16*FM*PPR), chunk row (p / PPR) % (16*FM) (x row m_base + that,
+  // clamped to M-1), byte column 16*(p%PPR)
   const char* xrowp[XPT];
-  int xcolb[XPT], xdst[XPT];
+  int xcolb[XPT], xdst[XPT], xsub[XPT];
   bool xmine[XPT];
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
     const int p = min((int)threadIdx.x + NT * i, XPIECES - 1);
     xmine[i] = (int)threadIdx.x + NT * i < XPIECES;
-    const int r = p / PPR;
+    xsub[i] = p / (16 * FM * PPR);
+    const int r = (p / PPR) % (16 * FM);
     xcolb[i] = (p % PPR) * 16;
     xrowp[i] = static_cast<const char*>(a.x) + (size_t)min(m_base + r, M - 1) * K * XB;
-    xdst[i] = r * XS + xcolb[i];
+    xdst[i] = xsub[i] * SUBB + r * XS + xcolb[i];
   }
   int xm[FM];
 #pragma unroll
@@ -744,19 +758,37 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
 #pragma unroll
       for (int j = 0; j < FM; ++j) acc[g][f][j] = f32x4{0, 0, 0, 0};
 
-  // First K of this lane's 16-byte W piece h (fragment layout) in chunk c
-  // (c counts from 0 in this split)
+  // This wave's chunk in round c, and the first K of its 16-byte W piece h
+  // (fragment layout) there
+  auto chunk_of = [&](int c, int q) { return c_begin + c * KW + q; };
   auto wk = [&](int c, int h) {
-    const int k0 = (c_begin + c) * KCH;
+    const int k0 = chunk_of(c, kw) * KCH;
     if constexpr (OP == OP_A8W8) return k0 + h * 64 + lq * 16;
     else if constexpr (OP == OP_FP8T) return k0 + lq * 32 + h * 16;
     else return k0 + h * 32 + lq * 8;
   };
   constexpr int LK = OP == OP_BF16 || OP == OP_GATED ? 8 : 16;   // K per 16-byte W load
 
+  // Each round issues its x loads (and A8W8 scales) before its W loads: the
+  // hardware retires a wave's loads in issue order, so the x copy into LDS,
+  // which every wave must finish before the chunk's barrier, waits only for
+  // L2-resident x and never for the wave's own HBM weight stream.
   auto load = [&](Round& b, int c) {
     c = min(c, max(rounds - 1, 0));
-    const int chunk = min(c_begin + c, NC - 1);
+    const int chunk = min(chunk_of(c, kw), NC - 1);
+    // x: 16-byte pieces of the round's chunk rows; a piece of a chunk past the
+    // split or past K re-reads in-range data (finite, against zeroed weights)
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int off = min(min(chunk_of(c, xsub[i]), NC - 1) * KCH * XB + xcolb[i], K * XB - 16);
+      b.x[i] = *reinterpret_cast<const u32x4*>(xrowp[i] + off);
+    }
+    if constexpr (OP == OP_A8W8) {
+#pragma unroll
+      for (int j = 0; j < FM; ++j) b.sx[j] = a.s0[(size_t)xm[j] * kb + chunk];
+#pragma unroll
+      for (int f = 0; f < FN; ++f) b.sw[f] = a.s1[(size_t)wblk[f] * kb + chunk];
+    }
     {
       // segment h of every fragment: 128 bytes of 8 rows; a segment piece past
       // K re-reads the last in-range piece (its weights are zeroed when used)
@@ -769,26 +801,18 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
           for (int f = 0; f < FN; ++f)
             b.w[g][f][h] = load_nt(reinterpret_cast<const u32x4*>(wrow[g][f][h] + off));
     }
-    // x: 16-byte pieces of the chunk rows; a piece past K re-reads
-    // the last in-range piece (finite data against zeroed weights)
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int off = min(chunk * KCH * XB + xcolb[i], K * XB - 16);
-      b.x[i] = *reinterpret_cast<const u32x4*>(xrowp[i] + off);
-    }
-    if constexpr (OP == OP_A8W8) {
-#pragma unroll
-      for (int j = 0; j < FM; ++j) b.sx[j] = a.s0[(size_t)xm[j] * kb + chunk];
-#pragma unroll
-      for (int f = 0; f < FN; ++f) b.sw[f] = a.s1[(size_t)wblk[f] * kb + chunk];
-    }
   };
 
   auto compute = [&](const Round& b0, int c, auto tail) {
     Round b = b0;
     unsigned char* buf = xl + (c & 1) * BUFB;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i)
+      if (XPIECES % NT == 0 || xmine[i]) *reinterpret_cast<u32x4*>(buf + xdst[i]) = b.x[i];
+    __syncthreads();
     {
-      // stage the 128-byte segments (row 8h + lane/8, column lane%8) ...
+      // the wave's own W stage needs no barrier (a wave's LDS accesses run in
+      // order): stage the 128-byte segments (row 8h + lane/8, column lane%8) ...
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -798,10 +822,6 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
             *reinterpret_cast<u32x4*>(wst + ((g * FN + f) * 16 + 8 * h + (lane >> 3)) * kWRowStride +
                                       (lane & 7) * 16) = b0.w[g][f][h];
     }
-#pragma unroll
-    for (int i = 0; i < XPT; ++i)
-      if (XPIECES % NT == 0 || xmine[i]) *reinterpret_cast<u32x4*>(buf + xdst[i]) = b.x[i];
-    __syncthreads();
     {
       // ... and read them back in fragment layout: row lr, the 16-byte piece h
       // of K-slot lq (fp8 weights with bf16 x: lane slot lq owns the 32
@@ -815,10 +835,10 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
             b.w[g][f][h] = *reinterpret_cast<const u32x4*>(
                 wst + ((g * FN + f) * 16 + lr) * kWRowStride + (OP == OP_FP8T ? lq * 32 + h * 16 : h * 64 + lq * 16));
     }
-    if constexpr (decltype(tail)::value) {        // lanes past K contribute nothing
+    if constexpr (decltype(tail)::value) {        // lanes past K or past the split contribute nothing
 #pragma unroll
       for (int h = 0; h < Round::WPF; ++h) {
-        const bool dead = wk(c, h) >= K;
+        const bool dead = wk(c, h) >= K || chunk_of(c, kw) >= c_end;
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -834,7 +854,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
-          B[u][j] = *reinterpret_cast<const u32x4*>(buf + (j * 16 + lr) * XS + u * 64 + lq * 16);
+          B[u][j] = *reinterpret_cast<const u32x4*>(buf + kw * SUBB + (j * 16 + lr) * XS + u * 64 + lq * 16);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -854,7 +874,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
-          B[u][j] = *reinterpret_cast<const u32x4*>(buf + (j * 16 + lr) * XS + lq * 64 + u * 16);
+          B[u][j] = *reinterpret_cast<const u32x4*>(buf + kw * SUBB + (j * 16 + lr) * XS + lq * 64 + u * 16);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -882,7 +902,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
         u32x4 B16[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          B16[h] = *reinterpret_cast<const u32x4*>(buf + (j * 16 + lr) * XS + h * 64 + lq * 16);
+          B16[h] = *reinterpret_cast<const u32x4*>(buf + kw * SUBB + (j * 16 + lr) * XS + h * 64 + lq * 16);
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
           f32x4 t = f32x4{0, 0, 0, 0};
@@ -905,6 +925,44 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   Round ring[P];
   ring_pipeline<P>(ring, rounds, load, compute);
 
+  // ---- K groups: waves kw > 0 hand their sums to wave kw = 0 of the same N
+  // group through LDS (the x buffers are free once every wave is past its
+  // last chunk), added in kw order
+  const bool owner = KW == 1 || kw == 0;
+  if constexpr (KW > 1) {
+    constexpr int NV = G * FN * FM * 4;   // accumulator values per lane
+    float* red = reinterpret_cast<float*>(xl);
+    __syncthreads();
+    if (kw > 0) {
+      float* dst = red + ((size_t)((kw - 1) * NG + ng) * NV) * 64;
+      int i = 0;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+          for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e, ++i) dst[i * 64 + lane] = acc[g][f][j][e];
+    }
+    __syncthreads();
+    if (kw == 0) {
+#pragma unroll
+      for (int q = 1; q < KW; ++q) {
+        const float* src = red + ((size_t)((q - 1) * NG + ng) * NV) * 64;
+        int i = 0;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int f = 0; f < FN; ++f)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+              for (int e = 0; e < 4; ++e, ++i) acc[g][f][j][e] += src[i * 64 + lane];
+      }
+    }
+  }
+
   unsigned short* y = static_cast<unsigned short*>(a.y);
   float scale = 1.0f;
   if constexpr (OP == OP_FP8T) scale = a.s0[0];
@@ -914,7 +972,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
         const int m = m_base + j * 16 + lr;
-        if (m >= M) continue;
+        if (!owner || m >= M) continue;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int n = nb + f * 16 + lq * 4 + e;
@@ -936,7 +994,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
         const int m = m_base + j * 16 + lr;
-        if (m >= M) continue;
+        if (!owner || m >= M) continue;
         const int n = nb + f * 16 + lq * 4;       // this lane's 4 consecutive outputs
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -961,13 +1019,14 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
              (unsigned)(S - 1);
     __syncthreads();
     if (last) {                                   // workgroup-uniform
-      constexpr int TW = 16 * FN * NW, TH = 16 * FM;
+      constexpr int TW = 16 * FN * NG, TH = 16 * FM;
       const int n0 = blockIdx.x * TW;
       if (vec) {
         // quads of 4 outputs: thread t takes quads t, t + NT, ...; every load
         // is issued before the sums
         constexpr int QPR = TW / 4;               // quads per tile row
-        constexpr int T = TH * QPR / NT;          // quads per thread (TH*QPR is a multiple of NT)
+        constexpr int Q = TH * QPR;               // quads of the tile
+        constexpr int T = (Q + NT - 1) / NT;      // quads per thread
         constexpr int TB0 = 32 / (S * G);         // quads per batch: at most 128 registers in flight
         constexpr int TB = TB0 < 1 ? 1 : (TB0 > T ? T : TB0);
 #pragma unroll
@@ -975,7 +1034,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
           f32x4 pv[TB][S][G];
 #pragma unroll
           for (int tb = 0; tb < TB; ++tb) {
-            const int q = threadIdx.x + NT * min(t0 + tb, T - 1);
+            const int q = min((int)threadIdx.x + NT * min(t0 + tb, T - 1), Q - 1);
             const int m = min(m_base + q / QPR, M - 1), n = min(n0 + 4 * (q % QPR), N - 4);
 #pragma unroll
             for (int sp = 0; sp < S; ++sp)
@@ -990,7 +1049,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
             if (t0 + tb >= T) continue;
             const int q = threadIdx.x + NT * (t0 + tb);
             const int m = m_base + q / QPR, n = n0 + 4 * (q % QPR);
-            if (m >= M || n >= N) continue;
+            if (q >= Q || m >= M || n >= N) continue;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               float v = 0.0f, u = 0.0f;
@@ -1054,12 +1113,13 @@ hipError_t launch_tile(const Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int OP, int FM, int FN, int S, int P, int NW>
+template <int OP, int FM, int FN, int S, int P, int NW, int KW>
 hipError_t launch_tlds(const Args& a, hipStream_t s) {
-  const unsigned gx = (unsigned)((a.N + 16 * FN * NW - 1) / (16 * FN * NW));
+  constexpr int TW = 16 * FN * (NW / KW);
+  const unsigned gx = (unsigned)((a.N + TW - 1) / TW);
   const unsigned gy = (unsigned)((a.M + 16 * FM - 1) / (16 * FM));
-  const size_t smem = (size_t)tlds_lds_bytes(OP, FM, FN, NW);
-  hipLaunchKernelGGL((tlds_kernel<OP, FM, FN, S, P, NW>), dim3(gx, gy, S), dim3(64 * NW), smem, s, a);
+  const size_t smem = (size_t)tlds_lds_bytes(OP, FM, FN, NW, KW);
+  hipLaunchKernelGGL((tlds_kernel<OP, FM, FN, S, P, NW, KW>), dim3(gx, gy, S), dim3(64 * NW), smem, s, a);
   return hipGetLastError();
 }
 
@@ -1074,9 +1134,9 @@ constexpr LaunchFn tile_fn() {
   else return nullptr;
 }
 
-template <int OP, int FM, int FN, int S, int P, int NW>
+template <int OP, int FM, int FN, int S, int P, int NW, int KW>
 constexpr LaunchFn tlds_fn() {
-  if constexpr (tlds_valid(OP, FM, FN, S, P, NW)) return &launch_tlds<OP, FM, FN, S, P, NW>;
+  if constexpr (tlds_valid(OP, FM, FN, S, P, NW, KW)) return &launch_tlds<OP, FM, FN, S, P, NW, KW>;
   else return nullptr;
 }
 
@@ -1096,11 +1156,11 @@ constexpr TileRow tile_row() {
 }
 
 // Buckets above MC fragments launch the MC-fragment kernel over more grid rows.
-template <int OP, int FN, int S, int P, int MC, int NW>
+template <int OP, int FN, int S, int P, int MC, int NW, int KW>
 constexpr TileRow tlds_row() {
-  return TileRow{{tlds_fn<OP, tlds_fm(1, MC), FN, S, P, NW>(), tlds_fn<OP, tlds_fm(2, MC), FN, S, P, NW>(),
-                  tlds_fn<OP, tlds_fm(4, MC), FN, S, P, NW>(), tlds_fn<OP, tlds_fm(6, MC), FN, S, P, NW>(),
-                  tlds_fn<OP, tlds_fm(8, MC), FN, S, P, NW>()}};
+  return TileRow{{tlds_fn<OP, tlds_fm(1, MC), FN, S, P, NW, KW>(), tlds_fn<OP, tlds_fm(2, MC), FN, S, P, NW, KW>(),
+                  tlds_fn<OP, tlds_fm(4, MC), FN, S, P, NW, KW>(), tlds_fn<OP, tlds_fm(6, MC), FN, S, P, NW, KW>(),
+                  tlds_fn<OP, tlds_fm(8, MC), FN, S, P, NW, KW>()}};
 }
 
 // Launch tables, one pair per op, defined in ops_<op>.hip:

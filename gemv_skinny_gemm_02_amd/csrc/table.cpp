@@ -3,6 +3,7 @@
 #include "table.hpp"
 
 #include <cctype>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -312,17 +313,21 @@ int Table::load(const std::string& path, const Identity& self, std::string* err)
 // The untuned entry point: what runs with no table, and the incumbent a table
 // entry has to beat.  A shape rule fitted to gfx950 measurements of the whole
 // variant list over the decode shapes:
-//  * rows 1..3, rows 4 unless both operands are fp8, and rows up to 12 when
-//    the weight is under 16 MiB or is fp8 with bf16 x: the VALU weight
-//    stream.  Two weight rows per wave for one row of x, four for more, eight
-//    for a vocabulary-sized N (>= 65536) with more than one row of x; K split
-//    over the 4 waves of a workgroup unless a weight row is under 2 KiB, where
-//    the 4 waves take different rows instead.
-//  * small weights (<= 4 MiB) at rows 16..32: the register MFMA tile.
-//  * otherwise the LDS-shared MFMA tile, with K split S ways so that the
-//    64-row output tiles times S come to about 256 workgroups or more: S = 4
-//    up to 8192 weight rows (gate and up rows counted), 2 up to 16384, else 1;
-//    two chunks in flight from the rows-96 bucket, four below.
+//  * rows 1..3, rows 4 unless the weight is fp8, and rows up to 8 when the
+//    weight is under 16 MiB: the VALU weight stream.  Two weight rows per
+//    wave for one row of x, four for more, eight for a vocabulary-sized N
+//    (>= 65536) with more than one row of x; K split over the 4 waves of a
+//    workgroup unless a weight row is under 2 KiB, where the 4 waves take
+//    different rows instead.
+//  * weights under 16 MiB above that: the LDS tile with 16 weight rows per
+//    workgroup and K split over its 4 waves (no cross-workgroup combine).
+//  * rows 6..16 where a weight row holds at least 4 KiB and the 16-row tiles
+//    come in whole multiples of 256 (one or more per CU): the same.
+//  * otherwise the LDS tile with K split S ways across workgroups, so that
+//    the 64-row output tiles times S come to about 256 workgroups or more:
+//    S = 4 up to 8192 weight rows (gate and up rows counted), 2 up to 16384,
+//    else 1; at most 4 fragments of x rows per workgroup from the rows-64
+//    bucket, and eight-wave workgroups from the rows-96 bucket.
 // `allow_ws` false keeps to variants that need no split-K workspace.
 namespace {
 
@@ -344,28 +349,35 @@ int default_pick(int op, int M, int N, int K, bool allow_ws) {
   const int b = M > kMaxBucket ? kMaxBucket : bucket_of(M);
   const double wbytes = (double)N * K * op_w_bytes(op) * op_groups(op);
   const double wrows = (double)N * op_groups(op);
+  const double rowb = (double)K * op_w_bytes(op);
   const double MiB = 1024.0 * 1024.0;
-  const bool gemv = b <= 3 || (b == 4 && op != OP_A8W8) || (b <= 12 && (wbytes < 16 * MiB || op == OP_FP8T));
+  const bool small_w = wbytes < 16 * MiB;
+  const bool gemv = b <= 3 || (b == 4 && op != OP_A8W8 && op != OP_FP8T) || (small_w && b <= 8);
   int v = -1;
   if (gemv) {
-    if ((double)K * op_w_bytes(op) < 2048) v = first_supported(op, M, {"gemv_r4_k1_p2", "gemv_r4_k2_p2"});
+    if (rowb < 2048) v = first_supported(op, M, {"gemv_r4_k1_p2", "gemv_r4_k2_p2"});
     else if (M == 1) v = first_supported(op, M, {"gemv_r2_k4_p1", "gemv_r4_k4_p1"});
     else if (N >= 65536) v = first_supported(op, M, {"gemv_r8_k4_p1", "gemv_r4_k4_p1", "gemv_r2_k4_p1"});
     else v = first_supported(op, M, {"gemv_r4_k4_p1", "gemv_r2_k4_p1", "gemv_r1_k4_p2"});
     if (v < 0) v = first_of_family(op, M, FAM_GEMV);
-  } else if (wbytes <= 4 * MiB && b <= 32) {
-    v = first_supported(op, M, {"tile_f1_k4_p4", "tile_f1_k4_p2"});
+  } else if (small_w) {
+    if (b <= 32 || wbytes <= 4 * MiB) v = first_supported(op, M, {"tlds_k4_f1_s1_p4_m1", "tlds_k4_f1_s1_p4_m2"});
+    else if (b <= 64) v = first_supported(op, M, {"tlds_k4_f1_s1_p4_m2", "tlds_k4_f1_s1_p4_m1"});
+    else v = first_supported(op, M, {"tlds_w8_k4_f1_s1_p4_m2", "tlds_k4_f1_s1_p4_m2"});
+  } else if (b <= 16 && rowb >= 4096 && std::fmod(wrows, 16.0 * 256.0) == 0.0) {
+    v = first_supported(op, M, {"tlds_k4_f1_s1_p4_m2", "tlds_k4_f1_s1_p4_m1"});
   } else {
     const int S = !allow_ws ? 1 : wrows <= 8192 ? 4 : wrows <= 16384 ? 2 : 1;
     // the capped variants (at most 4 or 2 fragments of x rows per workgroup)
-    // serve forms whose full-height tile does not fit the register budget
+    // also serve forms whose full-height tile does not fit the register budget
     if (S == 4)
-      v = first_supported(op, M, {b >= 96 ? "tlds_f1_s4_p2" : "tlds_f1_s4_p4", "tlds_f1_s4_p2", "tlds_f1_s4_p4_m4",
-                                  "tlds_f1_s4_p4_m2"});
+      v = b <= 32 ? first_supported(op, M, {"tlds_f1_s4_p4", "tlds_f1_s4_p4_m4", "tlds_f1_s4_p4_m2"})
+          : b <= 64 ? first_supported(op, M, {"tlds_f1_s4_p4_m4", "tlds_f1_s4_p4_m2"})
+                    : first_supported(op, M, {"tlds_w8_f1_s4_p4_m4", "tlds_f1_s4_p4_m4", "tlds_f1_s4_p4_m2"});
     else if (S == 2)
-      v = first_supported(op, M, {"tlds_f1_s2_p4", "tlds_f1_s2_p8", "tlds_f1_s2_p4_m4", "tlds_f1_s2_p4_m2"});
+      v = first_supported(op, M, {b <= 32 ? "tlds_f1_s2_p4" : "tlds_f1_s2_p4_m4", "tlds_f1_s2_p4_m4", "tlds_f1_s2_p4_m2"});
     else
-      v = first_supported(op, M, {"tlds_f1_s1_p4", "tlds_f1_s1_p4_m4", "tlds_f1_s1_p4_m2"});
+      v = first_supported(op, M, {b <= 32 ? "tlds_f1_s1_p4" : "tlds_f1_s1_p4_m4", "tlds_f1_s1_p4_m4", "tlds_f1_s1_p4_m2"});
   }
   if (v < 0) v = first_supported(op, M, {"tile_f1_k4_p4", "tile_f1_k4_p2"});
   if (v < 0) v = first_of_family(op, M, FAM_TILE);

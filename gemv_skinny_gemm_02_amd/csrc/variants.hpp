@@ -81,29 +81,37 @@ constexpr bool tile_valid(int op, int FM, int FN, int KS, int P) {
          (128 % ((4 / KS) * FN * 16)) == 0;
 }
 // LDS-shared-x tile path (tlds): 64*FN W rows per workgroup, S-way split-K.
-constexpr int tlds_xpt(int op, int FM, int NW) {
+constexpr int tlds_xpt(int op, int FM, int NW, int KW) {
   const int ppr = op == OP_FP8T ? 16 : 8;   // 16-byte x pieces per chunk row
-  return (16 * FM * ppr + 64 * NW - 1) / (64 * NW);
+  return (KW * 16 * FM * ppr + 64 * NW - 1) / (64 * NW);
 }
-constexpr int tlds_regs(int op, int FM, int FN, int P, int NW) {
+constexpr int tlds_regs(int op, int FM, int FN, int P, int NW, int KW) {
   const int G = op_groups(op);
-  const int per_chunk = G * FN * 2 * 4 + tlds_xpt(op, FM, NW) * 4 + (op == OP_A8W8 ? FM + FN : 0);
+  const int per_chunk = G * FN * 2 * 4 + tlds_xpt(op, FM, NW, KW) * 4 + (op == OP_A8W8 ? FM + FN : 0);
   const int acc = G * FN * FM * 4;
   const int xfrag = op == OP_FP8T ? 16 * FM : (op == OP_BF16 || op == OP_GATED ? 8 * FM : 0);   // a chunk's x fragments
   return P * per_chunk + acc * (op == OP_A8W8 ? 2 : 1) + FM * 4 + xfrag;
 }
-constexpr bool tlds_valid(int op, int FM, int FN, int S, int P, int NW) {
+// LDS bytes a tlds workgroup takes (x chunks or K-group partials, W stages).
+constexpr int tlds_smem(int op, int FM, int FN, int NW, int KW) {
+  const int xs = (op_w_fp8(op) ? 128 : 64) * op_x_bytes(op) + 16;
+  const int xb = 2 * KW * 16 * FM * xs;
+  const int rb = (KW - 1) * (NW / KW) * 64 * op_groups(op) * FN * FM * 16;
+  return (xb > rb ? xb : rb) + NW * op_groups(op) * FN * 16 * 144;
+}
+constexpr bool tlds_valid(int op, int FM, int FN, int S, int P, int NW, int KW) {
   const int G = op_groups(op);
-  return (S == 1 || S == 2 || S == 4 || S == 8) && (NW == 4 || NW == 8) && P >= 1 && G * FN * FM * 4 <= 128 &&
-         tlds_regs(op, FM, FN, P, NW) <= 224 && (128 % (64 * FN)) == 0;
+  return (S == 1 || S == 2 || S == 4 || S == 8) && (NW == 4 || NW == 8) && (KW == 1 || KW == 2 || KW == 4 || KW == 8) &&
+         NW % KW == 0 && P >= 1 && G * FN * FM * 4 <= 128 && tlds_regs(op, FM, FN, P, NW, KW) <= 224 &&
+         tlds_smem(op, FM, FN, NW, KW) <= 64 * 1024 && (128 % (64 * FN)) == 0;
 }
 // Bytes of split-K partials a tlds launch with S > 1 needs, and the number of
 // output tiles (one arrival counter each) its grid has.
 constexpr unsigned long long tlds_ws_bytes(int op, int S, int M, int N) {
   return S > 1 ? (unsigned long long)S * op_groups(op) * M * N * 4ull : 0ull;
 }
-constexpr unsigned long long tlds_tiles(int FN, int NW, int FM, int M, int N) {
-  return (unsigned long long)((N + 16 * FN * NW - 1) / (16 * FN * NW)) *
+constexpr unsigned long long tlds_tiles(int FN, int NG, int FM, int M, int N) {
+  return (unsigned long long)((N + 16 * FN * NG - 1) / (16 * FN * NG)) *
          (unsigned long long)((M + 16 * FM - 1) / (16 * FM));
 }
 // M fragments a tlds workgroup takes: the bucket's count, capped at MC.
@@ -117,13 +125,13 @@ constexpr int kSplitCounters = 65536;   // arrival counters kept in the workspac
 struct VariantDesc {
   const char* name;
   int family;
-  int p0, p1, p2, p3, p4;  // GEMV: R, KS, U.  TILE: FN, KS, U.  TLDS: FN, S, P, MC, NW.
+  int p0, p1, p2, p3, p4, p5;  // GEMV: R, KS, U.  TILE: FN, KS, U.  TLDS: FN, S, P, MC, NW, KW.
 };
 
 constexpr VariantDesc kVariants[] = {
-#define SKG_GEMV(name, R, KS, U) {#name, FAM_GEMV, R, KS, U, 0, 0},
-#define SKG_TILE(name, FN, KS, U) {#name, FAM_TILE, FN, KS, U, 0, 0},
-#define SKG_TLDS(name, FN, S, P, MC, NW) {#name, FAM_TLDS, FN, S, P, MC, NW},
+#define SKG_GEMV(name, R, KS, U) {#name, FAM_GEMV, R, KS, U, 0, 0, 0},
+#define SKG_TILE(name, FN, KS, U) {#name, FAM_TILE, FN, KS, U, 0, 0, 0},
+#define SKG_TLDS(name, FN, S, P, MC, NW, KW) {#name, FAM_TLDS, FN, S, P, MC, NW, KW},
 #include "variants.def"
 #undef SKG_GEMV
 #undef SKG_TILE
@@ -154,7 +162,7 @@ constexpr bool variant_supports(int op, int i, int M) {
     return mi >= 0 && gemv_valid(op, kGemvMT[mi], v.p0, v.p1, v.p2);
   }
   const int fm = M > kMaxBucket ? kNumTileFM - 1 : tile_fm_index(M);
-  if (v.family == FAM_TLDS) return tlds_valid(op, tlds_fm(kTileFM[fm], v.p3), v.p0, v.p1, v.p2, v.p4);
+  if (v.family == FAM_TLDS) return tlds_valid(op, tlds_fm(kTileFM[fm], v.p3), v.p0, v.p1, v.p2, v.p4, v.p5);
   return tile_valid(op, kTileFM[fm], v.p0, v.p1, v.p2);
 }
 
@@ -167,12 +175,12 @@ constexpr const char kSpaceText[] =
     "buckets=1,2,3,4,6,8,12,16,24,32,64,96,128;gemv_mt=1,2,3,4,6,8,12,16;tile_fm=1,2,4,6,8;tile_min=1;"
 #define SKG_GEMV(name, R, KS, U) "G:" #name "," #R "," #KS "," #U ";"
 #define SKG_TILE(name, FN, KS, U) "T:" #name "," #FN "," #KS "," #U ";"
-#define SKG_TLDS(name, FN, S, P, MC, NW) "L:" #name "," #FN "," #S "," #P "," #MC "," #NW ";"
+#define SKG_TLDS(name, FN, S, P, MC, NW, KW) "L:" #name "," #FN "," #S "," #P "," #MC "," #NW "," #KW ";"
 #include "variants.def"
 #undef SKG_GEMV
 #undef SKG_TILE
 #undef SKG_TLDS
-    "kernels=11";  // bump when a kernel's arithmetic or indexing changes
+    "kernels=14";  // bump when a kernel's arithmetic or indexing changes
 constexpr uint32_t kSpaceToken = fnv1a(kSpaceText);
 
 }  // namespace skg

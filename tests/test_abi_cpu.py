@@ -171,9 +171,10 @@ def test_malformed_and_missing(tmp_path):
 
 
 def test_defaults_follow_the_rows_rule():
-    """The untuned rule: VALU weight stream for few rows (up to 12 for small or
-    fp8-with-bf16-x weights), register tile for small weights at 16..32 rows,
-    LDS tile with a K split sized by N otherwise."""
+    """The untuned rule: VALU weight stream for few rows (up to 8 for small
+    weights), the LDS tile with the K split inside the workgroup for small
+    weights and for 6..16 rows on evenly tiling shapes, the LDS tile with a K
+    split across workgroups sized by N otherwise."""
     skg.skinny_gemm_load_table_as(None, _identity())
     q = lambda op, M, N, K: skg.skinny_gemm_query(op, M, N, K)[0]
     for op in skg.OPS:
@@ -181,23 +182,30 @@ def test_defaults_follow_the_rows_rule():
             assert q(op, M, 4096, 4096).startswith("gemv_"), (op, M)
         for M in (16, 24, 32, 64, 96, 128, 129, 1000):
             assert q(op, M, 4096, 4096).startswith("tlds_"), (op, M)
-    for M in (4, 6, 8, 12):     # bf16 4096x4096 is 32 MiB: LDS tile from 6 rows
-        assert q("bf16", M, 4096, 4096).startswith("gemv_" if M == 4 else "tlds_"), M
-        assert q("bf16", M, 1024, 1024).startswith("gemv_"), M
-        assert q("fp8_tensor", M, 4096, 4096).startswith("gemv_"), M
+    assert q("bf16", 4, 4096, 4096).startswith("gemv_")
+    assert q("fp8_tensor", 4, 248320, 4096).startswith("tlds_")
     assert q("a8w8_block", 4, 8192, 4096).startswith("tlds_")
-    for M in (16, 32):
-        assert q("bf16", M, 1024, 1024).startswith("tile_"), M
-    assert q("bf16", 64, 1024, 1024).startswith("tlds_")
+    for M in (4, 6, 8):         # small weights stay on the VALU stream up to 8 rows
+        assert q("bf16", M, 1024, 1024).startswith("gemv_"), M
+        assert q("bf16", M, 2048, 2048).startswith("gemv_"), M
+    for M in (12, 16, 32, 64, 128):
+        assert q("bf16", M, 1024, 1024).startswith("tlds_k4_"), M
+    assert q("bf16", 128, 2048, 2048) == "tlds_w8_k4_f1_s1_p4_m2"
     # GEMV shape: two rows per wave for one x row, eight for a vocabulary N,
     # one wave per row (no K split) for rows under 2 KiB
     assert q("bf16", 1, 4096, 4096) == "gemv_r2_k4_p1"
     assert q("bf16", 3, 4096, 4096) == "gemv_r4_k4_p1"
     assert q("fp8_tensor", 2, 248320, 4096) == "gemv_r8_k4_p1"
     assert q("a8w8_block", 1, 32768, 1024) == "gemv_r4_k1_p2"
-    # K split: 4 up to 8192 weight rows, 2 up to 16384, else 1 (gated counts both halves)
-    assert q("bf16", 16, 4096, 12288) == "tlds_f1_s4_p4"
-    assert q("bf16", 128, 4096, 12288) == "tlds_f1_s4_p2"
-    assert q("bf16", 16, 12288, 4096) == "tlds_f1_s2_p4"
-    assert q("gated", 16, 12288, 4096) == "tlds_f1_s1_p4"
-    assert q("a8w8_block", 16, 32768, 1024) == "tlds_f1_s1_p4"
+    # in-workgroup K split where the 16-row tiles come in multiples of 256
+    assert q("bf16", 8, 4096, 4096) == "tlds_k4_f1_s1_p4_m2"
+    assert q("gated", 16, 12288, 4096) == "tlds_k4_f1_s1_p4_m2"
+    assert q("a8w8_block", 8, 8192, 4096) == "tlds_k4_f1_s1_p4_m2"
+    assert q("bf16", 8, 6144, 4096) == "tlds_f1_s4_p4"            # 384 tiles: split across workgroups
+    assert q("a8w8_block", 8, 32768, 1024) == "tlds_f1_s1_p4"     # 1 KiB rows
+    # K split across workgroups: 4 up to 8192 weight rows, 2 up to 16384, else 1
+    assert q("bf16", 32, 4096, 12288) == "tlds_f1_s4_p4"
+    assert q("bf16", 64, 4096, 12288) == "tlds_f1_s4_p4_m4"
+    assert q("bf16", 128, 4096, 12288) == "tlds_w8_f1_s4_p4_m4"
+    assert q("bf16", 32, 12288, 4096) == "tlds_f1_s2_p4"
+    assert q("gated", 32, 12288, 4096) == "tlds_f1_s1_p4"
