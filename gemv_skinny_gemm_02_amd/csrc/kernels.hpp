@@ -620,16 +620,20 @@ __global__ __launch_bounds__(256) void tile_kernel(const Args a) {
 }
 
 // ============================================================ TILE (LDS x)
-// MFMA tile path for larger M.  The 4 waves of a workgroup split N (each wave
-// owns FN fragments of 16 W rows: 64*FN rows per workgroup) and share one copy
-// of the x chunk in LDS, so x is read from L2 once per 64*FN W rows instead of
-// once per 16.  K is split across S workgroups (grid z) so that the grid still
-// covers every CU; with S > 1 the workgroups of a tile combine their fp32
-// partials as described below.  W streams through a ring of
-// P chunks in registers; x chunks pass through registers into a double-
-// buffered LDS tile (one barrier per chunk; on gfx950 the barrier waits only for
-// LDS traffic, so the W loads stay in flight).  A chunk is 64 K (bf16 and fp8
-// weights) or one 128-K scale group (A8W8): 128 bytes of each x row.
+// MFMA tile path.  The NW waves of a workgroup form NW/KW groups along N
+// (each wave owns FN fragments of 16 W rows: 16*FN*NW/KW rows per workgroup)
+// of KW waves that split K inside the workgroup; all of them share the x
+// chunks in LDS, so x is read from L2 once per 16*FN*NW/KW W rows instead of
+// once per 16.  A workgroup takes at most MC fragments of 16 x rows; more
+// rows go to more workgroups along grid y.  K can also be split across S
+// workgroups (grid z) so that the grid still covers every CU; with S > 1 the
+// workgroups of a tile combine their fp32 partials as described below.  W
+// streams through a ring of P rounds in registers as 128-byte row segments
+// and reaches the MFMA fragment layout through a per-wave LDS stage; x chunks
+// pass through registers into a double-buffered LDS tile (one barrier per
+// round, which waits only for the x copy: each round's x loads are issued
+// before its W loads, and loads retire in issue order).  After the loop the
+// KW waves of an N group add their sums through LDS in a fixed order.
 //
 // Split-K (S > 1): every workgroup stores its fp32 partial tile with device-
 // coherent stores, waits for them to complete, and counts itself in the

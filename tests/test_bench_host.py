@@ -1,0 +1,45 @@
+"""Host logic of bench.py: the kernel symbol a variant runs as, and the
+traffic lookup in a counter summary (no GPU)."""
+import os
+
+import pytest
+
+import bench
+import gemv_skinny_gemm_02_amd as skg
+
+
+@pytest.mark.parametrize("variant,M,symbol", [
+    ("gemv_r2_k4_p1", 1, "void skg::gemv_kernel<0, 1, 2, 4, 1>(skg::Args)"),
+    ("gemv_r4_k1_p2", 7, "void skg::gemv_kernel<0, 8, 4, 1, 2>(skg::Args)"),
+    ("tile_f1_k4_p4", 24, "void skg::tile_kernel<0, 2, 1, 4, 4>(skg::Args)"),
+    ("tlds_f1_s4_p4", 16, "void skg::tlds_kernel<0, 1, 1, 4, 4, 4, 1>(skg::Args)"),
+    ("tlds_f1_s4_p4", 128, "void skg::tlds_kernel<0, 8, 1, 4, 4, 4, 1>(skg::Args)"),
+    ("tlds_f1_s4_p4_m2", 128, "void skg::tlds_kernel<0, 2, 1, 4, 4, 4, 1>(skg::Args)"),
+    ("tlds_w8_f1_s4_p4_m4", 96, "void skg::tlds_kernel<0, 4, 1, 4, 4, 8, 1>(skg::Args)"),
+    ("tlds_k4_f1_s1_p4_m1", 64, "void skg::tlds_kernel<0, 1, 1, 1, 4, 4, 4>(skg::Args)"),
+    ("tlds_w8_k8_f1_s1_p2_m1", 128, "void skg::tlds_kernel<0, 1, 1, 1, 2, 8, 8>(skg::Args)"),
+    ("tlds_f1_s4_p4", 40, "void skg::tlds_kernel<0, 4, 1, 4, 4, 4, 1>(skg::Args)"),   # 3 fragments -> the 4 build
+])
+def test_kernel_symbol(variant, M, symbol):
+    assert bench.kernel_symbol(variant, M) == symbol
+
+
+def test_every_variant_name_parses():
+    for i, name in enumerate(skg.variants("bf16")):
+        for M in (1, 16, 128):
+            if not skg.skinny_gemm_variant_supports("bf16", i, M):
+                continue
+            sym = bench.kernel_symbol(name, M)
+            assert sym.startswith("void skg::") and sym.endswith("(skg::Args)")
+
+
+def test_read_counters(tmp_path, monkeypatch):
+    os.makedirs(tmp_path / "profiles")
+    (tmp_path / "profiles" / "bf16_sweep_counters.txt").write_text(
+        "# comment\ncode_hash=abc\ncopy_fetch_factor=0.5\ncopy_write_factor=1.0\n"
+        "kernel void skg::k<0>(skg::Args) | 100.0 | 10.0\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    # HBM bytes = (FETCH / fetch factor + WRITE / write factor) KiB
+    assert bench.read_counters("void skg::k<0>(skg::Args)", "abc") == (100.0 / 0.5 + 10.0) * 1024
+    assert bench.read_counters("void skg::k<1>(skg::Args)", "abc") is None     # kernel not profiled
+    assert bench.read_counters("void skg::k<0>(skg::Args)", "other") is None   # sources changed since
