@@ -18,7 +18,9 @@ them:
 * an fp8 weight with one scale for the whole tensor (the fp8 draft head --
   mstar PR #1102, "What changed", draft_head: fp8 bullet);
 * A8W8 with block scales (DeepSeek-V4-flash decode round 3, "Retained change
-  2: decode-M rows for the A8W8 bpreshuffle table").
+  2: decode-M rows for the A8W8 bpreshuffle table"), and the same with the
+  activation quantisation folded in (``quant.py``; the same page leaves that
+  fusion as open work in "Rejected paths").
 
 Every function below is pinned by the CPU tests against brute force in exact
 rational arithmetic, exhaustive format tables checked against torch's casts,
@@ -29,8 +31,10 @@ from .formats import (dec_bf16, dec_e4m3fn, E4M3FN_TABLE, bf16_rne_bits,
 from .linear import (linear_bf16, linear_gated, linear_fp8_tensor,
                      linear_a8w8_block, dequant_a8w8, BLOCK)
 from .check import parity, ParityResult, TOL_MAX_REL, TOL_FRO
+from .quant import e4m3fn_rne_bits, quantize_a8w8_x, linear_a8w8_quant, E4M3_MAX
 
 __all__ = ["dec_bf16", "dec_e4m3fn", "E4M3FN_TABLE", "bf16_rne_bits", "silu",
            "linear_bf16", "linear_gated", "linear_fp8_tensor",
            "linear_a8w8_block", "dequant_a8w8", "BLOCK", "parity",
-           "ParityResult", "TOL_MAX_REL", "TOL_FRO"]
+           "ParityResult", "TOL_MAX_REL", "TOL_FRO", "e4m3fn_rne_bits",
+           "quantize_a8w8_x", "linear_a8w8_quant", "E4M3_MAX"]
