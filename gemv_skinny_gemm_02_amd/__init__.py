@@ -12,6 +12,7 @@ Entry points (see include/skinny_gemm.h for the contract):
     skinny_gemm_gated(x, W)                  W = [2N,K]: gate rows then up rows
     skinny_gemm_fp8_tensor(x, W, scales)     bf16 x, e4m3fn W, float32 scales[1]
     skinny_gemm_a8w8_block(x, W, x_scales, w_scales)
+    skinny_gemm_a8w8_block_quant(x, W, w_scales)   bf16 x quantised in the call
 each returning y [M, N] bf16 (or writing into ``y=``).
 """
 from __future__ import annotations
@@ -25,12 +26,13 @@ import torch
 __all__ = [
     "SkinnyGemmError", "lib_path", "load", "OPS",
     "skinny_gemm_bf16", "skinny_gemm_gated", "skinny_gemm_fp8_tensor", "skinny_gemm_a8w8_block",
+    "skinny_gemm_a8w8_block_quant",
     "skinny_gemm_run_variant", "skinny_gemm_query", "skinny_gemm_load_table", "skinny_gemm_load_table_as",
     "skinny_gemm_identity", "skinny_gemm_table_status", "skinny_gemm_num_variants",
     "skinny_gemm_variant_name", "skinny_gemm_variant_supports", "variants", "default_table_path",
 ]
 
-OPS = {"bf16": 0, "gated": 1, "fp8_tensor": 2, "a8w8_block": 3}
+OPS = {"bf16": 0, "gated": 1, "fp8_tensor": 2, "a8w8_block": 3, "a8w8_quant": 4}
 _STATUS = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "ELAUNCH", 4: "ETABLE"}
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +75,8 @@ def load() -> ctypes.CDLL:
             f.restype = i
         lib.skinny_gemm_a8w8_block.argtypes = [vp, vp, fp, fp, vp, i, i, i, vp]
         lib.skinny_gemm_a8w8_block.restype = i
+        lib.skinny_gemm_a8w8_block_quant.argtypes = [vp, vp, fp, fp, vp, i, i, i, vp]
+        lib.skinny_gemm_a8w8_block_quant.restype = i
         lib.skinny_gemm_last_error.argtypes = []
         lib.skinny_gemm_last_error.restype = ctypes.c_char_p
         lib.skinny_gemm_load_table.argtypes = [ctypes.c_char_p]
@@ -186,6 +190,21 @@ def skinny_gemm_a8w8_block(x, W, x_scales, w_scales, y=None, stream=None) -> tor
     return y
 
 
+def skinny_gemm_a8w8_block_quant(x, W, w_scales, x_scales=None, y=None, stream=None) -> torch.Tensor:
+    """A8W8 block scale with x bf16 [M,K] quantised inside the call (per row and
+    128-K group, scale max|x|/448); W e4m3fn [N,K] with w_scales
+    [ceil(N/128), ceil(K/128)]; y [M,N] bf16.  x_scales, if given, is a float32
+    [M, ceil(K/128)] tensor that receives the scales the call used."""
+    M, N, K = _mk(x, W, 1)
+    y = _out(y, M, N, x)
+    _check(load().skinny_gemm_a8w8_block_quant(_dev(x, "x", _BF16, 2), _dev(W, "W", _FP8, 2),
+                                               _dev(w_scales, "w_scales", (torch.float32,), 2),
+                                               _dev(x_scales, "x_scales", (torch.float32,), 2)
+                                               if x_scales is not None else None,
+                                               _dev(y, "y", _BF16, 2), M, N, K, _stream(stream)))
+    return y
+
+
 def skinny_gemm_run_variant(op, variant, x, W, s0=None, s1=None, y=None, stream=None) -> torch.Tensor:
     """Run one named (or numbered) variant of an op, bypassing the table."""
     opi = OPS[op] if isinstance(op, str) else int(op)
@@ -195,7 +214,7 @@ def skinny_gemm_run_variant(op, variant, x, W, s0=None, s1=None, y=None, stream=
             raise ValueError(f"unknown variant {variant!r}")
         variant = names.index(variant)
     xd = _FP8 if opi == 3 else _BF16
-    wd = _FP8 if opi in (2, 3) else _BF16
+    wd = _FP8 if opi in (2, 3, 4) else _BF16
     M, N, K = _mk(x, W, 2 if opi == 1 else 1)
     y = _out(y, M, N, x)
     p0 = _dev(s0, "s0", (torch.float32,), s0.dim()) if s0 is not None else None

@@ -24,7 +24,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libskinny_gemm.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["abi.hip", "ops_bf16.hip", "ops_gated.hip", "ops_fp8t.hip", "ops_a8w8.hip"]
+HIP_SOURCES = ["abi.hip", "ops_bf16.hip", "ops_gated.hip", "ops_fp8t.hip", "ops_a8w8.hip", "ops_a8w8q.hip"]
 CXX_SOURCES = ["table.cpp"]
 
 # Packed fp32 VALU ops are kept out of the device code: hipcc -O3 would form

@@ -189,24 +189,32 @@ skg_status validate(int op, const Args& a) {
   Buf by{a.y, M * N * 2, "y"};
   Buf b0{a.s0, 0, op == OP_A8W8 ? "x_scales" : "scales"};
   Buf b1{a.s1, 0, "w_scales"};
+  Buf bo{a.xs_out, 0, "x_scales_out"};   // an output: may be NULL
   if (op == OP_FP8T) b0.bytes = 4;
   if (op == OP_A8W8 && K > 0) {
     b0.bytes = M * kb * 4;
     b1.bytes = nb * kb * 4;
   }
+  if (op == OP_A8W8Q && K > 0) {
+    b1.bytes = nb * kb * 4;
+    if (a.xs_out) bo.bytes = M * kb * 4;
+  }
   if (K > 0 && ((reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.w)) & 15))
     return fail(SKG_EUNSUPPORTED, "x and W must be 16-byte aligned (x=%p W=%p)", a.x, a.w);
   if (reinterpret_cast<uintptr_t>(a.y) & 1) return fail(SKG_EUNSUPPORTED, "y must be 2-byte aligned");
-  if ((reinterpret_cast<uintptr_t>(a.s0) | reinterpret_cast<uintptr_t>(a.s1)) & 3)
+  if ((reinterpret_cast<uintptr_t>(a.s0) | reinterpret_cast<uintptr_t>(a.s1) |
+       reinterpret_cast<uintptr_t>(a.xs_out)) & 3)
     return fail(SKG_EUNSUPPORTED, "scales must be 4-byte aligned");
   if (K == 0) {
     bx.bytes = bw.bytes = 0;
-    b0.bytes = b1.bytes = 0;
+    b0.bytes = b1.bytes = bo.bytes = 0;
   }
-  for (const Buf* b : {&bx, &bw, &by, &b0, &b1})
+  for (const Buf* b : {&bx, &bw, &by, &b0, &b1, &bo})
     if (skg_status st = check_device_range(*b)) return st;
   for (const Buf* b : {&bx, &bw, &b0, &b1})
     if (overlap(by, *b)) return fail(SKG_EINVAL, "y overlaps %s", b->name);
+  for (const Buf* b : {&bx, &bw, &b1, &by})
+    if (overlap(bo, *b)) return fail(SKG_EINVAL, "x_scales_out overlaps %s", b->name);
   if ((size_t)a.N * (size_t)G > 0x7fffffffu) return fail(SKG_EUNSUPPORTED, "N too large");
   return SKG_OK;
 }
@@ -223,6 +231,7 @@ LaunchFn variant_fn(int op, int v, int M) {
       case OP_GATED: t = gemv_table<OP_GATED>(); break;
       case OP_FP8T: t = gemv_table<OP_FP8T>(); break;
       case OP_A8W8: t = gemv_table<OP_A8W8>(); break;
+      case OP_A8W8Q: t = gemv_table<OP_A8W8Q>(); break;
     }
     return t ? t[fi].f[mi] : nullptr;
   }
@@ -234,6 +243,7 @@ LaunchFn variant_fn(int op, int v, int M) {
     case OP_GATED: t = lds ? tlds_table<OP_GATED>() : tile_table<OP_GATED>(); break;
     case OP_FP8T: t = lds ? tlds_table<OP_FP8T>() : tile_table<OP_FP8T>(); break;
     case OP_A8W8: t = lds ? tlds_table<OP_A8W8>() : tile_table<OP_A8W8>(); break;
+    case OP_A8W8Q: t = lds ? tlds_table<OP_A8W8Q>() : tile_table<OP_A8W8Q>(); break;
   }
   return t ? t[fi].f[fm] : nullptr;
 }
@@ -357,10 +367,10 @@ skg_status launch(int op, int v, const Args& a_in, hipStream_t s) {
 }
 
 skg_status run_op(int op, const void* x, const void* w, const float* s0, const float* s1, void* y, int M, int N,
-                  int K, hipStream_t s) {
-  Args a{x, w, s0, s1, y, M, N, K, (K + 127) / 128, nullptr, nullptr};
+                  int K, hipStream_t s, float* xs_out = nullptr) {
+  Args a{x, w, s0, s1, y, M, N, K, (K + 127) / 128, nullptr, nullptr, op == OP_A8W8Q ? xs_out : nullptr};
   if (op != OP_FP8T && op != OP_A8W8) a.s0 = nullptr;
-  if (op != OP_A8W8) a.s1 = nullptr;
+  if (op != OP_A8W8 && op != OP_A8W8Q) a.s1 = nullptr;
   if (skg_status st = validate(op, a)) return st;
   if (M == 0 || N == 0) return SKG_OK;
   prime_workspace(s);
@@ -406,6 +416,11 @@ skg_status skinny_gemm_fp8_tensor(const void* x, const void* W, const float* sca
 skg_status skinny_gemm_a8w8_block(const void* x, const void* W, const float* x_scales, const float* w_scales,
                                   void* y, int M, int N, int K, hipStream_t stream) {
   return run_op(OP_A8W8, x, W, x_scales, w_scales, y, M, N, K, stream);
+}
+
+skg_status skinny_gemm_a8w8_block_quant(const void* x, const void* W, const float* w_scales, float* x_scales_out,
+                                        void* y, int M, int N, int K, hipStream_t stream) {
+  return run_op(OP_A8W8Q, x, W, nullptr, w_scales, y, M, N, K, stream, x_scales_out);
 }
 
 const char* skinny_gemm_last_error(void) { return g_err.c_str(); }
@@ -483,9 +498,10 @@ skg_status skinny_gemm_run_variant(int op, int variant, const int* knobs, const 
   if (!op_name(op)) return fail(SKG_EINVAL, "unknown op %d", op);
   if (variant < 0 || variant >= kNumVariants) return fail(SKG_EINVAL, "no variant %d", variant);
   if (knobs) return fail(SKG_EINVAL, "knobs are reserved: pass NULL");
-  Args a{x, W, s0, s1, y, M, N, K, (K + 127) / 128, nullptr, nullptr};
+  Args a{x, W, s0, s1, y, M, N, K, (K + 127) / 128, nullptr, nullptr, nullptr};
+  if (op == OP_A8W8Q) a.xs_out = const_cast<float*>(s0);   // its s0 is the x-scale output
   if (op != OP_FP8T && op != OP_A8W8) a.s0 = nullptr;
-  if (op != OP_A8W8) a.s1 = nullptr;
+  if (op != OP_A8W8 && op != OP_A8W8Q) a.s1 = nullptr;
   if (skg_status st = validate(op, a)) return st;
   if (M == 0 || N == 0) return SKG_OK;
   if (!variant_supports(op, variant, M))

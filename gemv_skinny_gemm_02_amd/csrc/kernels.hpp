@@ -36,12 +36,13 @@ struct Args {
   const void* x;
   const void* w;
   const float* s0;  // fp8 tensor: w_scale[1]; a8w8: x_scales[M, kb]
-  const float* s1;  // a8w8: w_scales[ceil(N/128), kb]
+  const float* s1;  // a8w8 (both forms): w_scales[ceil(N/128), kb]
   void* y;
   int M, N, K;
   int kb;           // ceil(K / 128): scale groups along K
   float* ws;        // split-K partials [S][G][M][N] fp32 (tlds variants with S > 1)
   unsigned* cnt;    // split-K arrival counters, one per output tile, zero between calls
+  float* xs_out;    // a8w8 with x quantised here: the x scales [M, kb] it computes, or NULL
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -647,41 +648,91 @@ __global__ __launch_bounds__(256) void tile_kernel(const Args a) {
 // A chunk is 128 bytes of every W row: 64 K for bf16 weights, 128 K for fp8
 // weights (for A8W8 also one 128-K scale group).  Its x rows are 128 bytes
 // (bf16 and fp8 x with 128-byte W rows) or 256 bytes (bf16 x with fp8 W).
+// With x quantised in the kernel (OP_A8W8Q) the 256 bytes of bf16 x per row
+// become 128 fp8 codes in LDS, with the row's float32 scale after the chunk.
 template <int OP>
 struct LdsChunk {
-  static constexpr int value = op_w_fp8(OP) ? 128 : 64;
+  static constexpr int value = tlds_kch(OP);
 };
-constexpr int tlds_xrow_bytes(int op) { return (op_w_fp8(op) ? 128 : 64) * op_x_bytes(op); }
-constexpr int tlds_xrow_stride(int op) { return tlds_xrow_bytes(op) + 16; }   // rows start 4 banks apart
-constexpr int kWRowStride = 144;           // W stage rows: 128 bytes + 16 of padding
 
 template <int OP, int FM, int FN, int NW, int KW>
 struct LdsRound {
   static constexpr int WPF = 2;                                              // 16-byte W loads per fragment per chunk
-  static constexpr int XPIECES = KW * 16 * FM * tlds_xrow_bytes(OP) / 16;   // 16-byte pieces of the round's x chunks
+  static constexpr int XPIECES = KW * 16 * FM * tlds_xg_bytes(OP) / 16;    // 16-byte pieces of the round's x chunks
   static constexpr int XPT = (XPIECES + 64 * NW - 1) / (64 * NW);      // pieces per thread
   u32x4 w[op_groups(OP)][FN][WPF];
   u32x4 x[XPT];
   float sx[OP == OP_A8W8 ? FM : 1];
-  float sw[OP == OP_A8W8 ? FN : 1];
+  float sw[OP == OP_A8W8 || OP == OP_A8W8Q ? FN : 1];
 };
+
+// The maximum of v over each row of 16 lanes, in every lane of the row (DPP
+// within the row: swap neighbours, swap pairs, mirror the half rows, mirror
+// the row).  Every lane of the row must be active.
+__device__ __forceinline__ unsigned row16_max(unsigned v) {
+  v = max(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));    // quad_perm [1,0,3,2]
+  v = max(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));    // quad_perm [2,3,0,1]
+  v = max(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true));   // row_half_mirror
+  v = max(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true));   // row_mirror
+  return v;
+}
+
+// Eight bf16 x of one 128-K group, whose largest magnitude is amax (> 0),
+// -> eight OCP e4m3fn codes (byte e of the result holds element e), and the
+// group's scale s = amax / 448 rounded once to float32.  Each code is the
+// round-to-nearest-even e4m3fn value of x / s, the float32 quotient clamped
+// to +-448 first.
+// No division is issued for amax >= 2^-55 (s >= 2^-64); every step below was
+// checked against the divisions it replaces by enumerating all of its
+// inputs, which are bf16 (8 significant bits):
+//  - s: s0 = amax * RN(1/448), then one correction s0 + (amax - 448 s0) RN(1/448)
+//    (the remainder is exact in one fma): equals RN(amax / 448) for every amax;
+//  - y = RN(1/s): the hardware reciprocal (within 1 ulp) and one Newton step
+//    y0 + y0 (1 - s y0): exact from either float neighbour of 1/s;
+//  - x / s: q0 = x y, remainder r = x - q0 s (exact in one fma), q0 + r y
+//    (Markstein's correction step for a correctly rounded reciprocal): equals
+//    the correctly rounded quotient wherever |x / s| >= 2^-11 for every pair
+//    x <= amax; below that the e4m3fn code is 0 either way.
+// Smaller groups divide.  The e4m3fn rounding is the hardware conversion
+// (round to nearest even; a magnitude that rounds to zero may keep its sign,
+// which no product sees).
+__device__ __forceinline__ uint2 quant8_e4m3fn(const u32x4 xv, float amax, float& s) {
+  float q[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    q[2 * e] = __uint_as_float(xv[e] << 16);
+    q[2 * e + 1] = __uint_as_float(xv[e] & 0xFFFF0000u);
+  }
+  if (__builtin_expect(amax >= 0x1p-55f, 1)) {
+    constexpr float kInv448 = 1.0f / 448.0f;
+    const float s0 = amax * kInv448;
+    s = __builtin_fmaf(__builtin_fmaf(-s0, 448.0f, amax), kInv448, s0);
+    const float y0 = __builtin_amdgcn_rcpf(s);
+    const float y = __builtin_fmaf(__builtin_fmaf(-s, y0, 1.0f), y0, y0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float q0 = q[e] * y;
+      q[e] = __builtin_fmaf(__builtin_fmaf(-q0, s, q[e]), y, q0);
+    }
+  } else {
+    s = amax / 448.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = q[e] / s;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) q[e] = __builtin_amdgcn_fmed3f(q[e], -448.0f, 448.0f);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
+  return make_uint2((unsigned)lo, (unsigned)hi);
+}
 
 // W rows move as 128-byte row segments (8 rows per wave instruction, whole
 // cache lines) and pass through a per-wave LDS stage into the MFMA fragment
 // layout: the fragment layout itself would read 16 rows x 64 bytes per
 // instruction, and that load pattern is limited by the vector L1 (its address
 // stage stalls on the cache), not by HBM.
-constexpr int tlds_wstage_bytes(int op, int FN) { return op_groups(op) * FN * 16 * kWRowStride; }
-// LDS of a workgroup: the double-buffered x chunks (KW per round), reused
-// after the loop for the K-group partials, then one W stage per wave.
-constexpr int tlds_red_bytes(int op, int FM, int FN, int NW, int KW) {
-  return (KW - 1) * (NW / KW) * 64 * op_groups(op) * FN * FM * 4 * 4;
-}
-constexpr int tlds_lds_bytes(int op, int FM, int FN, int NW, int KW) {
-  const int xb = 2 * KW * 16 * FM * tlds_xrow_stride(op), rb = tlds_red_bytes(op, FM, FN, NW, KW);
-  return (xb > rb ? xb : rb) + NW * tlds_wstage_bytes(op, FN);
-}
-
 template <int OP, int FM, int FN, int S, int P, int NW, int KW>
 __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   constexpr int NT = 64 * NW;                     // threads of the workgroup
@@ -693,14 +744,15 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   using Round = LdsRound<OP, FM, FN, NW, KW>;
   constexpr int XPIECES = Round::XPIECES;
   constexpr int XPT = Round::XPT;
-  constexpr int XS = tlds_xrow_stride(OP);        // LDS x row stride
-  constexpr int PPR = tlds_xrow_bytes(OP) / 16;   // 16-byte x pieces per chunk row
-  constexpr int SUBB = 16 * FM * XS;              // bytes of one x chunk in LDS
+  constexpr bool QX = OP == OP_A8W8Q;             // x quantised here: bf16 in, fp8 codes + scales in LDS
+  constexpr int XS = tlds_xl_stride(OP);          // LDS x row stride
+  constexpr int PPR = tlds_xg_bytes(OP) / 16;     // 16-byte x pieces per chunk row (as loaded)
+  constexpr int SUBB = tlds_sub_bytes(OP, FM);    // bytes of one x chunk in LDS
   constexpr int BUFB = KW * SUBB;                 // bytes of one LDS x buffer (a round's KW chunks)
   constexpr int XBUF = 2 * BUFB > tlds_red_bytes(OP, FM, FN, NW, KW) ? 2 * BUFB : tlds_red_bytes(OP, FM, FN, NW, KW);
   constexpr int WSTB = tlds_wstage_bytes(OP, FN);  // bytes of one wave's W stage
 
-  extern __shared__ __align__(16) unsigned char xl[];   // [2][16*FM][stride] x, then [4][G*FN*16][stride] W
+  extern __shared__ __align__(16) unsigned char xl[];   // [2][KW][x chunk] x, then [NW][G*FN*16][stride] W
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -737,18 +789,20 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   // x pieces this thread copies into LDS: piece p -> the round's chunk
   // p / (16*FM*PPR), chunk row (p / PPR) % (16*FM) (x row m_base + that,
   // clamped to M-1), byte column 16*(p%PPR)
+  // (x quantised here: the 8 codes of a piece land at byte 8*(p%PPR) of the
+  // LDS row, and the 16 lanes of a row, lanes 16q..16q+15, share its scale)
   const char* xrowp[XPT];
-  int xcolb[XPT], xdst[XPT], xsub[XPT];
+  int xcolb[XPT], xdst[XPT], xsub[XPT], xrr[XPT];
   bool xmine[XPT];
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
     const int p = min((int)threadIdx.x + NT * i, XPIECES - 1);
     xmine[i] = (int)threadIdx.x + NT * i < XPIECES;
     xsub[i] = p / (16 * FM * PPR);
-    const int r = (p / PPR) % (16 * FM);
+    xrr[i] = (p / PPR) % (16 * FM);
     xcolb[i] = (p % PPR) * 16;
-    xrowp[i] = static_cast<const char*>(a.x) + (size_t)min(m_base + r, M - 1) * K * XB;
-    xdst[i] = xsub[i] * SUBB + r * XS + xcolb[i];
+    xrowp[i] = static_cast<const char*>(a.x) + (size_t)min(m_base + xrr[i], M - 1) * K * XB;
+    xdst[i] = xsub[i] * SUBB + xrr[i] * XS + (QX ? (p % PPR) * 8 : xcolb[i]);
   }
   int xm[FM];
 #pragma unroll
@@ -767,7 +821,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   auto chunk_of = [&](int c, int q) { return c_begin + c * KW + q; };
   auto wk = [&](int c, int h) {
     const int k0 = chunk_of(c, kw) * KCH;
-    if constexpr (OP == OP_A8W8) return k0 + h * 64 + lq * 16;
+    if constexpr (OP == OP_A8W8 || OP == OP_A8W8Q) return k0 + h * 64 + lq * 16;
     else if constexpr (OP == OP_FP8T) return k0 + lq * 32 + h * 16;
     else return k0 + h * 32 + lq * 8;
   };
@@ -790,6 +844,8 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
     if constexpr (OP == OP_A8W8) {
 #pragma unroll
       for (int j = 0; j < FM; ++j) b.sx[j] = a.s0[(size_t)xm[j] * kb + chunk];
+    }
+    if constexpr (OP == OP_A8W8 || OP == OP_A8W8Q) {
 #pragma unroll
       for (int f = 0; f < FN; ++f) b.sw[f] = a.s1[(size_t)wblk[f] * kb + chunk];
     }
@@ -810,9 +866,40 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   auto compute = [&](const Round& b0, int c, auto tail) {
     Round b = b0;
     unsigned char* buf = xl + (c & 1) * BUFB;
+    if constexpr (QX) {
+      // quantise each 16-byte piece (8 bf16): the row's scale is the maximum
+      // magnitude over its 16 lanes over 448 (bf16 magnitudes compare as
+      // their bit patterns).  Padded rows (past M) and all-zero groups get
+      // zero codes and the scale 1; a row's 16 lanes take the same branch.
 #pragma unroll
-    for (int i = 0; i < XPT; ++i)
-      if (XPIECES % NT == 0 || xmine[i]) *reinterpret_cast<u32x4*>(buf + xdst[i]) = b.x[i];
+      for (int i = 0; i < XPT; ++i) {
+        uint2 qv = make_uint2(0u, 0u);
+        float s = 1.0f;
+        if (m_base + xrr[i] < M) {
+          unsigned am = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            am = max(am, (b.x[i][e] << 16) & 0x7FFF0000u);
+            am = max(am, b.x[i][e] & 0x7FFF0000u);
+          }
+          am = row16_max(am);
+          if (am != 0u) qv = quant8_e4m3fn(b.x[i], __uint_as_float(am), s);
+        }
+        if (XPIECES % NT == 0 || xmine[i]) {
+          *reinterpret_cast<uint2*>(buf + xdst[i]) = qv;
+          if (xcolb[i] == 0) {
+            *reinterpret_cast<float*>(buf + xsub[i] * SUBB + 16 * FM * XS + xrr[i] * 4) = s;
+            // the first column of workgroups also hands the scales out
+            const int m = m_base + xrr[i], ck = chunk_of(c, xsub[i]);
+            if (a.xs_out && blockIdx.x == 0 && m < M && ck < c_end) a.xs_out[(size_t)m * kb + ck] = s;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < XPT; ++i)
+        if (XPIECES % NT == 0 || xmine[i]) *reinterpret_cast<u32x4*>(buf + xdst[i]) = b.x[i];
+    }
     __syncthreads();
     {
       // the wave's own W stage needs no barrier (a wave's LDS accesses run in
@@ -900,13 +987,16 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
             acc[0][f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[f], __builtin_bit_cast(bf16x8, B[u][j]),
                                                                    acc[0][f][j], 0, 0, 0);
       }
-    } else {  // OP_A8W8: the chunk is one 128-K scale group
+    } else {  // OP_A8W8 / OP_A8W8Q: the chunk is one 128-K scale group
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
         u32x4 B16[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           B16[h] = *reinterpret_cast<const u32x4*>(buf + kw * SUBB + (j * 16 + lr) * XS + h * 64 + lq * 16);
+        float sxj;
+        if constexpr (QX) sxj = *reinterpret_cast<const float*>(buf + kw * SUBB + 16 * FM * XS + (j * 16 + lr) * 4);
+        else sxj = b.sx[j];
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
           f32x4 t = f32x4{0, 0, 0, 0};
@@ -918,7 +1008,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
             const long Bv = static_cast<long>((static_cast<unsigned long>(B16[h][p + 1]) << 32) | B16[h][p]);
             t = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(A, Bv, t, 0, 0, 0);
           }
-          const float sc = b.sx[j] * b.sw[f];
+          const float sc = sxj * b.sw[f];
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[0][f][j][e] = __builtin_fmaf(t[e], sc, acc[0][f][j][e]);
         }
@@ -1122,7 +1212,7 @@ hipError_t launch_tlds(const Args& a, hipStream_t s) {
   constexpr int TW = 16 * FN * (NW / KW);
   const unsigned gx = (unsigned)((a.N + TW - 1) / TW);
   const unsigned gy = (unsigned)((a.M + 16 * FM - 1) / (16 * FM));
-  const size_t smem = (size_t)tlds_lds_bytes(OP, FM, FN, NW, KW);
+  const size_t smem = (size_t)tlds_smem(OP, FM, FN, NW, KW);
   hipLaunchKernelGGL((tlds_kernel<OP, FM, FN, S, P, NW, KW>), dim3(gx, gy, S), dim3(64 * NW), smem, s, a);
   return hipGetLastError();
 }
@@ -1175,14 +1265,17 @@ template <> const GemvRow* gemv_table<OP_BF16>();
 template <> const GemvRow* gemv_table<OP_GATED>();
 template <> const GemvRow* gemv_table<OP_FP8T>();
 template <> const GemvRow* gemv_table<OP_A8W8>();
+template <> const GemvRow* gemv_table<OP_A8W8Q>();
 template <> const TileRow* tile_table<OP_BF16>();
 template <> const TileRow* tile_table<OP_GATED>();
 template <> const TileRow* tile_table<OP_FP8T>();
 template <> const TileRow* tile_table<OP_A8W8>();
+template <> const TileRow* tile_table<OP_A8W8Q>();
 template <int OP> const TileRow* tlds_table();
 template <> const TileRow* tlds_table<OP_BF16>();
 template <> const TileRow* tlds_table<OP_GATED>();
 template <> const TileRow* tlds_table<OP_FP8T>();
 template <> const TileRow* tlds_table<OP_A8W8>();
+template <> const TileRow* tlds_table<OP_A8W8Q>();
 
 }  // namespace skg

@@ -195,6 +195,7 @@ const char* op_name(int op) {
     case OP_GATED: return "gated";
     case OP_FP8T: return "fp8_tensor";
     case OP_A8W8: return "a8w8_block";
+    case OP_A8W8Q: return "a8w8_quant";
     default: return nullptr;
   }
 }
@@ -313,6 +314,11 @@ int Table::load(const std::string& path, const Identity& self, std::string* err)
 // The untuned entry point: what runs with no table, and the incumbent a table
 // entry has to beat.  A shape rule fitted to gfx950 measurements of the whole
 // variant list over the decode shapes:
+//  * x quantised in the call (A8W8 from bf16 x): the LDS tile with one K group
+//    per workgroup (quantisation runs in every round of every workgroup) and
+//    K split S ways across workgroups: S = 8 up to 64 tiles of 64 weight
+//    rows, 4 up to 128, 2 up to 256, else 1; from the rows-32 bucket
+//    eight-wave workgroups at S = 4, else two fragments per wave at S = 2.
 //  * rows 1..3, rows 4 unless the weight is fp8, and rows up to 8 when the
 //    weight is under 16 MiB: the VALU weight stream.  Two weight rows per
 //    wave for one row of x, four for more, eight for a vocabulary-sized N
@@ -352,7 +358,8 @@ int default_pick(int op, int M, int N, int K, bool allow_ws) {
   const double rowb = (double)K * op_w_bytes(op);
   const double MiB = 1024.0 * 1024.0;
   const bool small_w = wbytes < 16 * MiB;
-  const bool gemv = b <= 3 || (b == 4 && op != OP_A8W8 && op != OP_FP8T) || (small_w && b <= 8);
+  const bool gemv = op != OP_A8W8Q &&   // (x quantised in the kernel: LDS tile family only)
+                    (b <= 3 || (b == 4 && op != OP_A8W8 && op != OP_FP8T) || (small_w && b <= 8));
   int v = -1;
   if (gemv) {
     if (rowb < 2048) v = first_supported(op, M, {"gemv_r4_k1_p2", "gemv_r4_k2_p2"});
@@ -360,6 +367,21 @@ int default_pick(int op, int M, int N, int K, bool allow_ws) {
     else if (N >= 65536) v = first_supported(op, M, {"gemv_r8_k4_p1", "gemv_r4_k4_p1", "gemv_r2_k4_p1"});
     else v = first_supported(op, M, {"gemv_r4_k4_p1", "gemv_r2_k4_p1", "gemv_r1_k4_p2"});
     if (v < 0) v = first_of_family(op, M, FAM_GEMV);
+  } else if (op == OP_A8W8Q) {
+    // x is quantised in every round, so K split over the waves of a workgroup
+    // multiplies the quantisation each round waits for: one K group per
+    // workgroup, and the chip filled through the cross-workgroup split
+    const double tiles = wrows / 64.0;
+    const int S = !allow_ws ? 1 : tiles <= 64 ? 8 : tiles <= 128 ? 4 : tiles <= 256 ? 2 : 1;
+    if (b <= 16)
+      v = S == 8 ? first_supported(op, M, {"tlds_f1_s8_p2", "tlds_f1_s8_p4_m2"})
+          : S == 4 ? first_supported(op, M, {"tlds_f1_s4_p2", "tlds_f1_s4_p4_m2"})
+          : S == 2 ? first_supported(op, M, {"tlds_f1_s2_p4_m2", "tlds_f1_s2_p4"})
+                   : first_supported(op, M, {"tlds_f1_s1_p4", "tlds_f1_s1_p4_m2"});
+    else
+      v = S >= 4 ? first_supported(op, M, {"tlds_w8_f1_s4_p4_m4", "tlds_f1_s4_p4_m2"})
+          : allow_ws ? first_supported(op, M, {"tlds_f2_s2_p2", "tlds_f1_s2_p4_m2"})
+                     : first_supported(op, M, {"tlds_f1_s1_p4_m2", "tlds_f1_s1_p4_m4"});
   } else if (small_w) {
     if (b <= 32 || wbytes <= 4 * MiB) v = first_supported(op, M, {"tlds_k4_f1_s1_p4_m1", "tlds_k4_f1_s1_p4_m2"});
     else if (b <= 64) v = first_supported(op, M, {"tlds_k4_f1_s1_p4_m2", "tlds_k4_f1_s1_p4_m1"});

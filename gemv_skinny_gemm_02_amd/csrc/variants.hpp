@@ -6,11 +6,13 @@
 
 namespace skg {
 
-enum Op : int { OP_BF16 = 0, OP_GATED = 1, OP_FP8T = 2, OP_A8W8 = 3, NUM_OPS = 4 };
+// OP_A8W8Q: A8W8 block scale with bf16 x, quantised per row and 128-K group
+// inside the kernel (LDS tile path only).
+enum Op : int { OP_BF16 = 0, OP_GATED = 1, OP_FP8T = 2, OP_A8W8 = 3, OP_A8W8Q = 4, NUM_OPS = 5 };
 enum Family : int { FAM_GEMV = 0, FAM_TILE = 1, FAM_TLDS = 2 };
 
 // Rows buckets: M is rounded up to the next one (padded-M lookup with no
-// nearest fallback: DeepSeek-V4-flash decode round 3, "Retained change 2";
+// nearest fallback: Decode optimization round 3, "Retained change 2";
 // rows 3, 6 and 12 as in mstar PR #1102, "What changed").
 constexpr int kBuckets[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 64, 96, 128};
 constexpr int kNumBuckets = sizeof(kBuckets) / sizeof(kBuckets[0]);
@@ -42,7 +44,7 @@ constexpr int tile_fm_index(int M) {  // M rows in one launch row (<= 128)
 }
 
 constexpr int op_groups(int op) { return op == OP_GATED ? 2 : 1; }
-constexpr bool op_w_fp8(int op) { return op == OP_FP8T || op == OP_A8W8; }
+constexpr bool op_w_fp8(int op) { return op == OP_FP8T || op == OP_A8W8 || op == OP_A8W8Q; }
 constexpr bool op_x_fp8(int op) { return op == OP_A8W8; }
 constexpr int op_w_bytes(int op) { return op_w_fp8(op) ? 1 : 2; }
 constexpr int op_x_bytes(int op) { return op_x_fp8(op) ? 1 : 2; }
@@ -62,7 +64,7 @@ constexpr int gemv_regs(int op, int MT, int R, int P) {
 }
 constexpr bool gemv_valid(int op, int MT, int R, int KS, int P) {
   const int G = op_groups(op);
-  return (KS == 1 || KS == 2 || KS == 4) && P >= 1 && MT * R * G <= 64 &&
+  return op != OP_A8W8Q && (KS == 1 || KS == 2 || KS == 4) && P >= 1 && MT * R * G <= 64 &&
          gemv_regs(op, MT, R, P) <= kRegBudget && (128 % ((4 / KS) * R)) == 0;
 }
 constexpr int tile_red_bytes(int op, int FM, int FN, int KS) {
@@ -76,33 +78,49 @@ constexpr int tile_regs(int op, int FM, int FN, int P) {
 }
 constexpr bool tile_valid(int op, int FM, int FN, int KS, int P) {
   const int G = op_groups(op);
-  return (KS == 1 || KS == 2 || KS == 4) && P >= 1 && G * FN * FM * 4 <= 128 &&
+  return op != OP_A8W8Q && (KS == 1 || KS == 2 || KS == 4) && P >= 1 && G * FN * FM * 4 <= 128 &&
          tile_regs(op, FM, FN, P) <= kRegBudget && tile_red_bytes(op, FM, FN, KS) <= 65536 &&
          (128 % ((4 / KS) * FN * 16)) == 0;
 }
-// LDS-shared-x tile path (tlds): 64*FN W rows per workgroup, S-way split-K.
-constexpr int tlds_xpt(int op, int FM, int NW, int KW) {
-  const int ppr = op == OP_FP8T ? 16 : 8;   // 16-byte x pieces per chunk row
-  return (KW * 16 * FM * ppr + 64 * NW - 1) / (64 * NW);
+// LDS-shared-x tile path (tlds).  A chunk is 128 bytes of every W row (64 K
+// of bf16 weights, 128 K of fp8 weights); its x rows arrive as KCH*XB bytes
+// and sit in LDS as the same bytes, or, for OP_A8W8Q, as the 128 fp8 codes
+// followed (per chunk) by one float32 scale per row.
+constexpr int tlds_kch(int op) { return op_w_fp8(op) ? 128 : 64; }
+constexpr int tlds_xg_bytes(int op) { return tlds_kch(op) * op_x_bytes(op); }                  // x row in HBM
+constexpr int tlds_xl_bytes(int op) { return op == OP_A8W8Q ? tlds_kch(op) : tlds_xg_bytes(op); }  // x row in LDS
+constexpr int tlds_xl_stride(int op) { return tlds_xl_bytes(op) + 16; }   // rows start 4 banks apart
+constexpr int tlds_sub_bytes(int op, int FM) {                            // one chunk of x in LDS
+  return 16 * FM * tlds_xl_stride(op) + (op == OP_A8W8Q ? 16 * FM * 4 : 0);
+}
+constexpr int kWRowStride = 144;   // W stage rows: 128 bytes + 16 of padding
+constexpr int tlds_wstage_bytes(int op, int FN) { return op_groups(op) * FN * 16 * kWRowStride; }
+constexpr int tlds_red_bytes(int op, int FM, int FN, int NW, int KW) {   // K-group partials after the loop
+  return (KW - 1) * (NW / KW) * 64 * op_groups(op) * FN * FM * 4 * 4;
+}
+// LDS bytes of a workgroup: the double-buffered x chunks (KW per round),
+// reused after the loop for the K-group partials, then one W stage per wave.
+constexpr int tlds_smem(int op, int FM, int FN, int NW, int KW) {
+  const int xb = 2 * KW * tlds_sub_bytes(op, FM), rb = tlds_red_bytes(op, FM, FN, NW, KW);
+  return (xb > rb ? xb : rb) + NW * tlds_wstage_bytes(op, FN);
+}
+constexpr int tlds_xpt(int op, int FM, int NW, int KW) {   // 16-byte x pieces per thread per round
+  return (KW * 16 * FM * (tlds_xg_bytes(op) / 16) + 64 * NW - 1) / (64 * NW);
 }
 constexpr int tlds_regs(int op, int FM, int FN, int P, int NW, int KW) {
   const int G = op_groups(op);
-  const int per_chunk = G * FN * 2 * 4 + tlds_xpt(op, FM, NW, KW) * 4 + (op == OP_A8W8 ? FM + FN : 0);
+  const bool a8 = op == OP_A8W8 || op == OP_A8W8Q;
+  const int per_chunk = G * FN * 2 * 4 + tlds_xpt(op, FM, NW, KW) * 4 + (op == OP_A8W8 ? FM + FN : (a8 ? FN : 0));
   const int acc = G * FN * FM * 4;
-  const int xfrag = op == OP_FP8T ? 16 * FM : (op == OP_BF16 || op == OP_GATED ? 8 * FM : 0);   // a chunk's x fragments
-  return P * per_chunk + acc * (op == OP_A8W8 ? 2 : 1) + FM * 4 + xfrag;
-}
-// LDS bytes a tlds workgroup takes (x chunks or K-group partials, W stages).
-constexpr int tlds_smem(int op, int FM, int FN, int NW, int KW) {
-  const int xs = (op_w_fp8(op) ? 128 : 64) * op_x_bytes(op) + 16;
-  const int xb = 2 * KW * 16 * FM * xs;
-  const int rb = (KW - 1) * (NW / KW) * 64 * op_groups(op) * FN * FM * 16;
-  return (xb > rb ? xb : rb) + NW * op_groups(op) * FN * 16 * 144;
+  const int xfrag = op == OP_FP8T ? 16 * FM : (op == OP_BF16 || op == OP_GATED ? 8 * FM : (a8 ? 8 : 0));
+  const int quant = op == OP_A8W8Q ? 8 * tlds_xpt(op, FM, NW, KW) : 0;   // decoded x of the pieces being quantised
+  return P * per_chunk + acc * (a8 ? 2 : 1) + FM * 4 + xfrag + quant;
 }
 constexpr bool tlds_valid(int op, int FM, int FN, int S, int P, int NW, int KW) {
   const int G = op_groups(op);
   return (S == 1 || S == 2 || S == 4 || S == 8) && (NW == 4 || NW == 8) && (KW == 1 || KW == 2 || KW == 4 || KW == 8) &&
-         NW % KW == 0 && P >= 1 && G * FN * FM * 4 <= 128 && tlds_regs(op, FM, FN, P, NW, KW) <= 224 &&
+         NW % KW == 0 && P >= 1 && G * FN * FM * 4 <= 128 &&
+         tlds_regs(op, FM, FN, P, NW, KW) <= (op == OP_A8W8Q && NW == 8 ? 160 : 224) &&
          tlds_smem(op, FM, FN, NW, KW) <= 64 * 1024 && (128 % (64 * FN)) == 0;
 }
 // Bytes of split-K partials a tlds launch with S > 1 needs, and the number of

@@ -17,7 +17,7 @@ checkpoint.
 is the incumbent; a different variant is chosen only when its time is at least
 2 % below the default's (mstar PR #1104, "What changed": a size leaves what
 the tree serves only for a 2 % gain; every candidate is re-measured against
-the incumbent's real entry point: DeepSeek-V4-flash decode round 3, "Rejected
+the incumbent's real entry point: Decode optimization round 3, "Rejected
 paths", and Strata PR #1297, item 4, the true-default baseline).  The table
 keeps every candidate's time beside the choice, so moving a size is a one-word
 edit.
@@ -58,6 +58,8 @@ def workload_keys(ops):
         keys += [("fp8_tensor", M, N, K) for M in synth.HEAD_M]
     if "a8w8_block" in ops:
         keys += [("a8w8_block", M, N, K) for (N, K) in synth.A8W8_NK for M in synth.A8W8_M]
+    if "a8w8_quant" in ops:
+        keys += [("a8w8_quant", M, N, K) for (N, K) in synth.A8W8_NK for M in synth.A8W8_M]
     return keys
 
 
@@ -76,6 +78,8 @@ def alg_bytes(op, M, N, K):
     if op == "fp8_tensor":
         return N * K + 2 * M * K + 2 * M * N + 4
     kb, nb = -(-K // 128), -(-N // 128)
+    if op == "a8w8_quant":                       # bf16 x in, no x scales read
+        return N * K + 2 * M * K + 4 * nb * kb + 2 * M * N
     return N * K + M * K + 4 * M * kb + 4 * nb * kb + 2 * M * N
 
 
@@ -122,7 +126,7 @@ def tune(store, ops, quick=False, rotation_gib=1.0, replays=5, only_m=None):
         keys = [k for k in keys if k[1] in only_m]
     stream = torch.cuda.current_stream()
     make = {"bf16": synth.make_bf16, "gated": synth.make_gated, "fp8_tensor": synth.make_fp8_tensor,
-            "a8w8_block": synth.make_a8w8_block}
+            "a8w8_block": synth.make_a8w8_block, "a8w8_quant": synth.make_a8w8_quant}
     cache = {}
     with open(store, "a") as fout:
         for (op, M, N, K) in keys:
@@ -141,7 +145,7 @@ def tune(store, ops, quick=False, rotation_gib=1.0, replays=5, only_m=None):
                     x = torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).cuda()
                     w0 = torch.from_numpy(p.w.view(np.int16)).view(torch.bfloat16).cuda()
                 else:
-                    x = (torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16) if op == "fp8_tensor"
+                    x = (torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16) if op in ("fp8_tensor", "a8w8_quant")
                          else torch.from_numpy(p.x).view(torch.float8_e4m3fn)).cuda()
                     w0 = torch.from_numpy(p.w).view(torch.float8_e4m3fn).cuda()
                 s0 = torch.from_numpy(p.s0).cuda() if p.s0 is not None else None
@@ -213,7 +217,7 @@ def promote(store, out, identity=None):
         if prev is None or r["M"] > prev["M"] or (r["M"] == prev["M"] and r["time"] > prev["time"]):
             slot[r["variant"]] = r
     entries = []
-    order = {"bf16": 0, "gated": 1, "fp8_tensor": 2, "a8w8_block": 3}
+    order = {"bf16": 0, "gated": 1, "fp8_tensor": 2, "a8w8_block": 3, "a8w8_quant": 4}
     for k in sorted(by_key, key=lambda k: (order[k[0]], k[2], k[3], k[1])):
         slot = by_key[k]
         default = next(iter(slot.values()))["default"]
@@ -246,7 +250,7 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="mode", required=True)
     t = sub.add_parser("tune")
     t.add_argument("--store", required=True)
-    t.add_argument("--ops", default="bf16,gated,fp8_tensor,a8w8_block")
+    t.add_argument("--ops", default="bf16,gated,fp8_tensor,a8w8_block,a8w8_quant")
     t.add_argument("--quick", action="store_true")
     t.add_argument("--rotation-gib", type=float, default=1.0)
     t.add_argument("--only-m", default="")

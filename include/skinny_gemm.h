@@ -5,7 +5,8 @@
  *
  *     y[M, N] = x[M, K] . W[N, K]^T        (M = 1..128 rows, large N and K)
  *
- * in the four forms that the decode-linear pages route and tune:
+ * in the four forms that the decode-linear pages route and tune, and a fifth
+ * that folds the A8W8 activation quantisation into the call:
  *
  *   skinny_gemm_bf16        bf16 x, bf16 W                     (mstar PR #1104,
  *                           "Why": decode linears served by skinny GEMM / GEMV)
@@ -15,8 +16,12 @@
  *   skinny_gemm_fp8_tensor  bf16 x, fp8 W with one scale for the whole weight
  *                           (mstar PR #1102, "What changed": the fp8 draft head)
  *   skinny_gemm_a8w8_block  fp8 x with one scale per row per 128 K-columns, fp8
- *                           W with one scale per 128 x 128 block (DeepSeek-V4-
- *                           flash decode round 3, "Retained change 2")
+ *                           W with one scale per 128 x 128 block (Decode
+ *                           optimization round 3, "Retained change 2")
+ *   skinny_gemm_a8w8_block_quant
+ *                           the same with bf16 x, quantised inside the call
+ *                           (the same page leaves that fusion open in
+ *                           "Rejected paths")
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -40,7 +45,7 @@
  *           fault inside a kernel surfaces at the caller's next synchronisation.
  * Dispatch. Each call rounds M up to its rows bucket {1,2,3,4,6,8,12,16,24,32,
  *           64,96,128} and looks (op, bucket, N, K) up in the per-device table
- *           (DeepSeek-V4-flash decode round 3, "Retained change 2": padded-M
+ *           (Decode optimization round 3, "Retained change 2": padded-M
  *           lookup with no nearest fallback; mstar PR #1104, "What changed": one
  *           per-device table).  A miss, an absent table or a refused table uses
  *           the built-in default for the op and bucket.  M above 128 uses the
@@ -77,6 +82,7 @@ typedef int skg_status;
 #define SKG_OP_GATED 1
 #define SKG_OP_FP8_TENSOR 2
 #define SKG_OP_A8W8_BLOCK 3
+#define SKG_OP_A8W8_QUANT 4
 
 /* y[M,N] = x[M,K] . W[N,K]^T.  x, W: bf16.  scales: unused, may be NULL. */
 skg_status skinny_gemm_bf16(const void* x, const void* W, const float* scales,
@@ -101,6 +107,24 @@ skg_status skinny_gemm_fp8_tensor(const void* x, const void* W, const float* sca
 skg_status skinny_gemm_a8w8_block(const void* x, const void* W, const float* x_scales,
                                   const float* w_scales, void* y, int M, int N, int K,
                                   hipStream_t stream);
+
+/* A8W8 block scale with bf16 activations quantised inside the call.
+ * x: bf16 [M, K], finite.  For every row m and 128-K group g (the last group
+ * may be shorter) the call takes
+ *     s[m, g] = max |x[m, k]| over the group / 448, one float32 division
+ *               (1 when that maximum is 0), and
+ *     q[m, k] = e4m3fn code of x[m, k] / s[m, g] (one float32 division),
+ *               clamped to +-448 and rounded once to nearest even,
+ * then computes the A8W8 product above with x_scales = s and x = q.
+ * W: e4m3fn [N, K]; w_scales: float32 [ceil(N/128), ceil(K/128)].
+ * x_scales_out: NULL, or device float32 [M, ceil(K/128)] that receives s (it
+ * must not overlap the other arguments).  Served by the MFMA tile kernels
+ * only.  (Decode optimization round 3: the activation quantisation runs as
+ * its own kernels in "Profiling: why M=1-8 decode is dispatch-bound", and
+ * "Rejected paths" leaves folding it into the GEMM open.) */
+skg_status skinny_gemm_a8w8_block_quant(const void* x, const void* W, const float* w_scales,
+                                        float* x_scales_out, void* y, int M, int N, int K,
+                                        hipStream_t stream);
 
 /* Text of the calling thread's last non-OK status ("" if none). */
 const char* skinny_gemm_last_error(void);
@@ -143,6 +167,7 @@ int skinny_gemm_variant_supports(int op, int variant, int M);
 
 /* Run one named variant, bypassing the table (tuner and tests).  s0/s1 are the
  * op's scale arrays (fp8_tensor: s0 = w_scale; a8w8: s0 = x_scales,
+ * s1 = w_scales; a8w8_quant: s0 = x_scales_out (written, may be NULL),
  * s1 = w_scales; others NULL).  knobs: reserved, pass NULL. */
 skg_status skinny_gemm_run_variant(int op, int variant, const int* knobs,
                                    const void* x, const void* W, const float* s0,

@@ -17,7 +17,7 @@ them:
   changed");
 * an fp8 weight with one scale for the whole tensor (the fp8 draft head --
   mstar PR #1102, "What changed", draft_head: fp8 bullet);
-* A8W8 with block scales (DeepSeek-V4-flash decode round 3, "Retained change
+* A8W8 with block scales (Decode optimization round 3, "Retained change
   2: decode-M rows for the A8W8 bpreshuffle table"), and the same with the
   activation quantisation folded in (``quant.py``; the same page leaves that
   fusion as open work in "Rejected paths").

@@ -5,7 +5,7 @@ The bar: max |y - y_ref| <= 2^-7 * max |y_ref|, relative Frobenius error
 ||y - y_ref|| / ||y_ref|| <= 5e-3, no NaN or Inf; when y_ref is all zero, y must
 be exactly zero.  Several summation orders are equally correct (the pages
 record different vendor reduction orders differing at a relative L2 of up to
-6e-5 -- DeepSeek-V4-flash decode round 3, "Rejected paths", TunableOp bullet),
+6e-5 -- Decode optimization round 3, "Rejected paths", TunableOp bullet),
 so the bar is a tolerance, not bit equality.  Rounding the exact result once to
 bf16 already costs up to 2^-9 relative per element, a quarter of the max-abs
 budget.

@@ -84,7 +84,7 @@ def dequant_a8w8(xq, xs, wq, ws, cols=None):
 
 
 def linear_a8w8_block(xq, xs, wq, ws, cols=None) -> np.ndarray:
-    """A8W8 block-scale linear (DeepSeek-V4-flash decode round 3, "Retained
+    """A8W8 block-scale linear (Decode optimization round 3, "Retained
     change 2"): fp8 activations with one fp32 scale per row per 128 K-columns,
     fp8 weights with one fp32 scale per 128 x 128 block; y = x~ . W~^T over the
     dequantised operands (see ``dequant_a8w8``)."""

@@ -20,13 +20,15 @@ its 248k x 4096 vocabulary head, DeepSeek-V4-flash's A8W8 block-scale layers):
   scale's block (whole tensor; 1 x 128 groups of a row of x; 128 x 128 blocks
   of W), computed in float32, 1.0 when the block is all zero; the stored byte is
   RNE(clamp(v / scale, -448, 448)) via torch's CPU float8_e4m3fn cast.
+* the A8W8 form with x quantised inside the call takes x as bf16 (as above)
+  and W with its block scales as the A8W8 form does.
 """
 from .gen import (CHUNK, normal_f32, bf16_bits, e4m3fn_bytes, make_bf16,
-                  make_gated, make_fp8_tensor, make_a8w8_block, BLOCK,
+                  make_gated, make_fp8_tensor, make_a8w8_block, make_a8w8_quant, BLOCK,
                   rows_of, SWEEP_M, SWEEP_NK, GATED_M, GATED_NK, HEAD_M,
                   HEAD_NK, A8W8_M, A8W8_NK, CONFIG1)
 
 __all__ = ["CHUNK", "normal_f32", "bf16_bits", "e4m3fn_bytes", "make_bf16",
-           "make_gated", "make_fp8_tensor", "make_a8w8_block", "BLOCK",
+           "make_gated", "make_fp8_tensor", "make_a8w8_block", "make_a8w8_quant", "BLOCK",
            "rows_of", "SWEEP_M", "SWEEP_NK", "GATED_M", "GATED_NK", "HEAD_M",
            "HEAD_NK", "A8W8_M", "A8W8_NK", "CONFIG1"]

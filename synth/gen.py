@@ -88,7 +88,7 @@ class Problem:
     x: np.ndarray
     w: np.ndarray
     s0: np.ndarray | None = None       # fp8 tensor: w_scale[1]; a8w8: xs[M, K/128]
-    s1: np.ndarray | None = None       # a8w8: ws[N/128, K/128]
+    s1: np.ndarray | None = None       # a8w8 (both forms): ws[N/128, K/128]
     meta: dict = field(default_factory=dict)
 
 
@@ -158,6 +158,15 @@ def make_a8w8_block(M: int, N: int, K: int, seed: int = 0) -> Problem:
     xq, xs = _group_quant_rows(xf, BLOCK)
     wq, ws = _block_quant(wf, BLOCK, BLOCK)
     return Problem("a8w8_block", M, N, K, xq, wq, s0=xs, s1=ws)
+
+
+def make_a8w8_quant(M: int, N: int, K: int, seed: int = 0) -> Problem:
+    """A8W8 block scale with bf16 x (the call quantises it): x as make_bf16's,
+    W and its 128x128 block scales as make_a8w8_block's."""
+    x = bf16_bits(normal_f32(seed, TID_X, (M, K), 1.0))
+    wf = normal_f32(seed, TID_W, (N, K), 0.02)
+    wq, ws = _block_quant(wf, BLOCK, BLOCK)
+    return Problem("a8w8_quant", M, N, K, x, wq, s0=None, s1=ws)
 
 
 def rows_of(n_total: int, count: int, seed: int = 0) -> np.ndarray:

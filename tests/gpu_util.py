@@ -38,6 +38,9 @@ def to_device(p):
         return dev_bf16(p.x), dev_bf16(p.w), None, None
     if p.kind == "fp8_tensor":
         return dev_bf16(p.x), dev_fp8(p.w), dev_f32(p.s0), None
+    if p.kind == "a8w8_quant":       # s0: the x scales the call writes
+        kb = -(-p.K // 128)
+        return dev_bf16(p.x), dev_fp8(p.w), torch.full((p.M, kb), -1.0, device="cuda"), dev_f32(p.s1)
     return dev_fp8(p.x), dev_fp8(p.w), dev_f32(p.s0), dev_f32(p.s1)
 
 
@@ -52,6 +55,8 @@ def run(p, dev=None, variant=None, y=None):
         return skg.skinny_gemm_gated(x, w, y=y)
     if p.kind == "fp8_tensor":
         return skg.skinny_gemm_fp8_tensor(x, w, s0, y=y)
+    if p.kind == "a8w8_quant":
+        return skg.skinny_gemm_a8w8_block_quant(x, w, s1, x_scales=s0, y=y)
     return skg.skinny_gemm_a8w8_block(x, w, s0, s1, y=y)
 
 
@@ -62,6 +67,8 @@ def reference(p, cols=None) -> np.ndarray:
         return oracle.linear_gated(p.x, p.w, cols=cols)
     if p.kind == "fp8_tensor":
         return oracle.linear_fp8_tensor(p.x, p.w, p.s0, cols=cols)
+    if p.kind == "a8w8_quant":
+        return oracle.linear_a8w8_quant(p.x, p.w, p.s1, cols=cols)[0]
     return oracle.linear_a8w8_block(p.x, p.s0, p.w, p.s1, cols=cols)
 
 

@@ -7,6 +7,7 @@ import pytest
 import torch
 
 import gemv_skinny_gemm_02_amd as skg
+import oracle
 import synth
 from gpu_util import assert_parity, dev_bf16, dev_f32, dev_fp8, host_bits, reference, run, say, to_device
 
@@ -101,6 +102,43 @@ def test_status_codes():
     st, _ = _raw("skinny_gemm_run_variant", 1, names.index("gemv_r4_k4_p1"), None, xw.data_ptr(), w.data_ptr(),
                  None, None, yw.data_ptr(), 16, 8, 64, s)
     assert st == 2
+
+
+def test_quant_status_codes_and_scale_guards():
+    """The entry point that quantises x: its x-scale output is refused when it
+    overlaps an operand, and the call when its w scales are missing; K = 0
+    writes zeros and no scale; the scales it writes stay inside their
+    [M, ceil(K/128)] buffer."""
+    M, N, K = 17, 77, 272                                   # 3 groups, the last of 16
+    p = synth.make_a8w8_quant(M, N, K, seed=4)
+    x, w, _, ws = to_device(p)
+    y = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    kb = 3
+    s = _stream()
+    buf = torch.full((M * kb + 1024,), -7.0, dtype=torch.float32, device="cuda")
+    xs = buf[:M * kb]
+    fn = "skinny_gemm_a8w8_block_quant"
+    st, msg = _raw(fn, x.data_ptr(), w.data_ptr(), ws.data_ptr(), y.data_ptr(), y.data_ptr(), M, N, K, s)
+    assert st == 1 and "overlap" in msg, msg
+    st, msg = _raw(fn, x.data_ptr(), w.data_ptr(), ws.data_ptr(), x.data_ptr(), y.data_ptr(), M, N, K, s)
+    assert st == 1 and "overlap" in msg, msg
+    st, msg = _raw(fn, x.data_ptr(), w.data_ptr(), None, xs.data_ptr(), y.data_ptr(), M, N, K, s)
+    assert st == 1, msg
+    # K = 0: y = 0 and nothing written to the scales
+    y.fill_(5.0)
+    st, msg = _raw(fn, x.data_ptr(), w.data_ptr(), ws.data_ptr(), xs.data_ptr(), y.data_ptr(), M, N, 0, s)
+    assert st == 0, msg
+    torch.cuda.synchronize()
+    assert torch.all(y == 0) and torch.all(buf == -7.0)
+    # a real call: scales exact, nothing written past them, y at the parity bar
+    yb = torch.full((M * N + 4096,), 12345, dtype=torch.int16, device="cuda")
+    y2 = yb[:M * N].view(torch.bfloat16).view(M, N)
+    skg.skinny_gemm_a8w8_block_quant(x, w, ws, x_scales=xs.view(M, kb), y=y2)
+    torch.cuda.synchronize()
+    assert torch.all(buf[M * kb:] == -7.0) and torch.all(yb[M * N:] == 12345)
+    ref, _, want = oracle.linear_a8w8_quant(p.x, p.w, p.s1)
+    assert np.array_equal(xs.cpu().numpy().reshape(M, kb).view(np.uint32), want.view(np.uint32))
+    assert_parity(host_bits(y2), ref, "a8w8_quant guards")
 
 
 def test_short_allocation_refused():

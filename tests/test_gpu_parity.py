@@ -17,12 +17,13 @@ from gpu_util import assert_parity, dev_bf16, dev_f32, dev_fp8, host_bits, refer
 pytestmark = pytest.mark.gpu
 
 MAKE = {"bf16": synth.make_bf16, "gated": synth.make_gated,
-        "fp8_tensor": synth.make_fp8_tensor, "a8w8_block": synth.make_a8w8_block}
+        "fp8_tensor": synth.make_fp8_tensor, "a8w8_block": synth.make_a8w8_block,
+        "a8w8_quant": synth.make_a8w8_quant}
 
 
 def _small_shape(kind):
     # N and K ragged against every workgroup row count and K round; K % 16 == 0
-    return (257, 1040) if kind in ("fp8_tensor", "a8w8_block") else (257, 1032)
+    return (257, 1040) if kind in ("fp8_tensor", "a8w8_block", "a8w8_quant") else (257, 1032)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -108,6 +109,75 @@ def test_a8w8_full_shapes():
             y = run(p)
             torch.cuda.synchronize()
             _sampled(p, y)
+
+
+def test_a8w8_quant_full_shapes():
+    """A8W8 with x quantised in the call, at the A8W8 shapes; the x scales it
+    hands out equal the oracle's bit for bit."""
+    for (N, K) in synth.A8W8_NK:
+        for M in synth.A8W8_M:
+            p = synth.make_a8w8_quant(M, N, K, seed=0)
+            say(f"a8w8_quant M={M} N={N} K={K} -> {skg.skinny_gemm_query('a8w8_quant', M, N, K)}")
+            x, w, xs, ws = to_device(p)
+            y = skg.skinny_gemm_a8w8_block_quant(x, w, ws, x_scales=xs)
+            torch.cuda.synchronize()
+            _sampled(p, y)
+            _, want = oracle.quantize_a8w8_x(p.x)
+            assert np.array_equal(xs.cpu().numpy().view(np.uint32), want.view(np.uint32)), f"x scales M={M}"
+
+
+def test_a8w8_quant_codes_exact():
+    """The codes the call quantises x to, read back through W = identity and
+    unit weight scales (y[m, n] = s[m, n/128] * q[m, n]; neighbouring e4m3fn
+    values are at least 2^-4 apart relative, bf16 keeps 2^-8), equal the
+    oracle's codes bit for bit -- including exact ties at every e4m3fn
+    midpoint, the bf16 neighbours just below and just above every midpoint,
+    subnormal codes, saturation and all-zero groups."""
+    K = N = 384
+    pos = oracle.E4M3FN_TABLE[:0x7F]                          # 0 .. 448
+    mids = (pos[:-1] + pos[1:]) / 2                          # the 126 ties, as x / s
+    mb = oracle.bf16_rne_bits(mids).astype(np.int64)
+    up = oracle.dec_bf16((mb + 1).astype(np.uint16))         # next bf16 above each tie
+    dn = oracle.dec_bf16((mb - 1).astype(np.uint16))         # next bf16 below
+    r = np.random.default_rng(9)
+    rows = []
+    for j in (-3, 0, 5):
+        # each group holds 448 * 2^j, so its scale is exactly 2^j and x / s is
+        # exactly the tie, neighbour or grid value placed there
+        g0 = np.concatenate([[448.0], mids, [0.5]])
+        g1 = np.concatenate([[-448.0], -mids, [-1.0]])
+        g2 = np.concatenate([pos, [0.25]])
+        rows.append(np.concatenate([g0, g1, g2]) * 2.0 ** j)
+        g0 = np.concatenate([[448.0], up, [0.5]])
+        g1 = np.concatenate([[-448.0], -dn, [-1.0]])
+        g2 = np.concatenate([[448.0], dn, [0.25]])
+        rows.append(np.concatenate([g0, g1, g2]) * 2.0 ** j)
+    rows = np.array(rows)
+    xb_exact = oracle.bf16_rne_bits(rows)
+    assert np.array_equal(oracle.dec_bf16(xb_exact), rows)    # every value above is a bf16 value
+    z = r.standard_normal((2, 384)) * 30.0
+    z[0] = 0.0                                                # all-zero row: scale 1, codes 0
+    z[1, 128:256] = 0.0                                       # one all-zero group
+    xb = np.concatenate([xb_exact, oracle.bf16_rne_bits(z)])
+    codes, scales = oracle.quantize_a8w8_x(xb)
+    wq = np.zeros((N, K), np.uint8)
+    wq[np.arange(N), np.arange(K)] = 0x38                     # identity in e4m3fn
+    ws = np.ones((3, 3), np.float32)
+    M = xb.shape[0]
+    xs = torch.full((M, 3), -1.0, device="cuda")
+    for variant in [None] + [n for i, n in enumerate(skg.variants("a8w8_quant"))
+                             if skg.skinny_gemm_variant_supports("a8w8_quant", i, M)][:6]:
+        say(f"a8w8_quant codes variant={variant}")
+        if variant is None:
+            y = skg.skinny_gemm_a8w8_block_quant(dev_bf16(xb), dev_fp8(wq), dev_f32(ws), x_scales=xs)
+        else:
+            y = skg.skinny_gemm_run_variant("a8w8_quant", variant, dev_bf16(xb), dev_fp8(wq), xs, dev_f32(ws))
+        torch.cuda.synchronize()
+        s = xs.cpu().numpy()
+        assert np.array_equal(s.view(np.uint32), scales.view(np.uint32)), f"scales ({variant})"
+        yv = oracle.dec_bf16(host_bits(y)) / np.repeat(s.astype(np.float64), 128, axis=1)
+        back = oracle.e4m3fn_rne_bits(yv)                     # the nearest grid point to y / s
+        assert np.array_equal(back, codes), f"codes ({variant}): {np.argwhere(back != codes)[:5]}"
 
 
 def test_fp8_head_full_shape():
