@@ -4,8 +4,11 @@
 Workload: the bf16 decode-linear sweep -- M in {1,2,3,4,6,8,12,16,24,32,64,96,
 128} x (N, K) in {(4096,4096), (6144,4096), (4096,12288), (2048,2048),
 (1024,1024)}, x ~ N(0,1), W ~ N(0,0.02), seed 0.  One step is one pass of the
-whole path over that sweep: 65 calls of skinny_gemm_bf16 through the library's
-table dispatch.  Inputs are resident in HBM before timing starts.  Each shape
+whole path over that sweep: 65 calls of skinny_gemm_bf16_packed through the
+library's table dispatch, each weight packed once (skinny_gemm_pack_weight)
+before timing, as a deployment packs it at load.  The same step on row-major
+weights (skinny_gemm_bf16) is timed in the same run and reported beside the
+value.  Inputs are resident in HBM before timing starts.  Each shape
 cycles through enough copies of W (>= 1 GiB per shape) that every call streams
 its weight from HBM, not from the 256 MB Infinity Cache.  Steps are replayed
 from HIP graphs, eight steps per graph.  The dominant kernel's launches of
@@ -50,11 +53,12 @@ def kernel_symbol(variant: str, M: int, op: int = 0) -> str:
     """The kernel template instance a variant runs for M rows, as rocprofv3
     prints it.  Variant names are the family followed by one-letter fields:
     gemv_r<R>_k<KS>_p<P>, tile_f<FN>_k<KS>_p<P>, and
-    tlds[_w<NW>][_k<KW>]_f<FN>_s<S>_p<P>[_m<MC>] (NW waves, default 4, of
-    which KW split K inside the workgroup, default 1; at most MC 16-row
-    fragments per workgroup, default 8)."""
+    tlds[_d][_w<NW>][_k<KW>]_f<FN>_s<S>_p<P>[_m<MC>] (d: direct x; NW waves,
+    default 4, of which KW split K inside the workgroup, default 1; at most MC
+    16-row fragments per workgroup, default 8)."""
     parts = variant.split("_")
-    kv = {p[0]: int(p[1:]) for p in parts[1:]}
+    xd = 1 if "d" in parts[1:] else 0
+    kv = {p[0]: int(p[1:]) for p in parts[1:] if p != "d"}
     if parts[0] == "gemv":
         mt = next(b for b in (1, 2, 3, 4, 6, 8, 12, 16) if M <= b)
         return f"void skg::gemv_kernel<{op}, {mt}, {kv['r']}, {kv['k']}, {kv['p']}>(skg::Args)"
@@ -64,7 +68,7 @@ def kernel_symbol(variant: str, M: int, op: int = 0) -> str:
         return f"void skg::tile_kernel<{op}, {fm}, {kv['f']}, {kv['k']}, {kv['p']}>(skg::Args)"
     fm = min(fm, kv.get("m", 8))
     return (f"void skg::tlds_kernel<{op}, {fm}, {kv['f']}, {kv['s']}, {kv['p']}, {kv.get('w', 4)}, "
-            f"{kv.get('k', 1)}>(skg::Args)")
+            f"{kv.get('k', 1)}, {xd}>(skg::Args)")
 
 
 def lib_code_hash() -> str:
@@ -130,73 +134,12 @@ def cpu_baseline(calls, host, seconds: float):
                       f"{len(calls)} calls in step order), float64, {dt:.1f} s"}
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rotation-gib", type=float, default=1.0, help="bytes of W copies per shape")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--per-call-replays", type=int, default=5, help="graph replays per call shape")
-    ap.add_argument("--no-per-call", action="store_true",
-                    help="skip the per-call graph timings (profiling runs: keeps every dispatch of a kernel "
-                         "in the step's shape mix)")
-    ap.add_argument("--per-call-min", type=int, default=64, help="min launches per per-call graph")
-    args = ap.parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: the skinny linear is measured on one MI355X "
-              "(a multi-GPU run would shard N with no exchange; see the design notes)", file=sys.stderr)
-        return 2
-
-    import torch
-
-    import gemv_skinny_gemm_02_amd as skg
-    import synth
-
-    if not torch.cuda.is_available():
-        log("no GPU")
-        return 1
-    torch.cuda.set_device(0)
-    skg.load()
-    props = torch.cuda.get_device_properties(0)
-    dev_name = f"{props.gcnArchName.split(':')[0]} ({props.multi_processor_count} CUs)"
-    log("device", dev_name, "| identity", skg.skinny_gemm_identity())
-
-    shapes = list(synth.SWEEP_NK)
-    Ms = list(synth.SWEEP_M)
-    calls = [(M, N, K) for (N, K) in shapes for M in Ms]
-
-    # ---------------------------------------------------------- inputs
-    host, x_dev, w_dev, y_dev = {}, {}, {}, {}
-    free, _ = torch.cuda.mem_get_info()
-    need = sum(max(2, math.ceil(args.rotation_gib * 2**30 / (2 * N * K))) * 2 * N * K for N, K in shapes)
-    if need > 0.8 * free:
-        log(f"not enough device memory for the rotation copies ({need / 2**30:.1f} GiB needed)")
-        return 1
-    for (N, K) in shapes:
-        p = synth.make_bf16(max(Ms), N, K, seed=0)
-        host[(N, K)] = (p.x, p.w)
-        if K not in x_dev:
-            x_dev[K] = torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).cuda()
-        w0 = torch.from_numpy(p.w.view(np.int16)).view(torch.bfloat16).cuda()
-        R = max(2, math.ceil(args.rotation_gib * 2**30 / (2 * N * K)))
-        w_dev[(N, K)] = [w0] + [w0.clone() for _ in range(R - 1)]
-        for M in Ms:
-            y_dev[(M, N)] = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    torch.cuda.synchronize()
-    log("inputs resident:", {f"{N}x{K}": len(w_dev[(N, K)]) for N, K in shapes}, "copies")
-
-    stream = torch.cuda.current_stream()
-    choice = {c: skg.skinny_gemm_query("bf16", *c) for c in calls}
-    sym = {c: kernel_symbol(choice[c][0], c[0]) for c in calls}
-
-    def launch(c, copy):
-        M, N, K = c
-        ws = w_dev[(N, K)]
-        skg.skinny_gemm_bf16(x_dev[K][:M], ws[copy % len(ws)], y=y_dev[(M, N)])
-
+def measure_step(args, torch, skg, calls, Ms, stream, launch, op, step_bytes):
+    """Time args.steps steps of `calls` launched by `launch(call, copy)` (table
+    dispatch of form `op`): returns the step time, its rate and the dominant
+    kernel's live average launch time."""
+    choice = {c: skg.skinny_gemm_query(op, *c) for c in calls}
+    sym = {c: kernel_symbol(choice[c][0], c[0], skg.OPS[op]) for c in calls}
     for c in calls:                      # eager warm-up (and lazy table load)
         launch(c, 0)
     torch.cuda.synchronize()
@@ -273,12 +216,101 @@ def main() -> int:
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
     dom_us = sum(e0.elapsed_time(e1) for e0, e1 in pairs) * 1e3 / (args.steps * len(dom_calls))
-    step_bytes = sum(alg_bytes(*c) for c in calls)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    log(f"step {ms_step * 1e3:.1f} us ({wall / args.steps * 1e6:.1f} us wall), {value:.1f} GB/s, "
+    log(f"{op}: step {ms_step * 1e3:.1f} us ({wall / args.steps * 1e6:.1f} us wall), {value:.1f} GB/s, "
         f"dominant kernel {dom_us:.2f} us/launch")
 
     del g_rest, g_dom, g_rest_r, g_dom_r
+    return {"launch": launch, "choice": choice, "dominant": dominant, "dom_calls": dom_calls,
+            "rough_us": rough_us, "ms_step": ms_step, "dom_us": dom_us, "value": value}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotation-gib", type=float, default=1.0, help="bytes of W copies per shape")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--per-call-replays", type=int, default=5, help="graph replays per call shape")
+    ap.add_argument("--no-per-call", action="store_true",
+                    help="skip the per-call graph timings (profiling runs: keeps every dispatch of a kernel "
+                         "in the step's shape mix)")
+    ap.add_argument("--per-call-min", type=int, default=64, help="min launches per per-call graph")
+    ap.add_argument("--no-row-major", action="store_true",
+                    help="skip the row-major step (profiling runs of the packed layout)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the skinny linear is measured on one MI355X "
+              "(a multi-GPU run would shard N with no exchange; see the design notes)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import gemv_skinny_gemm_02_amd as skg
+    import synth
+
+    if not torch.cuda.is_available():
+        log("no GPU")
+        return 1
+    torch.cuda.set_device(0)
+    skg.load()
+    props = torch.cuda.get_device_properties(0)
+    dev_name = f"{props.gcnArchName.split(':')[0]} ({props.multi_processor_count} CUs)"
+    log("device", dev_name, "| identity", skg.skinny_gemm_identity())
+
+    shapes = list(synth.SWEEP_NK)
+    Ms = list(synth.SWEEP_M)
+    calls = [(M, N, K) for (N, K) in shapes for M in Ms]
+
+    # ---------------------------------------------------------- inputs
+    host, x_dev, w_dev, wp_dev, y_dev = {}, {}, {}, {}, {}
+    free, _ = torch.cuda.mem_get_info()
+    need = sum(max(2, math.ceil(args.rotation_gib * 2**30 / (2 * N * K))) * 2 * N * K for N, K in shapes)
+    need *= 1 if args.no_row_major else 2
+    if need > 0.8 * free:
+        log(f"not enough device memory for the rotation copies ({need / 2**30:.1f} GiB needed)")
+        return 1
+    for (N, K) in shapes:
+        p = synth.make_bf16(max(Ms), N, K, seed=0)
+        host[(N, K)] = (p.x, p.w)
+        if K not in x_dev:
+            x_dev[K] = torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).cuda()
+        w0 = torch.from_numpy(p.w.view(np.int16)).view(torch.bfloat16).cuda()
+        R = max(2, math.ceil(args.rotation_gib * 2**30 / (2 * N * K)))
+        wp_dev[(N, K)] = [skg.skinny_gemm_pack_weight("bf16", w0) for _ in range(R)]
+        w_dev[(N, K)] = [] if args.no_row_major else [w0] + [w0.clone() for _ in range(R - 1)]
+        for M in Ms:
+            y_dev[(M, N)] = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    log("inputs resident:", {f"{N}x{K}": len(wp_dev[(N, K)]) for N, K in shapes}, "copies per layout")
+
+    stream = torch.cuda.current_stream()
+    step_bytes = sum(alg_bytes(*c) for c in calls)
+
+    def launcher(packed):
+        def launch(c, copy):
+            M, N, K = c
+            if packed:
+                ws = wp_dev[(N, K)]
+                skg.skinny_gemm_bf16_packed(x_dev[K][:M], ws[copy % len(ws)], y=y_dev[(M, N)])
+            else:
+                ws = w_dev[(N, K)]
+                skg.skinny_gemm_bf16(x_dev[K][:M], ws[copy % len(ws)], y=y_dev[(M, N)])
+        return launch
+
+    st = measure_step(args, torch, skg, calls, Ms, stream, launcher(True), "bf16_packed", step_bytes)
+    row_major = None
+    if not args.no_row_major:
+        rm = measure_step(args, torch, skg, calls, Ms, stream, launcher(False), "bf16", step_bytes)
+        row_major = {"value": round(rm["value"], 1), "ms_per_step": round(rm["ms_step"], 4),
+                     "dominant_kernel": rm["dominant"], "avg_launch_us": round(rm["dom_us"], 3)}
+        w_dev.clear()           # free the row-major copies
+    launch, choice, dominant, dom_calls = st["launch"], st["choice"], st["dominant"], st["dom_calls"]
+    rough_us, ms_step, dom_us, value = st["rough_us"], st["ms_step"], st["dom_us"], st["value"]
+
     if args.no_per_call:
         per_call_us = dict(rough_us)
     else:
@@ -286,7 +318,7 @@ def main() -> int:
         per_call_us = {}
         for c in calls:
             M, N, K = c
-            R = len(w_dev[(N, K)])
+            R = len(wp_dev[(N, K)])
             n = max(args.per_call_min, 2 * R)
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
@@ -347,8 +379,11 @@ def main() -> int:
         "config": {"workload": "bf16 decode-linear sweep: M in {1,2,3,4,6,8,12,16,24,32,64,96,128} x (N,K) in "
                                "{(4096,4096),(6144,4096),(4096,12288),(2048,2048),(1024,1024)}, x~N(0,1), "
                                "W~N(0,0.02), seed 0, 65 calls per step, weights rotated past the Infinity Cache",
+                   "weight_layout": "fragment-packed (skinny_gemm_pack_weight once per weight copy, before "
+                                    "timing; the same bytes)",
                    "calls_per_step": len(calls), "alg_bytes_per_step": step_bytes, "device": dev_name,
                    "table": skg.skinny_gemm_table_status()[1]},
+        "row_major": row_major,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": round(traffic) if traffic is not None else None,

@@ -27,12 +27,17 @@ __all__ = [
     "SkinnyGemmError", "lib_path", "load", "OPS",
     "skinny_gemm_bf16", "skinny_gemm_gated", "skinny_gemm_fp8_tensor", "skinny_gemm_a8w8_block",
     "skinny_gemm_a8w8_block_quant",
+    "PackedWeight", "skinny_gemm_packed_weight_bytes", "skinny_gemm_pack_weight", "skinny_gemm_bf16_packed",
+    "skinny_gemm_gated_packed", "skinny_gemm_fp8_tensor_packed", "skinny_gemm_a8w8_block_packed",
+    "skinny_gemm_a8w8_block_quant_packed",
     "skinny_gemm_run_variant", "skinny_gemm_query", "skinny_gemm_load_table", "skinny_gemm_load_table_as",
     "skinny_gemm_identity", "skinny_gemm_table_status", "skinny_gemm_num_variants",
     "skinny_gemm_variant_name", "skinny_gemm_variant_supports", "variants", "default_table_path",
 ]
 
-OPS = {"bf16": 0, "gated": 1, "fp8_tensor": 2, "a8w8_block": 3, "a8w8_quant": 4}
+OPS = {"bf16": 0, "gated": 1, "fp8_tensor": 2, "a8w8_block": 3, "a8w8_quant": 4,
+       "bf16_packed": 5, "gated_packed": 6, "fp8_tensor_packed": 7, "a8w8_block_packed": 8, "a8w8_quant_packed": 9}
+PACKED = 5            # op id offset of the forms that take a fragment-packed weight
 _STATUS = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "ELAUNCH", 4: "ETABLE"}
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +82,18 @@ def load() -> ctypes.CDLL:
         lib.skinny_gemm_a8w8_block.restype = i
         lib.skinny_gemm_a8w8_block_quant.argtypes = [vp, vp, fp, fp, vp, i, i, i, vp]
         lib.skinny_gemm_a8w8_block_quant.restype = i
+        for name in ("skinny_gemm_bf16_packed", "skinny_gemm_gated_packed", "skinny_gemm_fp8_tensor_packed"):
+            f = getattr(lib, name)
+            f.argtypes = [vp, vp, fp, vp, i, i, i, vp]
+            f.restype = i
+        for name in ("skinny_gemm_a8w8_block_packed", "skinny_gemm_a8w8_block_quant_packed"):
+            f = getattr(lib, name)
+            f.argtypes = [vp, vp, fp, fp, vp, i, i, i, vp]
+            f.restype = i
+        lib.skinny_gemm_packed_weight_bytes.argtypes = [i, i, i]
+        lib.skinny_gemm_packed_weight_bytes.restype = ctypes.c_size_t
+        lib.skinny_gemm_pack_weight.argtypes = [i, vp, vp, i, i, vp]
+        lib.skinny_gemm_pack_weight.restype = i
         lib.skinny_gemm_last_error.argtypes = []
         lib.skinny_gemm_last_error.restype = ctypes.c_char_p
         lib.skinny_gemm_load_table.argtypes = [ctypes.c_char_p]
@@ -205,21 +222,131 @@ def skinny_gemm_a8w8_block_quant(x, W, w_scales, x_scales=None, y=None, stream=N
     return y
 
 
+# ------------------------------------------------------ packed weights
+_BASE_NAMES = ("bf16", "gated", "fp8_tensor", "a8w8_block", "a8w8_quant")
+
+
+class PackedWeight:
+    """A weight in the fragment-packed layout, as skinny_gemm_pack_weight writes
+    it for one form `op` (a row-major form name) and shape: N output rows (per
+    half for the gated form) and K columns.  `data` is the uint8 device tensor
+    that holds it."""
+
+    def __init__(self, data: torch.Tensor, op: str, N: int, K: int):
+        self.data, self.op, self.N, self.K = data, op, N, K
+
+    def __repr__(self) -> str:
+        return f"PackedWeight(op={self.op!r}, N={self.N}, K={self.K}, bytes={self.data.numel()})"
+
+
+def _base(op) -> int:
+    opi = OPS[op] if isinstance(op, str) else int(op)
+    return opi - PACKED if opi >= PACKED else opi
+
+
+def skinny_gemm_packed_weight_bytes(op, N: int, K: int) -> int:
+    """Bytes of the packed weight of form `op` at N rows (per half for gated), K columns."""
+    return int(load().skinny_gemm_packed_weight_bytes(_base(op), N, K))
+
+
+def skinny_gemm_pack_weight(op, W, stream=None) -> PackedWeight:
+    """Write the fragment-packed copy of the row-major weight W for form `op`
+    (W as that form's row-major entry point takes it) into a new device tensor."""
+    b = _base(op)
+    wd = _FP8 if b in (2, 3, 4) else _BF16
+    rows, K = W.shape
+    N = rows // 2 if b == 1 else rows
+    if b == 1 and rows % 2:
+        raise ValueError("gated W must have 2N rows")
+    data = torch.empty(max(skinny_gemm_packed_weight_bytes(b, N, K), 0), dtype=torch.uint8, device=W.device)
+    _check(load().skinny_gemm_pack_weight(b, _dev(W, "W", wd, 2), data.data_ptr() if data.numel() else 0, N, K,
+                                          _stream(stream)))
+    return PackedWeight(data, _BASE_NAMES[b], N, K)
+
+
+def _pk(x, Wp, op: str):
+    if not isinstance(Wp, PackedWeight):
+        raise TypeError("W_packed must be a PackedWeight from skinny_gemm_pack_weight")
+    if Wp.op != op:
+        raise ValueError(f"W_packed was packed for {Wp.op!r}, not {op!r}")
+    M, K = x.shape
+    if Wp.K != K:
+        raise ValueError(f"x is [{M}, {K}] but W_packed has K={Wp.K}")
+    return M, Wp.N, K, _dev(Wp.data, "W_packed", (torch.uint8,), 1)
+
+
+def skinny_gemm_bf16_packed(x, W_packed, scales=None, y=None, stream=None) -> torch.Tensor:
+    """skinny_gemm_bf16 with the weight packed by skinny_gemm_pack_weight("bf16", W)."""
+    M, N, K, wp = _pk(x, W_packed, "bf16")
+    y = _out(y, M, N, x)
+    _check(load().skinny_gemm_bf16_packed(_dev(x, "x", _BF16, 2), wp, None, _dev(y, "y", _BF16, 2), M, N, K,
+                                          _stream(stream)))
+    return y
+
+
+def skinny_gemm_gated_packed(x, W_packed, scales=None, y=None, stream=None) -> torch.Tensor:
+    """skinny_gemm_gated with the weight packed by skinny_gemm_pack_weight("gated", W)."""
+    M, N, K, wp = _pk(x, W_packed, "gated")
+    y = _out(y, M, N, x)
+    _check(load().skinny_gemm_gated_packed(_dev(x, "x", _BF16, 2), wp, None, _dev(y, "y", _BF16, 2), M, N, K,
+                                           _stream(stream)))
+    return y
+
+
+def skinny_gemm_fp8_tensor_packed(x, W_packed, scales, y=None, stream=None) -> torch.Tensor:
+    """skinny_gemm_fp8_tensor with the weight packed by skinny_gemm_pack_weight("fp8_tensor", W)."""
+    M, N, K, wp = _pk(x, W_packed, "fp8_tensor")
+    y = _out(y, M, N, x)
+    _check(load().skinny_gemm_fp8_tensor_packed(_dev(x, "x", _BF16, 2), wp,
+                                                _dev(scales, "scales", (torch.float32,), 1),
+                                                _dev(y, "y", _BF16, 2), M, N, K, _stream(stream)))
+    return y
+
+
+def skinny_gemm_a8w8_block_packed(x, W_packed, x_scales, w_scales, y=None, stream=None) -> torch.Tensor:
+    """skinny_gemm_a8w8_block with the weight packed by skinny_gemm_pack_weight("a8w8_block", W)."""
+    M, N, K, wp = _pk(x, W_packed, "a8w8_block")
+    y = _out(y, M, N, x)
+    _check(load().skinny_gemm_a8w8_block_packed(_dev(x, "x", _FP8, 2), wp,
+                                                _dev(x_scales, "x_scales", (torch.float32,), 2),
+                                                _dev(w_scales, "w_scales", (torch.float32,), 2),
+                                                _dev(y, "y", _BF16, 2), M, N, K, _stream(stream)))
+    return y
+
+
+def skinny_gemm_a8w8_block_quant_packed(x, W_packed, w_scales, x_scales=None, y=None, stream=None) -> torch.Tensor:
+    """skinny_gemm_a8w8_block_quant with the weight packed by skinny_gemm_pack_weight("a8w8_quant", W)."""
+    M, N, K, wp = _pk(x, W_packed, "a8w8_quant")
+    y = _out(y, M, N, x)
+    _check(load().skinny_gemm_a8w8_block_quant_packed(_dev(x, "x", _BF16, 2), wp,
+                                                      _dev(w_scales, "w_scales", (torch.float32,), 2),
+                                                      _dev(x_scales, "x_scales", (torch.float32,), 2)
+                                                      if x_scales is not None else None,
+                                                      _dev(y, "y", _BF16, 2), M, N, K, _stream(stream)))
+    return y
+
+
 def skinny_gemm_run_variant(op, variant, x, W, s0=None, s1=None, y=None, stream=None) -> torch.Tensor:
-    """Run one named (or numbered) variant of an op, bypassing the table."""
+    """Run one named (or numbered) variant of an op, bypassing the table.  For a
+    packed op W is the PackedWeight of its row-major form."""
     opi = OPS[op] if isinstance(op, str) else int(op)
     if isinstance(variant, str):
         names = variants(opi)
         if variant not in names:
             raise ValueError(f"unknown variant {variant!r}")
         variant = names.index(variant)
-    xd = _FP8 if opi == 3 else _BF16
-    wd = _FP8 if opi in (2, 3, 4) else _BF16
-    M, N, K = _mk(x, W, 2 if opi == 1 else 1)
+    b = _base(opi)
+    xd = _FP8 if b == 3 else _BF16
+    wd = _FP8 if b in (2, 3, 4) else _BF16
+    if opi >= PACKED:
+        M, N, K, wp = _pk(x, W, _BASE_NAMES[b])
+    else:
+        M, N, K = _mk(x, W, 2 if b == 1 else 1)
+        wp = _dev(W, "W", wd, 2)
     y = _out(y, M, N, x)
     p0 = _dev(s0, "s0", (torch.float32,), s0.dim()) if s0 is not None else None
     p1 = _dev(s1, "s1", (torch.float32,), s1.dim()) if s1 is not None else None
-    _check(load().skinny_gemm_run_variant(opi, int(variant), None, _dev(x, "x", xd, 2), _dev(W, "W", wd, 2),
+    _check(load().skinny_gemm_run_variant(opi, int(variant), None, _dev(x, "x", xd, 2), wp,
                                           p0, p1, _dev(y, "y", _BF16, 2), M, N, K, _stream(stream)))
     return y
 

@@ -181,21 +181,22 @@ skg_status validate(int op, const Args& a) {
   if (a.M == 0 || a.N == 0) return SKG_OK;
   const int km = op_k_multiple(op);
   if (a.K % km) return fail(SKG_EUNSUPPORTED, "%s needs K %% %d == 0 (K=%d)", op_name(op), km, a.K);
+  const int base = op_base(op);
   const size_t M = a.M, N = a.N, K = a.K;
   const size_t G = op_groups(op);
   const size_t kb = (K + 127) / 128, nb = (N + 127) / 128;
   Buf bx{a.x, M * K * op_x_bytes(op), "x"};
-  Buf bw{a.w, G * N * K * op_w_bytes(op), "W"};
+  Buf bw{a.w, op_packed(op) ? packed_weight_bytes(op, a.N, a.K) : G * N * K * op_w_bytes(op), "W"};
   Buf by{a.y, M * N * 2, "y"};
-  Buf b0{a.s0, 0, op == OP_A8W8 ? "x_scales" : "scales"};
+  Buf b0{a.s0, 0, base == OP_A8W8 ? "x_scales" : "scales"};
   Buf b1{a.s1, 0, "w_scales"};
   Buf bo{a.xs_out, 0, "x_scales_out"};   // an output: may be NULL
-  if (op == OP_FP8T) b0.bytes = 4;
-  if (op == OP_A8W8 && K > 0) {
+  if (base == OP_FP8T) b0.bytes = 4;
+  if (base == OP_A8W8 && K > 0) {
     b0.bytes = M * kb * 4;
     b1.bytes = nb * kb * 4;
   }
-  if (op == OP_A8W8Q && K > 0) {
+  if (base == OP_A8W8Q && K > 0) {
     b1.bytes = nb * kb * 4;
     if (a.xs_out) bo.bytes = M * kb * 4;
   }
@@ -244,6 +245,11 @@ LaunchFn variant_fn(int op, int v, int M) {
     case OP_FP8T: t = lds ? tlds_table<OP_FP8T>() : tile_table<OP_FP8T>(); break;
     case OP_A8W8: t = lds ? tlds_table<OP_A8W8>() : tile_table<OP_A8W8>(); break;
     case OP_A8W8Q: t = lds ? tlds_table<OP_A8W8Q>() : tile_table<OP_A8W8Q>(); break;
+    case OP_PACKED + OP_BF16: t = lds ? tlds_table<OP_PACKED + OP_BF16>() : nullptr; break;
+    case OP_PACKED + OP_GATED: t = lds ? tlds_table<OP_PACKED + OP_GATED>() : nullptr; break;
+    case OP_PACKED + OP_FP8T: t = lds ? tlds_table<OP_PACKED + OP_FP8T>() : nullptr; break;
+    case OP_PACKED + OP_A8W8: t = lds ? tlds_table<OP_PACKED + OP_A8W8>() : nullptr; break;
+    case OP_PACKED + OP_A8W8Q: t = lds ? tlds_table<OP_PACKED + OP_A8W8Q>() : nullptr; break;
   }
   return t ? t[fi].f[fm] : nullptr;
 }
@@ -368,9 +374,10 @@ skg_status launch(int op, int v, const Args& a_in, hipStream_t s) {
 
 skg_status run_op(int op, const void* x, const void* w, const float* s0, const float* s1, void* y, int M, int N,
                   int K, hipStream_t s, float* xs_out = nullptr) {
-  Args a{x, w, s0, s1, y, M, N, K, (K + 127) / 128, nullptr, nullptr, op == OP_A8W8Q ? xs_out : nullptr};
-  if (op != OP_FP8T && op != OP_A8W8) a.s0 = nullptr;
-  if (op != OP_A8W8 && op != OP_A8W8Q) a.s1 = nullptr;
+  const int base = op_base(op);
+  Args a{x, w, s0, s1, y, M, N, K, (K + 127) / 128, nullptr, nullptr, base == OP_A8W8Q ? xs_out : nullptr};
+  if (base != OP_FP8T && base != OP_A8W8) a.s0 = nullptr;
+  if (base != OP_A8W8 && base != OP_A8W8Q) a.s1 = nullptr;
   if (skg_status st = validate(op, a)) return st;
   if (M == 0 || N == 0) return SKG_OK;
   prime_workspace(s);
@@ -421,6 +428,55 @@ skg_status skinny_gemm_a8w8_block(const void* x, const void* W, const float* x_s
 skg_status skinny_gemm_a8w8_block_quant(const void* x, const void* W, const float* w_scales, float* x_scales_out,
                                         void* y, int M, int N, int K, hipStream_t stream) {
   return run_op(OP_A8W8Q, x, W, nullptr, w_scales, y, M, N, K, stream, x_scales_out);
+}
+
+skg_status skinny_gemm_bf16_packed(const void* x, const void* W_packed, const float* scales, void* y, int M, int N,
+                                   int K, hipStream_t stream) {
+  return run_op(OP_PACKED + OP_BF16, x, W_packed, scales, nullptr, y, M, N, K, stream);
+}
+
+skg_status skinny_gemm_gated_packed(const void* x, const void* W_packed, const float* scales, void* y, int M, int N,
+                                    int K, hipStream_t stream) {
+  return run_op(OP_PACKED + OP_GATED, x, W_packed, scales, nullptr, y, M, N, K, stream);
+}
+
+skg_status skinny_gemm_fp8_tensor_packed(const void* x, const void* W_packed, const float* scales, void* y, int M,
+                                         int N, int K, hipStream_t stream) {
+  return run_op(OP_PACKED + OP_FP8T, x, W_packed, scales, nullptr, y, M, N, K, stream);
+}
+
+skg_status skinny_gemm_a8w8_block_packed(const void* x, const void* W_packed, const float* x_scales,
+                                         const float* w_scales, void* y, int M, int N, int K, hipStream_t stream) {
+  return run_op(OP_PACKED + OP_A8W8, x, W_packed, x_scales, w_scales, y, M, N, K, stream);
+}
+
+skg_status skinny_gemm_a8w8_block_quant_packed(const void* x, const void* W_packed, const float* w_scales,
+                                               float* x_scales_out, void* y, int M, int N, int K,
+                                               hipStream_t stream) {
+  return run_op(OP_PACKED + OP_A8W8Q, x, W_packed, nullptr, w_scales, y, M, N, K, stream, x_scales_out);
+}
+
+size_t skinny_gemm_packed_weight_bytes(int op, int N, int K) {
+  if (!op_name(op) || N <= 0 || K <= 0 || K % op_k_multiple(op)) return 0;
+  return packed_weight_bytes(op, N, K);
+}
+
+skg_status skinny_gemm_pack_weight(int op, const void* W, void* W_packed, int N, int K, hipStream_t stream) {
+  if (!op_name(op)) return fail(SKG_EINVAL, "unknown op %d", op);
+  if (N < 0 || K < 0) return fail(SKG_EINVAL, "negative size N=%d K=%d", N, K);
+  if (N == 0 || K == 0) return SKG_OK;
+  const int km = op_k_multiple(op);
+  if (K % km) return fail(SKG_EUNSUPPORTED, "%s needs K %% %d == 0 (K=%d)", op_name(op), km, K);
+  if ((size_t)N * (size_t)op_groups(op) > 0x7fffffffu) return fail(SKG_EUNSUPPORTED, "N too large");
+  if ((reinterpret_cast<uintptr_t>(W) | reinterpret_cast<uintptr_t>(W_packed)) & 15)
+    return fail(SKG_EUNSUPPORTED, "W and W_packed must be 16-byte aligned");
+  const Buf bw{W, (size_t)op_groups(op) * N * K * op_w_bytes(op), "W"};
+  const Buf bp{W_packed, packed_weight_bytes(op, N, K), "W_packed"};
+  for (const Buf* b : {&bw, &bp})
+    if (skg_status st = check_device_range(*b)) return st;
+  if (overlap(bw, bp)) return fail(SKG_EINVAL, "W_packed overlaps W");
+  const hipError_t e = launch_pack(op, W, W_packed, N, K, stream);
+  return e == hipSuccess ? SKG_OK : fail(SKG_ELAUNCH, "pack launch: %s", hipGetErrorString(e));
 }
 
 const char* skinny_gemm_last_error(void) { return g_err.c_str(); }
@@ -499,9 +555,10 @@ skg_status skinny_gemm_run_variant(int op, int variant, const int* knobs, const 
   if (variant < 0 || variant >= kNumVariants) return fail(SKG_EINVAL, "no variant %d", variant);
   if (knobs) return fail(SKG_EINVAL, "knobs are reserved: pass NULL");
   Args a{x, W, s0, s1, y, M, N, K, (K + 127) / 128, nullptr, nullptr, nullptr};
-  if (op == OP_A8W8Q) a.xs_out = const_cast<float*>(s0);   // its s0 is the x-scale output
-  if (op != OP_FP8T && op != OP_A8W8) a.s0 = nullptr;
-  if (op != OP_A8W8 && op != OP_A8W8Q) a.s1 = nullptr;
+  const int base = op_base(op);
+  if (base == OP_A8W8Q) a.xs_out = const_cast<float*>(s0);   // its s0 is the x-scale output
+  if (base != OP_FP8T && base != OP_A8W8) a.s0 = nullptr;
+  if (base != OP_A8W8 && base != OP_A8W8Q) a.s1 = nullptr;
   if (skg_status st = validate(op, a)) return st;
   if (M == 0 || N == 0) return SKG_OK;
   if (!variant_supports(op, variant, M))

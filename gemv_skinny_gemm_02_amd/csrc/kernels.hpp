@@ -655,15 +655,16 @@ struct LdsChunk {
   static constexpr int value = tlds_kch(OP);
 };
 
-template <int OP, int FM, int FN, int NW, int KW>
+template <int OP, int FM, int FN, int NW, int KW, int XD>
 struct LdsRound {
+  static constexpr int BO = op_base(OP);
   static constexpr int WPF = 2;                                              // 16-byte W loads per fragment per chunk
   static constexpr int XPIECES = KW * 16 * FM * tlds_xg_bytes(OP) / 16;    // 16-byte pieces of the round's x chunks
-  static constexpr int XPT = (XPIECES + 64 * NW - 1) / (64 * NW);      // pieces per thread
+  static constexpr int XPT = tlds_xpt(OP, FM, NW, KW, XD);              // pieces per thread (direct x: FM * XV)
   u32x4 w[op_groups(OP)][FN][WPF];
   u32x4 x[XPT];
-  float sx[OP == OP_A8W8 ? FM : 1];
-  float sw[OP == OP_A8W8 || OP == OP_A8W8Q ? FN : 1];
+  float sx[BO == OP_A8W8 ? FM : 1];
+  float sw[BO == OP_A8W8 || BO == OP_A8W8Q ? FN : 1];
 };
 
 // The maximum of v over each row of 16 lanes, in every lane of the row (DPP
@@ -733,23 +734,33 @@ __device__ __forceinline__ uint2 quant8_e4m3fn(const u32x4 xv, float amax, float
 // layout: the fragment layout itself would read 16 rows x 64 bytes per
 // instruction, and that load pattern is limited by the vector L1 (its address
 // stage stalls on the cache), not by HBM.
-template <int OP, int FM, int FN, int S, int P, int NW, int KW>
+// A fragment-packed weight (packed ops) is stored in fragment layout, chunk
+// by chunk: one wave load reads 1 KiB of contiguous bytes straight into the
+// MFMA operand, with no stage, and the workgroups running at one time read
+// neighbouring blocks of the same chunk.
+// With direct x (XD = 1) every lane loads its own x fragments (from L2, as
+// the rows are few) and no x tile, and no barrier per chunk, is needed.
+template <int OP, int FM, int FN, int S, int P, int NW, int KW, int XD>
 __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
+  constexpr int BO = op_base(OP);                 // the form
+  constexpr bool PK = op_packed(OP);              // weight in the fragment-packed layout
   constexpr int NT = 64 * NW;                     // threads of the workgroup
   constexpr int NG = NW / KW;                     // wave groups along N (KW waves each split K)
   constexpr int G = op_groups(OP);
   constexpr int KCH = LdsChunk<OP>::value;
   constexpr int WB = op_w_bytes(OP);
   constexpr int XB = op_x_bytes(OP);
-  using Round = LdsRound<OP, FM, FN, NW, KW>;
+  using Round = LdsRound<OP, FM, FN, NW, KW, XD>;
   constexpr int XPIECES = Round::XPIECES;
   constexpr int XPT = Round::XPT;
-  constexpr bool QX = OP == OP_A8W8Q;             // x quantised here: bf16 in, fp8 codes + scales in LDS
+  constexpr bool QX = BO == OP_A8W8Q;             // x quantised here: bf16 in, fp8 codes + scales in LDS
   constexpr int XS = tlds_xl_stride(OP);          // LDS x row stride
   constexpr int PPR = tlds_xg_bytes(OP) / 16;     // 16-byte x pieces per chunk row (as loaded)
   constexpr int SUBB = tlds_sub_bytes(OP, FM);    // bytes of one x chunk in LDS
   constexpr int BUFB = KW * SUBB;                 // bytes of one LDS x buffer (a round's KW chunks)
-  constexpr int XBUF = 2 * BUFB > tlds_red_bytes(OP, FM, FN, NW, KW) ? 2 * BUFB : tlds_red_bytes(OP, FM, FN, NW, KW);
+  constexpr int XTB = XD ? 0 : 2 * BUFB;           // bytes of the x tile
+  constexpr int XBUF = XTB > tlds_red_bytes(OP, FM, FN, NW, KW) ? XTB : tlds_red_bytes(OP, FM, FN, NW, KW);
+  constexpr int XV = tlds_xv(OP);                 // direct x: 16-byte pieces per fragment per chunk
   constexpr int WSTB = tlds_wstage_bytes(OP, FN);  // bytes of one wave's W stage
 
   extern __shared__ __align__(16) unsigned char xl[];   // [2][KW][x chunk] x, then [NW][G*FN*16][stride] W
@@ -786,6 +797,17 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
     wblk[f] = min(nb + f * 16, N - 1) >> 7;
   }
   unsigned char* wst = xl + XBUF + wave * WSTB;   // this wave's W stage
+  // fragment-packed weight: the 2 KiB block of chunk c, group g and 16-row
+  // block b starts at ((c*G + g)*N16 + b)*2048; load h of it at +1024h, this
+  // lane's 16 bytes at +16*lane
+  const int N16 = (N + 15) >> 4;
+  const size_t cstride = (size_t)G * N16 * 2048;
+  const char* wpk[G][FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      wpk[g][f] = static_cast<const char*>(a.w) + ((size_t)g * N16 + (min(nb + f * 16, N - 1) >> 4)) * 2048 + lane * 16;
   // x pieces this thread copies into LDS: piece p -> the round's chunk
   // p / (16*FM*PPR), chunk row (p / PPR) % (16*FM) (x row m_base + that,
   // clamped to M-1), byte column 16*(p%PPR)
@@ -795,7 +817,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   int xcolb[XPT], xdst[XPT], xsub[XPT], xrr[XPT];
   bool xmine[XPT];
 #pragma unroll
-  for (int i = 0; i < XPT; ++i) {
+  for (int i = 0; i < (XD ? 0 : XPT); ++i) {
     const int p = min((int)threadIdx.x + NT * i, XPIECES - 1);
     xmine[i] = (int)threadIdx.x + NT * i < XPIECES;
     xsub[i] = p / (16 * FM * PPR);
@@ -821,11 +843,11 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   auto chunk_of = [&](int c, int q) { return c_begin + c * KW + q; };
   auto wk = [&](int c, int h) {
     const int k0 = chunk_of(c, kw) * KCH;
-    if constexpr (OP == OP_A8W8 || OP == OP_A8W8Q) return k0 + h * 64 + lq * 16;
-    else if constexpr (OP == OP_FP8T) return k0 + lq * 32 + h * 16;
+    if constexpr (BO == OP_A8W8 || BO == OP_A8W8Q) return k0 + h * 64 + lq * 16;
+    else if constexpr (BO == OP_FP8T) return k0 + lq * 32 + h * 16;
     else return k0 + h * 32 + lq * 8;
   };
-  constexpr int LK = OP == OP_BF16 || OP == OP_GATED ? 8 : 16;   // K per 16-byte W load
+  constexpr int LK = BO == OP_BF16 || BO == OP_GATED ? 8 : 16;   // K per 16-byte W load
 
   // Each round issues its x loads (and A8W8 scales) before its W loads: the
   // hardware retires a wave's loads in issue order, so the x copy into LDS,
@@ -836,20 +858,41 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
     const int chunk = min(chunk_of(c, kw), NC - 1);
     // x: 16-byte pieces of the round's chunk rows; a piece of a chunk past the
     // split or past K re-reads in-range data (finite, against zeroed weights)
+    if constexpr (XD) {
+      // direct x: piece v of fragment j holds the bytes this lane's MFMA
+      // operand takes (the weight's K permutation), from row xm[j]
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int off = min(min(chunk_of(c, xsub[i]), NC - 1) * KCH * XB + xcolb[i], K * XB - 16);
-      b.x[i] = *reinterpret_cast<const u32x4*>(xrowp[i] + off);
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int v = 0; v < XV; ++v) {
+          const int off = chunk * KCH * XB + (BO == OP_FP8T ? lq * 64 + v * 16 : v * 64 + lq * 16);
+          b.x[j * XV + v] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.x) + (size_t)xm[j] * K * XB +
+                                                            min(off, K * XB - 16));
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < XPT; ++i) {
+        const int off = min(min(chunk_of(c, xsub[i]), NC - 1) * KCH * XB + xcolb[i], K * XB - 16);
+        b.x[i] = *reinterpret_cast<const u32x4*>(xrowp[i] + off);
+      }
     }
-    if constexpr (OP == OP_A8W8) {
+    if constexpr (BO == OP_A8W8) {
 #pragma unroll
       for (int j = 0; j < FM; ++j) b.sx[j] = a.s0[(size_t)xm[j] * kb + chunk];
     }
-    if constexpr (OP == OP_A8W8 || OP == OP_A8W8Q) {
+    if constexpr (BO == OP_A8W8 || BO == OP_A8W8Q) {
 #pragma unroll
       for (int f = 0; f < FN; ++f) b.sw[f] = a.s1[(size_t)wblk[f] * kb + chunk];
     }
-    {
+    if constexpr (PK) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int f = 0; f < FN; ++f)
+            b.w[g][f][h] = load_nt(reinterpret_cast<const u32x4*>(wpk[g][f] + chunk * cstride + h * 1024));
+    } else {
       // segment h of every fragment: 128 bytes of 8 rows; a segment piece past
       // K re-reads the last in-range piece (its weights are zeroed when used)
       const int off = min(chunk * KCH * WB, K * WB - 16 - (lane & 7) * 16);
@@ -895,13 +938,13 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
           }
         }
       }
-    } else {
+    } else if constexpr (!XD) {
 #pragma unroll
       for (int i = 0; i < XPT; ++i)
         if (XPIECES % NT == 0 || xmine[i]) *reinterpret_cast<u32x4*>(buf + xdst[i]) = b.x[i];
     }
-    __syncthreads();
-    {
+    if constexpr (!XD) __syncthreads();
+    if constexpr (!PK) {
       // the wave's own W stage needs no barrier (a wave's LDS accesses run in
       // order): stage the 128-byte segments (row 8h + lane/8, column lane%8) ...
 #pragma unroll
@@ -913,7 +956,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
             *reinterpret_cast<u32x4*>(wst + ((g * FN + f) * 16 + 8 * h + (lane >> 3)) * kWRowStride +
                                       (lane & 7) * 16) = b0.w[g][f][h];
     }
-    {
+    if constexpr (!PK) {
       // ... and read them back in fragment layout: row lr, the 16-byte piece h
       // of K-slot lq (fp8 weights with bf16 x: lane slot lq owns the 32
       // contiguous K of bytes 32*lq.., for W and x alike)
@@ -924,7 +967,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
 #pragma unroll
           for (int h = 0; h < 2; ++h)
             b.w[g][f][h] = *reinterpret_cast<const u32x4*>(
-                wst + ((g * FN + f) * 16 + lr) * kWRowStride + (OP == OP_FP8T ? lq * 32 + h * 16 : h * 64 + lq * 16));
+                wst + ((g * FN + f) * 16 + lr) * kWRowStride + (BO == OP_FP8T ? lq * 32 + h * 16 : h * 64 + lq * 16));
     }
     if constexpr (decltype(tail)::value) {        // lanes past K or past the split contribute nothing
 #pragma unroll
@@ -936,7 +979,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
           for (int f = 0; f < FN; ++f) b.w[g][f][h] = dead ? u32x4{0, 0, 0, 0} : b.w[g][f][h];
       }
     }
-    if constexpr (OP == OP_BF16 || OP == OP_GATED) {
+    if constexpr (BO == OP_BF16 || BO == OP_GATED) {
       // every x fragment of the chunk is read before the first MFMA: with one
       // wave per SIMD nothing else hides an LDS read's latency, so the reads
       // go out back to back and the MFMAs consume them in issue order
@@ -945,7 +988,8 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
-          B[u][j] = *reinterpret_cast<const u32x4*>(buf + kw * SUBB + (j * 16 + lr) * XS + u * 64 + lq * 16);
+          B[u][j] = XD ? b.x[j * XV + u]
+                       : *reinterpret_cast<const u32x4*>(buf + kw * SUBB + (j * 16 + lr) * XS + u * 64 + lq * 16);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -957,7 +1001,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
             for (int f = 0; f < FN; ++f)
               acc[g][f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                   __builtin_bit_cast(bf16x8, b.w[g][f][u]), __builtin_bit_cast(bf16x8, B[u][j]), acc[g][f][j], 0, 0, 0);
-    } else if constexpr (OP == OP_FP8T) {
+    } else if constexpr (BO == OP_FP8T) {
       // four MFMA steps of 8 K per lane slot: step u takes K 32*lq + 8u .. +7
       // of the chunk from W (fp8, converted exactly to bf16) and x alike
       u32x4 B[4][FM];
@@ -965,7 +1009,8 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
-          B[u][j] = *reinterpret_cast<const u32x4*>(buf + kw * SUBB + (j * 16 + lr) * XS + lq * 64 + u * 16);
+          B[u][j] = XD ? b.x[j * XV + u]
+                       : *reinterpret_cast<const u32x4*>(buf + kw * SUBB + (j * 16 + lr) * XS + lq * 64 + u * 16);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -993,7 +1038,8 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
         u32x4 B16[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          B16[h] = *reinterpret_cast<const u32x4*>(buf + kw * SUBB + (j * 16 + lr) * XS + h * 64 + lq * 16);
+          B16[h] = XD ? b.x[j * XV + h]
+                      : *reinterpret_cast<const u32x4*>(buf + kw * SUBB + (j * 16 + lr) * XS + h * 64 + lq * 16);
         float sxj;
         if constexpr (QX) sxj = *reinterpret_cast<const float*>(buf + kw * SUBB + 16 * FM * XS + (j * 16 + lr) * 4);
         else sxj = b.sx[j];
@@ -1059,7 +1105,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
 
   unsigned short* y = static_cast<unsigned short*>(a.y);
   float scale = 1.0f;
-  if constexpr (OP == OP_FP8T) scale = a.s0[0];
+  if constexpr (BO == OP_FP8T) scale = a.s0[0];
   if constexpr (S == 1) {
 #pragma unroll
     for (int f = 0; f < FN; ++f)
@@ -1072,8 +1118,8 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
           const int n = nb + f * 16 + lq * 4 + e;
           if (n >= N) continue;
           float v = acc[0][f][j][e];
-          if constexpr (OP == OP_GATED) v = silu_f32(v) * acc[G - 1][f][j][e];
-          if constexpr (OP == OP_FP8T) v *= scale;
+          if constexpr (BO == OP_GATED) v = silu_f32(v) * acc[G - 1][f][j][e];
+          if constexpr (BO == OP_FP8T) v *= scale;
           y[(size_t)m * N + n] = f32_to_bf16(v);
         }
       }
@@ -1152,8 +1198,8 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
                 v += pv[tb][sp][0][e];
                 if constexpr (G == 2) u += pv[tb][sp][G - 1][e];
               }
-              if constexpr (OP == OP_GATED) v = silu_f32(v) * u;
-              if constexpr (OP == OP_FP8T) v *= scale;
+              if constexpr (BO == OP_GATED) v = silu_f32(v) * u;
+              if constexpr (BO == OP_FP8T) v *= scale;
               y[(size_t)m * N + n + e] = f32_to_bf16(v);
             }
           }
@@ -1172,8 +1218,8 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
               u += __hip_atomic_load(a.ws + ((size_t)sp * G + 1) * MN + i, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
           }
-          if constexpr (OP == OP_GATED) v = silu_f32(v) * u;
-          if constexpr (OP == OP_FP8T) v *= scale;
+          if constexpr (BO == OP_GATED) v = silu_f32(v) * u;
+          if constexpr (BO == OP_FP8T) v *= scale;
           y[i] = f32_to_bf16(v);
         }
       }
@@ -1207,13 +1253,13 @@ hipError_t launch_tile(const Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int OP, int FM, int FN, int S, int P, int NW, int KW>
+template <int OP, int FM, int FN, int S, int P, int NW, int KW, int XD>
 hipError_t launch_tlds(const Args& a, hipStream_t s) {
   constexpr int TW = 16 * FN * (NW / KW);
   const unsigned gx = (unsigned)((a.N + TW - 1) / TW);
   const unsigned gy = (unsigned)((a.M + 16 * FM - 1) / (16 * FM));
-  const size_t smem = (size_t)tlds_smem(OP, FM, FN, NW, KW);
-  hipLaunchKernelGGL((tlds_kernel<OP, FM, FN, S, P, NW, KW>), dim3(gx, gy, S), dim3(64 * NW), smem, s, a);
+  const size_t smem = (size_t)tlds_smem(OP, FM, FN, NW, KW, XD);
+  hipLaunchKernelGGL((tlds_kernel<OP, FM, FN, S, P, NW, KW, XD>), dim3(gx, gy, S), dim3(64 * NW), smem, s, a);
   return hipGetLastError();
 }
 
@@ -1228,9 +1274,9 @@ constexpr LaunchFn tile_fn() {
   else return nullptr;
 }
 
-template <int OP, int FM, int FN, int S, int P, int NW, int KW>
+template <int OP, int FM, int FN, int S, int P, int NW, int KW, int XD>
 constexpr LaunchFn tlds_fn() {
-  if constexpr (tlds_valid(OP, FM, FN, S, P, NW, KW)) return &launch_tlds<OP, FM, FN, S, P, NW, KW>;
+  if constexpr (tlds_valid(OP, FM, FN, S, P, NW, KW, XD)) return &launch_tlds<OP, FM, FN, S, P, NW, KW, XD>;
   else return nullptr;
 }
 
@@ -1250,11 +1296,11 @@ constexpr TileRow tile_row() {
 }
 
 // Buckets above MC fragments launch the MC-fragment kernel over more grid rows.
-template <int OP, int FN, int S, int P, int MC, int NW, int KW>
+template <int OP, int FN, int S, int P, int MC, int NW, int KW, int XD>
 constexpr TileRow tlds_row() {
-  return TileRow{{tlds_fn<OP, tlds_fm(1, MC), FN, S, P, NW, KW>(), tlds_fn<OP, tlds_fm(2, MC), FN, S, P, NW, KW>(),
-                  tlds_fn<OP, tlds_fm(4, MC), FN, S, P, NW, KW>(), tlds_fn<OP, tlds_fm(6, MC), FN, S, P, NW, KW>(),
-                  tlds_fn<OP, tlds_fm(8, MC), FN, S, P, NW, KW>()}};
+  return TileRow{{tlds_fn<OP, tlds_fm(1, MC), FN, S, P, NW, KW, XD>(), tlds_fn<OP, tlds_fm(2, MC), FN, S, P, NW, KW, XD>(),
+                  tlds_fn<OP, tlds_fm(4, MC), FN, S, P, NW, KW, XD>(), tlds_fn<OP, tlds_fm(6, MC), FN, S, P, NW, KW, XD>(),
+                  tlds_fn<OP, tlds_fm(8, MC), FN, S, P, NW, KW, XD>()}};
 }
 
 // Launch tables, one pair per op, defined in ops_<op>.hip:
@@ -1277,5 +1323,14 @@ template <> const TileRow* tlds_table<OP_GATED>();
 template <> const TileRow* tlds_table<OP_FP8T>();
 template <> const TileRow* tlds_table<OP_A8W8>();
 template <> const TileRow* tlds_table<OP_A8W8Q>();
+template <> const TileRow* tlds_table<OP_PACKED + OP_BF16>();
+template <> const TileRow* tlds_table<OP_PACKED + OP_GATED>();
+template <> const TileRow* tlds_table<OP_PACKED + OP_FP8T>();
+template <> const TileRow* tlds_table<OP_PACKED + OP_A8W8>();
+template <> const TileRow* tlds_table<OP_PACKED + OP_A8W8Q>();
+
+// Writes the fragment-packed copy of W [G*N, K] (G = 2 for the gated form)
+// for op into Wp (packed_weight_bytes(op, N, K) bytes), on stream s.
+hipError_t launch_pack(int op, const void* W, void* Wp, int N, int K, hipStream_t s);
 
 }  // namespace skg

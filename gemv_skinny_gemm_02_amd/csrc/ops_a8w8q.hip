@@ -8,7 +8,7 @@ namespace {
 constexpr GemvRow kGemv[kNumGemv] = {
 #define SKG_GEMV(name, R, KS, U) gemv_row<OP_A8W8Q, R, KS, U>(),
 #define SKG_TILE(name, FN, KS, U)
-#define SKG_TLDS(name, FN, S, P, MC, NW, KW)
+#define SKG_TLDS(name, FN, S, P, MC, NW, KW, XD)
 #include "variants.def"
 #undef SKG_GEMV
 #undef SKG_TILE
@@ -17,7 +17,7 @@ constexpr GemvRow kGemv[kNumGemv] = {
 constexpr TileRow kTile[kNumTile] = {
 #define SKG_GEMV(name, R, KS, U)
 #define SKG_TILE(name, FN, KS, U) tile_row<OP_A8W8Q, FN, KS, U>(),
-#define SKG_TLDS(name, FN, S, P, MC, NW, KW)
+#define SKG_TLDS(name, FN, S, P, MC, NW, KW, XD)
 #include "variants.def"
 #undef SKG_GEMV
 #undef SKG_TILE
@@ -26,7 +26,7 @@ constexpr TileRow kTile[kNumTile] = {
 constexpr TileRow kTlds[kNumTlds] = {
 #define SKG_GEMV(name, R, KS, U)
 #define SKG_TILE(name, FN, KS, U)
-#define SKG_TLDS(name, FN, S, P, MC, NW, KW) tlds_row<OP_A8W8Q, FN, S, P, MC, NW, KW>(),
+#define SKG_TLDS(name, FN, S, P, MC, NW, KW, XD) tlds_row<OP_A8W8Q, FN, S, P, MC, NW, KW, XD>(),
 #include "variants.def"
 #undef SKG_GEMV
 #undef SKG_TILE

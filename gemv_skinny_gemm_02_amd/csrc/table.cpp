@@ -196,6 +196,11 @@ const char* op_name(int op) {
     case OP_FP8T: return "fp8_tensor";
     case OP_A8W8: return "a8w8_block";
     case OP_A8W8Q: return "a8w8_quant";
+    case OP_PACKED + OP_BF16: return "bf16_packed";
+    case OP_PACKED + OP_GATED: return "gated_packed";
+    case OP_PACKED + OP_FP8T: return "fp8_tensor_packed";
+    case OP_PACKED + OP_A8W8: return "a8w8_block_packed";
+    case OP_PACKED + OP_A8W8Q: return "a8w8_quant_packed";
     default: return nullptr;
   }
 }
@@ -314,19 +319,31 @@ int Table::load(const std::string& path, const Identity& self, std::string* err)
 // The untuned entry point: what runs with no table, and the incumbent a table
 // entry has to beat.  A shape rule fitted to gfx950 measurements of the whole
 // variant list over the decode shapes:
-//  * x quantised in the call (A8W8 from bf16 x): the LDS tile with one K group
-//    per workgroup (quantisation runs in every round of every workgroup) and
-//    K split S ways across workgroups: S = 8 up to 64 tiles of 64 weight
-//    rows, 4 up to 128, 2 up to 256, else 1; from the rows-32 bucket
-//    eight-wave workgroups at S = 4, else two fragments per wave at S = 2.
-//  * rows 1..3, rows 4 unless the weight is fp8, and rows up to 8 when the
-//    weight is under 16 MiB: the VALU weight stream.  Two weight rows per
-//    wave for one row of x, four for more, eight for a vocabulary-sized N
-//    (>= 65536) with more than one row of x; K split over the 4 waves of a
-//    workgroup unless a weight row is under 2 KiB, where the 4 waves take
-//    different rows instead.
+//  * x quantised in the call (A8W8 from bf16 x), row-major or packed weight:
+//    the LDS tile with one K group per workgroup (quantisation runs in every
+//    round of every workgroup) and K split S ways across workgroups: S = 8
+//    up to 64 tiles of 64 weight rows, 4 up to 128, 2 up to 256, else 1;
+//    from the rows-32 bucket eight-wave workgroups at S = 4, else two
+//    fragments per wave at S = 2.
+//  * other forms with a packed weight, by 16-row weight blocks: from 1024
+//    blocks the LDS tile with one K group (x through LDS); from 384, up to
+//    16 rows, eight waves of which four split K (direct x up to 4 rows from
+//    512 blocks), then S = 2 or 1 tiles; at 256, direct x with K split over
+//    4 waves up to 12 rows, then the LDS x tile (in-workgroup, then S = 2 or
+//    4 splits); below, direct x up to 8 rows, then the in-workgroup split.
+//  * A8W8 (row-major), rows up to 16: the LDS tile with one K group from
+//    16384 weight rows, else eight waves (direct x up to 4 rows).
+//  * rows 1..3, rows 4 unless the weight is fp8 or its rows are large, and
+//    rows up to 6 when the weight is under 16 MiB: the VALU weight stream.
+//    Two weight rows per wave for one row of x, four for more, eight for a
+//    vocabulary-sized N (>= 65536) with more than one row of x; K split over
+//    the 4 waves of a workgroup unless a weight row is under 2 KiB, where the
+//    4 waves take different rows instead.
+//  * rows 4..6 on weights of >= 16 MiB with rows of >= 8 KiB and >= 4096
+//    rows: direct x, K split over eight waves.
 //  * weights under 16 MiB above that: the LDS tile with 16 weight rows per
-//    workgroup and K split over its 4 waves (no cross-workgroup combine).
+//    workgroup and K split over its 4 waves (no cross-workgroup combine),
+//    direct x up to 64 rows.
 //  * rows 6..16 where a weight row holds at least 4 KiB and the 16-row tiles
 //    come in whole multiples of 256 (one or more per CU): the same.
 //  * otherwise the LDS tile with K split S ways across workgroups, so that
@@ -358,16 +375,58 @@ int default_pick(int op, int M, int N, int K, bool allow_ws) {
   const double rowb = (double)K * op_w_bytes(op);
   const double MiB = 1024.0 * 1024.0;
   const bool small_w = wbytes < 16 * MiB;
-  const bool gemv = op != OP_A8W8Q &&   // (x quantised in the kernel: LDS tile family only)
-                    (b <= 3 || (b == 4 && op != OP_A8W8 && op != OP_FP8T) || (small_w && b <= 8));
+  const int bo = op_base(op);
+  const bool pk = op_packed(op);
+  // (x quantised in the kernel, or a packed weight: LDS tile family only)
+  const bool gemv = !pk && bo != OP_A8W8Q && bo != OP_A8W8 &&
+                    (b <= 3 || (b == 4 && bo != OP_FP8T && !(wrows >= 4096 && rowb >= 8192)) ||
+                     (small_w && b <= 6));
+  const double blocks = wrows / 16.0;   // 16-row weight blocks
+  // S > 1 variants need the split-K workspace: without it, the same tile with S = 1
+  auto ws_or = [&](const char* with_ws, const char* without) { return allow_ws ? with_ws : without; };
   int v = -1;
-  if (gemv) {
+  if (pk && bo != OP_A8W8Q) {
+    // packed weight (measured on gfx950): x through LDS with one K group when
+    // blocks are plenty; eight-wave K split for few rows on mid-sized
+    // weights; direct x for few rows on small ones
+    const char* n = nullptr;
+    if (blocks >= 1024) {
+      n = b <= 16 ? "tlds_f1_s1_p4_m2" : "tlds_f1_s1_p4_m4";
+    } else if (blocks >= 384) {
+      n = (b <= 4 && blocks >= 512) ? "tlds_d_k4_f1_s1_p4_m2"
+          : b <= 16                 ? "tlds_w8_k4_f1_s1_p4_m2"
+          : b <= 32                 ? ws_or("tlds_f1_s2_p4_m2", "tlds_f1_s1_p4_m2")
+          : b <= 64                 ? (blocks >= 512 ? "tlds_f1_s1_p4_m2" : ws_or("tlds_f1_s2_p4_m4", "tlds_f1_s1_p4_m4"))
+          : b <= 96                 ? ws_or("tlds_w8_f1_s4_p4", "tlds_f1_s1_p4_m4")
+                                    : ws_or("tlds_w8_f1_s2_p4_m4", "tlds_f1_s1_p4_m4");
+    } else if (blocks >= 256) {
+      n = b <= 12   ? "tlds_d_k4_f1_s1_p4_m1"
+          : b <= 16 ? "tlds_k4_f1_s1_p4_m1"
+          : b <= 32 ? ws_or("tlds_k2_f1_s2_p4_m2", "tlds_k4_f1_s1_p4_m2")
+          : b <= 64 ? ws_or("tlds_f1_s4_p4_m4", "tlds_f1_s1_p4_m4")
+          : b <= 96 ? ws_or("tlds_f1_s4_p4", "tlds_f1_s1_p4_m4")
+                    : ws_or("tlds_f1_s2_p4_m4", "tlds_f1_s1_p4_m4");
+    } else {
+      n = b <= 8 ? "tlds_d_k4_f1_s1_p4_m1"
+          : (b <= 64 || blocks < 128) ? "tlds_k4_f1_s1_p4_m1"
+                                      : "tlds_w8_k4_f1_s1_p4_m2";
+    }
+    v = first_supported(op, M, {n, "tlds_k4_f1_s1_p4_m1", "tlds_f1_s1_p4_m2"});
+  } else if (!pk && bo == OP_A8W8 && b <= 16) {
+    // A8W8, few rows: the LDS tile beats the VALU stream from one row
+    v = wrows >= 16384 ? first_supported(op, M, {"tlds_f1_s1_p4_m2", "tlds_f1_s1_p4_m4"})
+                       : first_supported(op, M, {b <= 4 ? "tlds_d_w8_k8_f1_s1_p4_m2" : "tlds_w8_k4_f1_s1_p4_m2",
+                                                 "tlds_k4_f1_s1_p4_m2"});
+  } else if (gemv) {
     if (rowb < 2048) v = first_supported(op, M, {"gemv_r4_k1_p2", "gemv_r4_k2_p2"});
     else if (M == 1) v = first_supported(op, M, {"gemv_r2_k4_p1", "gemv_r4_k4_p1"});
     else if (N >= 65536) v = first_supported(op, M, {"gemv_r8_k4_p1", "gemv_r4_k4_p1", "gemv_r2_k4_p1"});
     else v = first_supported(op, M, {"gemv_r4_k4_p1", "gemv_r2_k4_p1", "gemv_r1_k4_p2"});
     if (v < 0) v = first_of_family(op, M, FAM_GEMV);
-  } else if (op == OP_A8W8Q) {
+  } else if (bo != OP_A8W8Q && !small_w && b >= 4 && b <= 6 && wrows >= 4096 && rowb >= 8192) {
+    // large weight rows, a few rows of x: direct x, K split over eight waves
+    v = first_supported(op, M, {"tlds_d_w8_k8_f1_s1_p4_m2", "tlds_k4_f1_s1_p4_m2"});
+  } else if (bo == OP_A8W8Q) {
     // x is quantised in every round, so K split over the waves of a workgroup
     // multiplies the quantisation each round waits for: one K group per
     // workgroup, and the chip filled through the cross-workgroup split
@@ -383,7 +442,9 @@ int default_pick(int op, int M, int N, int K, bool allow_ws) {
           : allow_ws ? first_supported(op, M, {"tlds_f2_s2_p2", "tlds_f1_s2_p4_m2"})
                      : first_supported(op, M, {"tlds_f1_s1_p4_m2", "tlds_f1_s1_p4_m4"});
   } else if (small_w) {
-    if (b <= 32 || wbytes <= 4 * MiB) v = first_supported(op, M, {"tlds_k4_f1_s1_p4_m1", "tlds_k4_f1_s1_p4_m2"});
+    if (b <= 64 && (b <= 32 || wbytes <= 4 * MiB))
+      v = first_supported(op, M, {"tlds_d_k4_f1_s1_p4_m1", "tlds_k4_f1_s1_p4_m1", "tlds_k4_f1_s1_p4_m2"});
+    else if (b <= 32 || wbytes <= 4 * MiB) v = first_supported(op, M, {"tlds_k4_f1_s1_p4_m1", "tlds_k4_f1_s1_p4_m2"});
     else if (b <= 64) v = first_supported(op, M, {"tlds_k4_f1_s1_p4_m2", "tlds_k4_f1_s1_p4_m1"});
     else v = first_supported(op, M, {"tlds_w8_k4_f1_s1_p4_m2", "tlds_k4_f1_s1_p4_m2"});
   } else if (b <= 16 && rowb >= 4096 && std::fmod(wrows, 16.0 * 256.0) == 0.0) {

@@ -7,8 +7,11 @@
 namespace skg {
 
 // OP_A8W8Q: A8W8 block scale with bf16 x, quantised per row and 128-K group
-// inside the kernel (LDS tile path only).
-enum Op : int { OP_BF16 = 0, OP_GATED = 1, OP_FP8T = 2, OP_A8W8 = 3, OP_A8W8Q = 4, NUM_OPS = 5 };
+// inside the kernel (LDS tile path only).  Ops OP_PACKED + o are op o with
+// the weight in the fragment-packed layout (LDS tile path only).
+enum Op : int { OP_BF16 = 0, OP_GATED = 1, OP_FP8T = 2, OP_A8W8 = 3, OP_A8W8Q = 4, OP_PACKED = 5, NUM_OPS = 10 };
+constexpr int op_base(int op) { return op >= OP_PACKED ? op - OP_PACKED : op; }
+constexpr bool op_packed(int op) { return op >= OP_PACKED; }
 enum Family : int { FAM_GEMV = 0, FAM_TILE = 1, FAM_TLDS = 2 };
 
 // Rows buckets: M is rounded up to the next one (padded-M lookup with no
@@ -43,9 +46,11 @@ constexpr int tile_fm_index(int M) {  // M rows in one launch row (<= 128)
   return kNumTileFM - 1;
 }
 
-constexpr int op_groups(int op) { return op == OP_GATED ? 2 : 1; }
-constexpr bool op_w_fp8(int op) { return op == OP_FP8T || op == OP_A8W8 || op == OP_A8W8Q; }
-constexpr bool op_x_fp8(int op) { return op == OP_A8W8; }
+constexpr int op_groups(int op) { return op_base(op) == OP_GATED ? 2 : 1; }
+constexpr bool op_w_fp8(int op) {
+  return op_base(op) == OP_FP8T || op_base(op) == OP_A8W8 || op_base(op) == OP_A8W8Q;
+}
+constexpr bool op_x_fp8(int op) { return op_base(op) == OP_A8W8; }
 constexpr int op_w_bytes(int op) { return op_w_fp8(op) ? 1 : 2; }
 constexpr int op_x_bytes(int op) { return op_x_fp8(op) ? 1 : 2; }
 // K elements in one 16-byte weight load of one lane.
@@ -64,7 +69,7 @@ constexpr int gemv_regs(int op, int MT, int R, int P) {
 }
 constexpr bool gemv_valid(int op, int MT, int R, int KS, int P) {
   const int G = op_groups(op);
-  return op != OP_A8W8Q && (KS == 1 || KS == 2 || KS == 4) && P >= 1 && MT * R * G <= 64 &&
+  return op != OP_A8W8Q && !op_packed(op) && (KS == 1 || KS == 2 || KS == 4) && P >= 1 && MT * R * G <= 64 &&
          gemv_regs(op, MT, R, P) <= kRegBudget && (128 % ((4 / KS) * R)) == 0;
 }
 constexpr int tile_red_bytes(int op, int FM, int FN, int KS) {
@@ -78,7 +83,7 @@ constexpr int tile_regs(int op, int FM, int FN, int P) {
 }
 constexpr bool tile_valid(int op, int FM, int FN, int KS, int P) {
   const int G = op_groups(op);
-  return op != OP_A8W8Q && (KS == 1 || KS == 2 || KS == 4) && P >= 1 && G * FN * FM * 4 <= 128 &&
+  return op != OP_A8W8Q && !op_packed(op) && (KS == 1 || KS == 2 || KS == 4) && P >= 1 && G * FN * FM * 4 <= 128 &&
          tile_regs(op, FM, FN, P) <= kRegBudget && tile_red_bytes(op, FM, FN, KS) <= 65536 &&
          (128 % ((4 / KS) * FN * 16)) == 0;
 }
@@ -88,40 +93,47 @@ constexpr bool tile_valid(int op, int FM, int FN, int KS, int P) {
 // followed (per chunk) by one float32 scale per row.
 constexpr int tlds_kch(int op) { return op_w_fp8(op) ? 128 : 64; }
 constexpr int tlds_xg_bytes(int op) { return tlds_kch(op) * op_x_bytes(op); }                  // x row in HBM
-constexpr int tlds_xl_bytes(int op) { return op == OP_A8W8Q ? tlds_kch(op) : tlds_xg_bytes(op); }  // x row in LDS
+constexpr int tlds_xl_bytes(int op) {                                    // x row in LDS
+  return op_base(op) == OP_A8W8Q ? tlds_kch(op) : tlds_xg_bytes(op);
+}
 constexpr int tlds_xl_stride(int op) { return tlds_xl_bytes(op) + 16; }   // rows start 4 banks apart
 constexpr int tlds_sub_bytes(int op, int FM) {                            // one chunk of x in LDS
-  return 16 * FM * tlds_xl_stride(op) + (op == OP_A8W8Q ? 16 * FM * 4 : 0);
+  return 16 * FM * tlds_xl_stride(op) + (op_base(op) == OP_A8W8Q ? 16 * FM * 4 : 0);
 }
+// With x loaded by each lane itself (direct x, no LDS x tile): 16-byte x
+// pieces per fragment per chunk.
+constexpr int tlds_xv(int op) { return tlds_xg_bytes(op) / 64; }
 constexpr int kWRowStride = 144;   // W stage rows: 128 bytes + 16 of padding
 constexpr int tlds_wstage_bytes(int op, int FN) { return op_groups(op) * FN * 16 * kWRowStride; }
 constexpr int tlds_red_bytes(int op, int FM, int FN, int NW, int KW) {   // K-group partials after the loop
   return (KW - 1) * (NW / KW) * 64 * op_groups(op) * FN * FM * 4 * 4;
 }
-// LDS bytes of a workgroup: the double-buffered x chunks (KW per round),
-// reused after the loop for the K-group partials, then one W stage per wave.
-constexpr int tlds_smem(int op, int FM, int FN, int NW, int KW) {
-  const int xb = 2 * KW * tlds_sub_bytes(op, FM), rb = tlds_red_bytes(op, FM, FN, NW, KW);
-  return (xb > rb ? xb : rb) + NW * tlds_wstage_bytes(op, FN);
+// LDS bytes of a workgroup: the double-buffered x chunks (KW per round; none
+// with direct x), reused after the loop for the K-group partials, then one W
+// stage per wave (none with a packed weight, which arrives in fragment layout).
+constexpr int tlds_smem(int op, int FM, int FN, int NW, int KW, int XD) {
+  const int xb = XD ? 0 : 2 * KW * tlds_sub_bytes(op, FM), rb = tlds_red_bytes(op, FM, FN, NW, KW);
+  return (xb > rb ? xb : rb) + (op_packed(op) ? 0 : NW * tlds_wstage_bytes(op, FN));
 }
-constexpr int tlds_xpt(int op, int FM, int NW, int KW) {   // 16-byte x pieces per thread per round
-  return (KW * 16 * FM * (tlds_xg_bytes(op) / 16) + 64 * NW - 1) / (64 * NW);
+constexpr int tlds_xpt(int op, int FM, int NW, int KW, int XD) {   // 16-byte x pieces per thread per round
+  return XD ? FM * tlds_xv(op) : (KW * 16 * FM * (tlds_xg_bytes(op) / 16) + 64 * NW - 1) / (64 * NW);
 }
-constexpr int tlds_regs(int op, int FM, int FN, int P, int NW, int KW) {
-  const int G = op_groups(op);
-  const bool a8 = op == OP_A8W8 || op == OP_A8W8Q;
-  const int per_chunk = G * FN * 2 * 4 + tlds_xpt(op, FM, NW, KW) * 4 + (op == OP_A8W8 ? FM + FN : (a8 ? FN : 0));
+constexpr int tlds_regs(int op, int FM, int FN, int P, int NW, int KW, int XD) {
+  const int G = op_groups(op), b = op_base(op);
+  const bool a8 = b == OP_A8W8 || b == OP_A8W8Q;
+  const int per_chunk = G * FN * 2 * 4 + tlds_xpt(op, FM, NW, KW, XD) * 4 + (b == OP_A8W8 ? FM + FN : (a8 ? FN : 0));
   const int acc = G * FN * FM * 4;
-  const int xfrag = op == OP_FP8T ? 16 * FM : (op == OP_BF16 || op == OP_GATED ? 8 * FM : (a8 ? 8 : 0));
-  const int quant = op == OP_A8W8Q ? 8 * tlds_xpt(op, FM, NW, KW) : 0;   // decoded x of the pieces being quantised
+  const int xfrag = b == OP_FP8T ? 16 * FM : (b == OP_BF16 || b == OP_GATED ? 8 * FM : (a8 ? 8 : 0));
+  const int quant = b == OP_A8W8Q ? 8 * tlds_xpt(op, FM, NW, KW, XD) : 0;   // decoded x of the pieces being quantised
   return P * per_chunk + acc * (a8 ? 2 : 1) + FM * 4 + xfrag + quant;
 }
-constexpr bool tlds_valid(int op, int FM, int FN, int S, int P, int NW, int KW) {
+constexpr bool tlds_valid(int op, int FM, int FN, int S, int P, int NW, int KW, int XD) {
   const int G = op_groups(op);
+  const bool q = op_base(op) == OP_A8W8Q;
   return (S == 1 || S == 2 || S == 4 || S == 8) && (NW == 4 || NW == 8) && (KW == 1 || KW == 2 || KW == 4 || KW == 8) &&
-         NW % KW == 0 && P >= 1 && G * FN * FM * 4 <= 128 &&
-         tlds_regs(op, FM, FN, P, NW, KW) <= (op == OP_A8W8Q && NW == 8 ? 160 : 224) &&
-         tlds_smem(op, FM, FN, NW, KW) <= 64 * 1024 && (128 % (64 * FN)) == 0;
+         NW % KW == 0 && P >= 1 && G * FN * FM * 4 <= 128 && (XD == 0 || (XD == 1 && !q && FM <= 2)) &&
+         tlds_regs(op, FM, FN, P, NW, KW, XD) <= (q && NW == 8 ? 160 : 224) &&
+         tlds_smem(op, FM, FN, NW, KW, XD) <= 64 * 1024 && (128 % (64 * FN)) == 0;
 }
 // Bytes of split-K partials a tlds launch with S > 1 needs, and the number of
 // output tiles (one arrival counter each) its grid has.
@@ -131,6 +143,12 @@ constexpr unsigned long long tlds_ws_bytes(int op, int S, int M, int N) {
 constexpr unsigned long long tlds_tiles(int FN, int NG, int FM, int M, int N) {
   return (unsigned long long)((N + 16 * FN * NG - 1) / (16 * FN * NG)) *
          (unsigned long long)((M + 16 * FM - 1) / (16 * FM));
+}
+// Bytes of the fragment-packed weight of op: G groups of ceil(N/16) blocks
+// of 16 rows, each cut into ceil(K*WB/128) chunks of 128 bytes per row, each
+// (chunk, group, block) 2 KiB in MFMA fragment layout.
+constexpr unsigned long long packed_weight_bytes(int op, int N, int K) {
+  return (unsigned long long)((K * op_w_bytes(op) + 127) / 128) * op_groups(op) * ((N + 15) / 16) * 2048ull;
 }
 // M fragments a tlds workgroup takes: the bucket's count, capped at MC.
 constexpr int tlds_fm(int FM, int MC) { return FM < MC ? FM : MC; }
@@ -143,13 +161,13 @@ constexpr int kSplitCounters = 65536;   // arrival counters kept in the workspac
 struct VariantDesc {
   const char* name;
   int family;
-  int p0, p1, p2, p3, p4, p5;  // GEMV: R, KS, U.  TILE: FN, KS, U.  TLDS: FN, S, P, MC, NW, KW.
+  int p0, p1, p2, p3, p4, p5, p6;  // GEMV: R, KS, U.  TILE: FN, KS, U.  TLDS: FN, S, P, MC, NW, KW, XD.
 };
 
 constexpr VariantDesc kVariants[] = {
-#define SKG_GEMV(name, R, KS, U) {#name, FAM_GEMV, R, KS, U, 0, 0, 0},
-#define SKG_TILE(name, FN, KS, U) {#name, FAM_TILE, FN, KS, U, 0, 0, 0},
-#define SKG_TLDS(name, FN, S, P, MC, NW, KW) {#name, FAM_TLDS, FN, S, P, MC, NW, KW},
+#define SKG_GEMV(name, R, KS, U) {#name, FAM_GEMV, R, KS, U, 0, 0, 0, 0},
+#define SKG_TILE(name, FN, KS, U) {#name, FAM_TILE, FN, KS, U, 0, 0, 0, 0},
+#define SKG_TLDS(name, FN, S, P, MC, NW, KW, XD) {#name, FAM_TLDS, FN, S, P, MC, NW, KW, XD},
 #include "variants.def"
 #undef SKG_GEMV
 #undef SKG_TILE
@@ -180,7 +198,7 @@ constexpr bool variant_supports(int op, int i, int M) {
     return mi >= 0 && gemv_valid(op, kGemvMT[mi], v.p0, v.p1, v.p2);
   }
   const int fm = M > kMaxBucket ? kNumTileFM - 1 : tile_fm_index(M);
-  if (v.family == FAM_TLDS) return tlds_valid(op, tlds_fm(kTileFM[fm], v.p3), v.p0, v.p1, v.p2, v.p4, v.p5);
+  if (v.family == FAM_TLDS) return tlds_valid(op, tlds_fm(kTileFM[fm], v.p3), v.p0, v.p1, v.p2, v.p4, v.p5, v.p6);
   return tile_valid(op, kTileFM[fm], v.p0, v.p1, v.p2);
 }
 
@@ -193,12 +211,12 @@ constexpr const char kSpaceText[] =
     "buckets=1,2,3,4,6,8,12,16,24,32,64,96,128;gemv_mt=1,2,3,4,6,8,12,16;tile_fm=1,2,4,6,8;tile_min=1;"
 #define SKG_GEMV(name, R, KS, U) "G:" #name "," #R "," #KS "," #U ";"
 #define SKG_TILE(name, FN, KS, U) "T:" #name "," #FN "," #KS "," #U ";"
-#define SKG_TLDS(name, FN, S, P, MC, NW, KW) "L:" #name "," #FN "," #S "," #P "," #MC "," #NW "," #KW ";"
+#define SKG_TLDS(name, FN, S, P, MC, NW, KW, XD) "L:" #name "," #FN "," #S "," #P "," #MC "," #NW "," #KW "," #XD ";"
 #include "variants.def"
 #undef SKG_GEMV
 #undef SKG_TILE
 #undef SKG_TLDS
-    "kernels=14";  // bump when a kernel's arithmetic or indexing changes
+    "kernels=15";  // bump when a kernel's arithmetic or indexing changes
 constexpr uint32_t kSpaceToken = fnv1a(kSpaceText);
 
 }  // namespace skg

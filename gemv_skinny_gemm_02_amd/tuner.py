@@ -60,7 +60,15 @@ def workload_keys(ops):
         keys += [("a8w8_block", M, N, K) for (N, K) in synth.A8W8_NK for M in synth.A8W8_M]
     if "a8w8_quant" in ops:
         keys += [("a8w8_quant", M, N, K) for (N, K) in synth.A8W8_NK for M in synth.A8W8_M]
+    # the packed forms run on the same shapes as their row-major forms
+    for op in [o for o in ops if o.endswith("_packed")]:
+        keys += [(op, M, N, K) for (_, M, N, K) in workload_keys([op[:-len("_packed")]])]
     return keys
+
+
+def base_op(op):
+    """The row-major form of an op name."""
+    return op[:-len("_packed")] if op.endswith("_packed") else op
 
 
 def bucket_of(M):
@@ -71,6 +79,7 @@ def bucket_of(M):
 
 
 def alg_bytes(op, M, N, K):
+    op = base_op(op)
     if op == "bf16":
         return 2 * N * K + 2 * M * K + 2 * M * N
     if op == "gated":
@@ -127,6 +136,7 @@ def tune(store, ops, quick=False, rotation_gib=1.0, replays=5, only_m=None):
     stream = torch.cuda.current_stream()
     make = {"bf16": synth.make_bf16, "gated": synth.make_gated, "fp8_tensor": synth.make_fp8_tensor,
             "a8w8_block": synth.make_a8w8_block, "a8w8_quant": synth.make_a8w8_quant}
+    ops = list(ops)
     cache = {}
     with open(store, "a") as fout:
         for (op, M, N, K) in keys:
@@ -137,15 +147,16 @@ def tune(store, ops, quick=False, rotation_gib=1.0, replays=5, only_m=None):
             if not todo:
                 continue
             shape_key = (op, N, K)
+            bop = base_op(op)
             if shape_key not in cache:
                 cache.clear()
                 torch.cuda.empty_cache()
-                p = make[op](max(m for (o, m, n, k) in keys if (o, n, k) == shape_key), N, K, seed=0)
-                if op in ("bf16", "gated"):
+                p = make[bop](max(m for (o, m, n, k) in keys if (o, n, k) == shape_key), N, K, seed=0)
+                if bop in ("bf16", "gated"):
                     x = torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).cuda()
                     w0 = torch.from_numpy(p.w.view(np.int16)).view(torch.bfloat16).cuda()
                 else:
-                    x = (torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16) if op in ("fp8_tensor", "a8w8_quant")
+                    x = (torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16) if bop in ("fp8_tensor", "a8w8_quant")
                          else torch.from_numpy(p.x).view(torch.float8_e4m3fn)).cuda()
                     w0 = torch.from_numpy(p.w).view(torch.float8_e4m3fn).cuda()
                 s0 = torch.from_numpy(p.s0).cuda() if p.s0 is not None else None
@@ -153,11 +164,15 @@ def tune(store, ops, quick=False, rotation_gib=1.0, replays=5, only_m=None):
                 R = max(2, math.ceil(rotation_gib * 2**30 / (w0.numel() * w0.element_size())))
                 free, _ = torch.cuda.mem_get_info()
                 R = max(1, min(R, int(0.6 * free // (w0.numel() * w0.element_size()))))
-                ws = [w0] + [w0.clone() for _ in range(R - 1)]
+                if op != bop:      # packed copies, each packed from the same weight
+                    ws = [skg.skinny_gemm_pack_weight(bop, w0) for _ in range(R)]
+                    del w0
+                else:
+                    ws = [w0] + [w0.clone() for _ in range(R - 1)]
                 cache[shape_key] = (x, ws, s0, s1)
             x, ws, s0, s1 = cache[shape_key]
             xm = x[:M]
-            s0m = s0[:M] if (op == "a8w8_block" and s0 is not None) else s0
+            s0m = s0[:M] if (bop == "a8w8_block" and s0 is not None) else s0
             y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
             # the true default: what dispatch runs with no table
             default_name = skg.skinny_gemm_query(op, M, N, K)[0] if not skg.skinny_gemm_table_status()[0] else None
@@ -217,7 +232,9 @@ def promote(store, out, identity=None):
         if prev is None or r["M"] > prev["M"] or (r["M"] == prev["M"] and r["time"] > prev["time"]):
             slot[r["variant"]] = r
     entries = []
-    order = {"bf16": 0, "gated": 1, "fp8_tensor": 2, "a8w8_block": 3, "a8w8_quant": 4}
+    order = {"bf16": 0, "gated": 1, "fp8_tensor": 2, "a8w8_block": 3, "a8w8_quant": 4,
+             "bf16_packed": 5, "gated_packed": 6, "fp8_tensor_packed": 7, "a8w8_block_packed": 8,
+             "a8w8_quant_packed": 9}
     for k in sorted(by_key, key=lambda k: (order[k[0]], k[2], k[3], k[1])):
         slot = by_key[k]
         default = next(iter(slot.values()))["default"]
@@ -250,7 +267,8 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="mode", required=True)
     t = sub.add_parser("tune")
     t.add_argument("--store", required=True)
-    t.add_argument("--ops", default="bf16,gated,fp8_tensor,a8w8_block,a8w8_quant")
+    t.add_argument("--ops", default="bf16,gated,fp8_tensor,a8w8_block,a8w8_quant,bf16_packed,gated_packed,"
+                                    "fp8_tensor_packed,a8w8_block_packed,a8w8_quant_packed")
     t.add_argument("--quick", action="store_true")
     t.add_argument("--rotation-gib", type=float, default=1.0)
     t.add_argument("--only-m", default="")

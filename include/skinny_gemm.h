@@ -23,6 +23,11 @@
  *                           (the same page leaves that fusion open in
  *                           "Rejected paths")
  *
+ * and each of the five with the weight pre-shuffled once into a fragment-
+ * packed layout (skinny_gemm_pack_weight, then skinny_gemm_<form>_packed):
+ * the A8W8 table the decode page tunes is the one for its pre-shuffled
+ * ("bpreshuffle") weight (Decode optimization round 3, "Retained change 2").
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * Memory.   Every tensor argument is a DEVICE pointer to caller-owned memory,
@@ -83,6 +88,13 @@ typedef int skg_status;
 #define SKG_OP_FP8_TENSOR 2
 #define SKG_OP_A8W8_BLOCK 3
 #define SKG_OP_A8W8_QUANT 4
+/* The same five forms with a fragment-packed weight: SKG_OP_PACKED + the form. */
+#define SKG_OP_PACKED 5
+#define SKG_OP_BF16_PACKED 5
+#define SKG_OP_GATED_PACKED 6
+#define SKG_OP_FP8_TENSOR_PACKED 7
+#define SKG_OP_A8W8_BLOCK_PACKED 8
+#define SKG_OP_A8W8_QUANT_PACKED 9
 
 /* y[M,N] = x[M,K] . W[N,K]^T.  x, W: bf16.  scales: unused, may be NULL. */
 skg_status skinny_gemm_bf16(const void* x, const void* W, const float* scales,
@@ -126,6 +138,52 @@ skg_status skinny_gemm_a8w8_block_quant(const void* x, const void* W, const floa
                                         float* x_scales_out, void* y, int M, int N, int K,
                                         hipStream_t stream);
 
+/* ---- Fragment-packed weights -------------------------------------------
+ * The weight of form `op` (SKG_OP_BF16 .. SKG_OP_A8W8_QUANT; a packed op id
+ * means its form), laid out once so that every 16-byte load of the MFMA tile
+ * kernels is one lane's operand and a wave's load is 1 KiB of contiguous
+ * bytes.  With WB bytes per weight element (2 for bf16, 1 for e4m3fn), G = 2
+ * for the gated form (gate rows, then up rows) else 1, NC = ceil(K*WB/128)
+ * chunks of 128 bytes along each row and N16 = ceil(N/16) blocks of 16 rows:
+ *   the 2048-byte unit of chunk c, group g, block b starts at byte
+ *   ((c*G + g)*N16 + b) * 2048 (chunk-major: the blocks of one chunk are
+ *   contiguous); its 16 bytes at 1024*h + 16*l (h = 0, 1; l = 0..63) hold
+ *   row 16*b + l%16 of group g, row bytes 128*c + off .. +15, where with
+ *   q = l/16, off = 32*q + 16*h for the fp8_tensor form and 64*h + 16*q for
+ *   the others; bytes of rows >= N or past the row (K*WB) are zero.
+ * Scales keep their row-major layouts.  Results equal those of the row-major
+ * form up to float32 summation order (bit-identical run to run). */
+
+/* Bytes of the packed weight of form `op` with N rows (per half for the gated
+ * form) and K columns; 0 for an unknown op, N or K <= 0, or a K that is not a
+ * multiple of the form's K multiple. */
+size_t skinny_gemm_packed_weight_bytes(int op, int N, int K);
+
+/* Write the packed copy of the row-major weight W (as the form's row-major
+ * entry point takes it: [N, K], or [2N, K] for gated) into W_packed (device,
+ * skinny_gemm_packed_weight_bytes(op, N, K) bytes, 16-byte aligned, must not
+ * overlap W), ordered on `stream`.  W is only read.  N == 0 or K == 0 is a
+ * no-op. */
+skg_status skinny_gemm_pack_weight(int op, const void* W, void* W_packed, int N, int K,
+                                   hipStream_t stream);
+
+/* The five forms with a packed weight: the arguments, result and errors of
+ * the row-major entry point of the same name without "_packed", with
+ * W_packed written by skinny_gemm_pack_weight for that form, N and K.  Served
+ * by the MFMA tile kernels only. */
+skg_status skinny_gemm_bf16_packed(const void* x, const void* W_packed, const float* scales,
+                                   void* y, int M, int N, int K, hipStream_t stream);
+skg_status skinny_gemm_gated_packed(const void* x, const void* W_packed, const float* scales,
+                                    void* y, int M, int N, int K, hipStream_t stream);
+skg_status skinny_gemm_fp8_tensor_packed(const void* x, const void* W_packed, const float* scales,
+                                         void* y, int M, int N, int K, hipStream_t stream);
+skg_status skinny_gemm_a8w8_block_packed(const void* x, const void* W_packed, const float* x_scales,
+                                         const float* w_scales, void* y, int M, int N, int K,
+                                         hipStream_t stream);
+skg_status skinny_gemm_a8w8_block_quant_packed(const void* x, const void* W_packed,
+                                               const float* w_scales, float* x_scales_out, void* y,
+                                               int M, int N, int K, hipStream_t stream);
+
 /* Text of the calling thread's last non-OK status ("" if none). */
 const char* skinny_gemm_last_error(void);
 
@@ -168,7 +226,8 @@ int skinny_gemm_variant_supports(int op, int variant, int M);
 /* Run one named variant, bypassing the table (tuner and tests).  s0/s1 are the
  * op's scale arrays (fp8_tensor: s0 = w_scale; a8w8: s0 = x_scales,
  * s1 = w_scales; a8w8_quant: s0 = x_scales_out (written, may be NULL),
- * s1 = w_scales; others NULL).  knobs: reserved, pass NULL. */
+ * s1 = w_scales; others NULL); a packed op takes its form's arrays and the
+ * packed weight as W.  knobs: reserved, pass NULL. */
 skg_status skinny_gemm_run_variant(int op, int variant, const int* knobs,
                                    const void* x, const void* W, const float* s0,
                                    const float* s1, void* y, int M, int N, int K,

@@ -60,6 +60,29 @@ def run(p, dev=None, variant=None, y=None):
     return skg.skinny_gemm_a8w8_block(x, w, s0, s1, y=y)
 
 
+def to_device_packed(p):
+    """Device tensors (x, W_packed, s0, s1) of a synth.Problem, the weight
+    packed by the library for the problem's form."""
+    x, w, s0, s1 = to_device(p)
+    return x, skg.skinny_gemm_pack_weight(p.kind, w), s0, s1
+
+
+def run_packed(p, dev=None, variant=None, y=None):
+    """Run the packed form of problem p (dispatch, or one variant)."""
+    x, wp, s0, s1 = dev if dev is not None else to_device_packed(p)
+    if variant is not None:
+        return skg.skinny_gemm_run_variant(p.kind + "_packed", variant, x, wp, s0, s1, y=y)
+    if p.kind == "bf16":
+        return skg.skinny_gemm_bf16_packed(x, wp, y=y)
+    if p.kind == "gated":
+        return skg.skinny_gemm_gated_packed(x, wp, y=y)
+    if p.kind == "fp8_tensor":
+        return skg.skinny_gemm_fp8_tensor_packed(x, wp, s0, y=y)
+    if p.kind == "a8w8_quant":
+        return skg.skinny_gemm_a8w8_block_quant_packed(x, wp, s1, x_scales=s0, y=y)
+    return skg.skinny_gemm_a8w8_block_packed(x, wp, s0, s1, y=y)
+
+
 def reference(p, cols=None) -> np.ndarray:
     if p.kind == "bf16":
         return oracle.linear_bf16(p.x, p.w, cols=cols)

@@ -179,34 +179,47 @@ def test_defaults_follow_the_rows_rule():
     q = lambda op, M, N, K: skg.skinny_gemm_query(op, M, N, K)[0]
     for op in skg.OPS:
         for M in (1, 2, 3):
-            if op != "a8w8_quant":      # x quantised in the call: tile kernels only
+            if op == "a8w8_quant_packed":
+                assert q(op, M, 4096, 4096).startswith("tlds_f1_s"), (op, M)
+            elif op.endswith("_packed"):  # packed weight, few rows: direct x
+                assert q(op, M, 4096, 4096).startswith("tlds_d_"), (op, M)
+            elif op not in ("a8w8_quant", "a8w8_block"):   # A8W8: the LDS tile from one row
                 assert q(op, M, 4096, 4096).startswith("gemv_"), (op, M)
+            else:
+                assert q(op, M, 4096, 4096).startswith("tlds_"), (op, M)
         for M in (16, 24, 32, 64, 96, 128, 129, 1000):
             assert q(op, M, 4096, 4096).startswith("tlds_"), (op, M)
+    for M in (64, 96, 128):     # packed weight, many rows: x through LDS
+        assert not q("bf16_packed", M, 4096, 4096).startswith("tlds_d_"), M
     for M in (1, 2, 3, 4, 8, 16, 64, 128, 300):
         assert q("a8w8_quant", M, 8192, 4096).startswith("tlds_"), M
         assert q("a8w8_quant", M, 32768, 1024).startswith("tlds_"), M
-    assert q("bf16", 4, 4096, 4096).startswith("gemv_")
+    assert q("bf16", 4, 2048, 2048).startswith("gemv_")
     assert q("fp8_tensor", 4, 248320, 4096).startswith("tlds_")
     assert q("a8w8_block", 4, 8192, 4096).startswith("tlds_")
-    for M in (4, 6, 8):         # small weights stay on the VALU stream up to 8 rows
+    for M in (4, 6):            # small weights stay on the VALU stream up to 6 rows
         assert q("bf16", M, 1024, 1024).startswith("gemv_"), M
         assert q("bf16", M, 2048, 2048).startswith("gemv_"), M
-    for M in (12, 16, 32, 64, 128):
-        assert q("bf16", M, 1024, 1024).startswith("tlds_k4_"), M
+    for M in (8, 12, 16, 32, 64):   # then direct x with K split over the waves
+        assert q("bf16", M, 1024, 1024) == "tlds_d_k4_f1_s1_p4_m1", M
+    assert q("bf16", 128, 1024, 1024).startswith("tlds_k4_")
+    for M in (4, 6):            # large rows: direct x over eight waves
+        assert q("bf16", M, 4096, 4096) == "tlds_d_w8_k8_f1_s1_p4_m2", M
+        assert q("bf16", M, 4096, 12288) == "tlds_d_w8_k8_f1_s1_p4_m2", M
     assert q("bf16", 128, 2048, 2048) == "tlds_w8_k4_f1_s1_p4_m2"
     # GEMV shape: two rows per wave for one x row, eight for a vocabulary N,
     # one wave per row (no K split) for rows under 2 KiB
     assert q("bf16", 1, 4096, 4096) == "gemv_r2_k4_p1"
     assert q("bf16", 3, 4096, 4096) == "gemv_r4_k4_p1"
     assert q("fp8_tensor", 2, 248320, 4096) == "gemv_r8_k4_p1"
-    assert q("a8w8_block", 1, 32768, 1024) == "gemv_r4_k1_p2"
+    assert q("a8w8_block", 1, 32768, 1024) == "tlds_f1_s1_p4_m2"
+    assert q("a8w8_block", 1, 8192, 4096) == "tlds_d_w8_k8_f1_s1_p4_m2"
     # in-workgroup K split where the 16-row tiles come in multiples of 256
     assert q("bf16", 8, 4096, 4096) == "tlds_k4_f1_s1_p4_m2"
     assert q("gated", 16, 12288, 4096) == "tlds_k4_f1_s1_p4_m2"
-    assert q("a8w8_block", 8, 8192, 4096) == "tlds_k4_f1_s1_p4_m2"
+    assert q("a8w8_block", 8, 8192, 4096) == "tlds_w8_k4_f1_s1_p4_m2"
     assert q("bf16", 8, 6144, 4096) == "tlds_f1_s4_p4"            # 384 tiles: split across workgroups
-    assert q("a8w8_block", 8, 32768, 1024) == "tlds_f1_s1_p4"     # 1 KiB rows
+    assert q("a8w8_block", 8, 32768, 1024) == "tlds_f1_s1_p4_m2"  # 1 KiB rows
     # K split across workgroups: 4 up to 8192 weight rows, 2 up to 16384, else 1
     assert q("bf16", 32, 4096, 12288) == "tlds_f1_s4_p4"
     assert q("bf16", 64, 4096, 12288) == "tlds_f1_s4_p4_m4"

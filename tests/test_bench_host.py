@@ -12,25 +12,30 @@ import gemv_skinny_gemm_02_amd as skg
     ("gemv_r2_k4_p1", 1, "void skg::gemv_kernel<0, 1, 2, 4, 1>(skg::Args)"),
     ("gemv_r4_k1_p2", 7, "void skg::gemv_kernel<0, 8, 4, 1, 2>(skg::Args)"),
     ("tile_f1_k4_p4", 24, "void skg::tile_kernel<0, 2, 1, 4, 4>(skg::Args)"),
-    ("tlds_f1_s4_p4", 16, "void skg::tlds_kernel<0, 1, 1, 4, 4, 4, 1>(skg::Args)"),
-    ("tlds_f1_s4_p4", 128, "void skg::tlds_kernel<0, 8, 1, 4, 4, 4, 1>(skg::Args)"),
-    ("tlds_f1_s4_p4_m2", 128, "void skg::tlds_kernel<0, 2, 1, 4, 4, 4, 1>(skg::Args)"),
-    ("tlds_w8_f1_s4_p4_m4", 96, "void skg::tlds_kernel<0, 4, 1, 4, 4, 8, 1>(skg::Args)"),
-    ("tlds_k4_f1_s1_p4_m1", 64, "void skg::tlds_kernel<0, 1, 1, 1, 4, 4, 4>(skg::Args)"),
-    ("tlds_w8_k8_f1_s1_p2_m1", 128, "void skg::tlds_kernel<0, 1, 1, 1, 2, 8, 8>(skg::Args)"),
-    ("tlds_f1_s4_p4", 40, "void skg::tlds_kernel<0, 4, 1, 4, 4, 4, 1>(skg::Args)"),   # 3 fragments -> the 4 build
+    ("tlds_f1_s4_p4", 16, "void skg::tlds_kernel<0, 1, 1, 4, 4, 4, 1, 0>(skg::Args)"),
+    ("tlds_f1_s4_p4", 128, "void skg::tlds_kernel<0, 8, 1, 4, 4, 4, 1, 0>(skg::Args)"),
+    ("tlds_f1_s4_p4_m2", 128, "void skg::tlds_kernel<0, 2, 1, 4, 4, 4, 1, 0>(skg::Args)"),
+    ("tlds_w8_f1_s4_p4_m4", 96, "void skg::tlds_kernel<0, 4, 1, 4, 4, 8, 1, 0>(skg::Args)"),
+    ("tlds_k4_f1_s1_p4_m1", 64, "void skg::tlds_kernel<0, 1, 1, 1, 4, 4, 4, 0>(skg::Args)"),
+    ("tlds_w8_k8_f1_s1_p2_m1", 128, "void skg::tlds_kernel<0, 1, 1, 1, 2, 8, 8, 0>(skg::Args)"),
+    ("tlds_f1_s4_p4", 40, "void skg::tlds_kernel<0, 4, 1, 4, 4, 4, 1, 0>(skg::Args)"),   # 3 fragments -> the 4 build
+    ("tlds_d_k4_f1_s1_p4_m1", 4, "void skg::tlds_kernel<0, 1, 1, 1, 4, 4, 4, 1>(skg::Args)"),
+    ("tlds_d_w8_k8_f1_s1_p4_m2", 32, "void skg::tlds_kernel<0, 2, 1, 1, 4, 8, 8, 1>(skg::Args)"),
 ])
 def test_kernel_symbol(variant, M, symbol):
     assert bench.kernel_symbol(variant, M) == symbol
 
 
 def test_every_variant_name_parses():
-    for i, name in enumerate(skg.variants("bf16")):
-        for M in (1, 16, 128):
-            if not skg.skinny_gemm_variant_supports("bf16", i, M):
-                continue
-            sym = bench.kernel_symbol(name, M)
-            assert sym.startswith("void skg::") and sym.endswith("(skg::Args)")
+    for op in ("bf16", "bf16_packed"):
+        for i, name in enumerate(skg.variants(op)):
+            for M in (1, 16, 128):
+                if not skg.skinny_gemm_variant_supports(op, i, M):
+                    continue
+                sym = bench.kernel_symbol(name, M, skg.OPS[op])
+                assert sym.startswith("void skg::") and sym.endswith("(skg::Args)")
+                if name.startswith("tlds"):
+                    assert sym.endswith(f", {1 if name.startswith('tlds_d_') else 0}>(skg::Args)"), (name, sym)
 
 
 def test_read_counters(tmp_path, monkeypatch):

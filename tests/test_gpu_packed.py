@@ -1,0 +1,145 @@
+"""The fragment-packed weight on the GPU: the bytes the pack call writes
+against the layout the header defines (restated here in numpy), and every
+packed variant, the packed dispatch and the full workload shapes against the
+CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import gemv_skinny_gemm_02_amd as skg
+import oracle
+import synth
+from gpu_util import (assert_parity, dev_bf16, dev_fp8, host_bits, reference, run, run_packed, say, to_device,
+                      to_device_packed)
+
+pytestmark = pytest.mark.gpu
+
+MAKE = {"bf16": synth.make_bf16, "gated": synth.make_gated,
+        "fp8_tensor": synth.make_fp8_tensor, "a8w8_block": synth.make_a8w8_block,
+        "a8w8_quant": synth.make_a8w8_quant}
+
+
+def _small_shape(kind):
+    return (257, 1040) if kind in ("fp8_tensor", "a8w8_block", "a8w8_quant") else (257, 1032)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    skg.load()
+
+
+def layout(w: np.ndarray, kind: str, N: int, K: int) -> np.ndarray:
+    """The packed bytes of row-major weight bytes w [G*N, K*WB], as the header
+    defines them: unit (c, g, b) of 2048 bytes at ((c*G + g)*N16 + b)*2048; its
+    16 bytes at 1024h + 16l are row 16b + l%16 of group g, row bytes
+    128c + off .. +15, off = 32q + 16h (fp8_tensor) or 64h + 16q (q = l/16);
+    zero past the rows and past the row."""
+    G = 2 if kind == "gated" else 1
+    rowb = w.shape[1]
+    NC, N16 = -(-rowb // 128), -(-N // 16)
+    pad = np.zeros((G, N16 * 16, NC * 128), np.uint8)
+    pad[:, :N, :rowb] = w.reshape(G, N, rowb)
+    c, g, b, h, l, e = np.ix_(np.arange(NC), np.arange(G), np.arange(N16), np.arange(2), np.arange(64),
+                              np.arange(16))
+    q = l // 16
+    off = 32 * q + 16 * h if kind == "fp8_tensor" else 64 * h + 16 * q
+    return pad[g, 16 * b + l % 16, 128 * c + off + e].reshape(-1)
+
+
+@pytest.mark.parametrize("kind", list(MAKE))
+def test_pack_layout(kind):
+    for (N, K) in [(37, 272), (256, 1024), (130, 16 if kind != "bf16" and kind != "gated" else 8)]:
+        p = MAKE[kind](1, N, K, seed=5)
+        x, w, _, _ = to_device(p)
+        nbytes = skg.skinny_gemm_packed_weight_bytes(kind, N, K)
+        G = 2 if kind == "gated" else 1
+        WB = 2 if kind in ("bf16", "gated") else 1
+        assert nbytes == -(-K * WB // 128) * G * -(-N // 16) * 2048
+        say(f"pack {kind} N={N} K={K} -> {nbytes} bytes")
+        wp = skg.skinny_gemm_pack_weight(kind, w)
+        torch.cuda.synchronize()
+        got = wp.data.cpu().numpy()
+        want = layout(w.cpu().view(torch.uint8).numpy().reshape(G * N, K * WB), kind, N, K)
+        assert got.shape == want.shape and np.array_equal(got, want), kind
+
+
+@pytest.mark.parametrize("kind", list(MAKE))
+def test_every_packed_variant_small(kind):
+    N, K = _small_shape(kind)
+    op = kind + "_packed"
+    names = skg.variants(op)
+    for M in (1, 2, 3, 5, 8, 12, 16, 17, 40, 128):
+        p = MAKE[kind](M, N, K, seed=1)
+        dev = to_device_packed(p)
+        ref = reference(p)
+        ran = 0
+        for i, name in enumerate(names):
+            if not skg.skinny_gemm_variant_supports(op, i, M):
+                continue
+            say(f"{op} M={M} N={N} K={K} variant={name}")
+            y = run_packed(p, dev, variant=name)
+            torch.cuda.synchronize()
+            assert_parity(host_bits(y), ref, f"{op} {name} M={M}")
+            ran += 1
+        assert ran > 0, f"no variant runs {op} at M={M}"
+
+
+@pytest.mark.parametrize("kind", list(MAKE))
+def test_packed_dispatch_ragged(kind):
+    """Default dispatch of the packed form over M buckets and M past 128, ragged
+    N and K; the x scales the quantising form hands out are those of the
+    row-major form."""
+    for (N, K) in [(129, 256), (1000, 2064), (64, 4096)]:
+        for M in (1, 4, 6, 7, 13, 24, 33, 96, 130, 200):
+            p = MAKE[kind](M, N, K, seed=2)
+            say(f"{kind}_packed dispatch M={M} N={N} K={K} -> {skg.skinny_gemm_query(kind + '_packed', M, N, K)}")
+            dev = to_device_packed(p)
+            y = run_packed(p, dev)
+            torch.cuda.synchronize()
+            assert_parity(host_bits(y), reference(p), f"{kind}_packed dispatch M={M} N={N} K={K}")
+            if kind == "a8w8_quant":
+                xs_packed = dev[2].clone()
+                d2 = to_device(p)
+                run(p, d2)
+                torch.cuda.synchronize()
+                assert torch.equal(xs_packed.view(torch.int32), d2[2].view(torch.int32))
+
+
+def test_packed_full_shapes():
+    """The bf16 sweep shapes and both A8W8 shapes at full size through the packed
+    dispatch, sampled columns."""
+    for (N, K) in synth.SWEEP_NK:
+        base = synth.make_bf16(128, N, K, seed=0)
+        wp = skg.skinny_gemm_pack_weight("bf16", dev_bf16(base.w))
+        for M in (1, 4, 8, 16, 64, 128):
+            x = dev_bf16(base.x[:M])
+            say(f"bf16_packed M={M} N={N} K={K} -> {skg.skinny_gemm_query('bf16_packed', M, N, K)}")
+            y = skg.skinny_gemm_bf16_packed(x, wp)
+            torch.cuda.synchronize()
+            cols = synth.rows_of(N, 64, seed=M)
+            ref = oracle.linear_bf16(base.x[:M], base.w, cols=cols)
+            assert_parity(host_bits(y)[:, cols], ref, f"bf16_packed M={M} N={N} K={K}")
+    for (N, K) in synth.A8W8_NK:
+        for M in (1, 16, 64):
+            p = synth.make_a8w8_block(M, N, K, seed=0)
+            say(f"a8w8_block_packed M={M} N={N} K={K}")
+            y = run_packed(p)
+            torch.cuda.synchronize()
+            cols = synth.rows_of(N, 64, seed=M)
+            assert_parity(host_bits(y)[:, cols], reference(p, cols=cols), f"a8w8_block_packed M={M} N={N} K={K}")
+
+
+def test_pack_refusals():
+    w = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
+    lib = skg.load()
+    n = skg.skinny_gemm_packed_weight_bytes("bf16", 64, 256)
+    buf = torch.zeros(n + 64, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    assert lib.skinny_gemm_pack_weight(0, w.data_ptr(), buf.data_ptr(), 64, 256, s) == 0
+    assert lib.skinny_gemm_pack_weight(0, w.data_ptr(), buf.data_ptr() + 8, 64, 256, s) == 2      # alignment
+    assert lib.skinny_gemm_pack_weight(0, w.data_ptr(), w.data_ptr(), 64, 256, s) == 1            # overlap
+    assert lib.skinny_gemm_pack_weight(0, w.data_ptr(), buf.data_ptr(), 64, 252, s) == 2          # K multiple
+    assert lib.skinny_gemm_pack_weight(17, w.data_ptr(), buf.data_ptr(), 64, 256, s) == 1         # op
+    assert skg.skinny_gemm_packed_weight_bytes("bf16", 64, 252) == 0
