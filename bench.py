@@ -14,6 +14,9 @@ its weight from HBM, not from the 256 MB Infinity Cache.  Steps are replayed
 from HIP graphs, eight steps per graph.  The dominant kernel's launches of
 those steps are grouped in their own graph and bracketed by HIP events on the
 launch stream, which gives its live average duration for the roofline figure.
+Beside the nominal peaks it reports what a kernel can reach on the device: the
+fastest plain read of each shape's rotated weight copies and the rate of a
+register-only bf16 MFMA loop (the library's measurement kernels).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -225,6 +228,62 @@ def measure_step(args, torch, skg, calls, Ms, stream, launch, op, step_bytes):
             "rough_us": rough_us, "ms_step": ms_step, "dom_us": dom_us, "value": value}
 
 
+def _graph_us(torch, stream, n, enqueue, replays):
+    """Median µs per launch of a graph of n launches enqueue(i)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            enqueue(i)
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(max(1, replays)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3 / n)
+    del g
+    return statistics.median(ts)
+
+
+def measure_ceilings(args, torch, skg, shapes, wp_dev, stream):
+    """What a kernel can reach here: per weight size, the fastest plain read of
+    the same rotated weight copies (the library's read-stream kernel, graph
+    replay as for the calls, best of three grid sizes); and the bf16 MFMA rate
+    of a register-only MFMA loop on every CU."""
+    sink = torch.empty(256, dtype=torch.int32, device="cuda")
+    read = {}
+    for (N, K) in shapes:
+        bufs = [w.data for w in wp_dev[(N, K)]]
+        R = len(bufs)
+        n = max(args.per_call_min, 2 * R)
+        best = None
+        for grid in (512, 1024, 2048):
+            us = _graph_us(torch, stream, n, lambda i: skg.skinny_gemm_calib_read(bufs[i % R], grid, sink),
+                           args.per_call_replays)
+            if best is None or us < best[0]:
+                best = (us, grid)
+        nbytes = bufs[0].numel()
+        read[(N, K)] = {"bytes": nbytes, "us": round(best[0], 3), "GB/s": round(nbytes / (best[0] * 1e-6) / 1e9, 1),
+                        "grid": best[1]}
+    grid, iters = 8 * 256, 2048
+    flops = skg.skinny_gemm_calib_mfma(grid, iters, sink)       # warm-up
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        skg.skinny_gemm_calib_mfma(grid, iters, sink)
+        b.record(stream)
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    mfma_tflops = flops / min(ts) / 1e12
+    log("read ceilings:", {f"{N}x{K}": v["us"] for (N, K), v in read.items()}, f"| mfma bf16 {mfma_tflops:.0f} TFLOP/s")
+    return {"read": read, "mfma_bf16_tflops": mfma_tflops}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,6 +396,9 @@ def main() -> int:
             per_call_us[c] = statistics.median(ts)
             del g
 
+    # ------------------------------------ achievable ceilings on this device
+    ceil = measure_ceilings(args, torch, skg, shapes, wp_dev, stream)
+
     # --------------------------- a copy of known size (counter calibration)
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -348,6 +410,9 @@ def main() -> int:
     # ------------------------------------------------------------ report
     dom_bytes = sum(alg_bytes(*c) for c in dom_calls) / len(dom_calls)
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    # the same launch mix at each shape's read ceiling (weight bytes read alone)
+    dom_ceil_us = sum(ceil["read"][(N, K)]["us"] for (_, N, K) in dom_calls) / len(dom_calls)
+    achievable = dom_bytes / (dom_ceil_us * 1e-6) / 1e9
     code_hash = lib_code_hash()
     traffic = read_counters(dominant, code_hash)
     detail = {}
@@ -359,7 +424,9 @@ def main() -> int:
             gbs = alg_bytes(*c) / (us * 1e-6) / 1e9
             tfl = 2 * M * N * K / (us * 1e-6) / 1e12
             row[f"{N}x{K}"] = {"us": round(us, 2), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
-                               "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4), "variant": choice[c][0]}
+                               "read_ceiling_frac": round(ceil["read"][(N, K)]["us"] / us, 3),
+                               "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+                               "mfma_ceiling_frac": round(tfl / ceil["mfma_bf16_tflops"], 4), "variant": choice[c][0]}
         detail[f"M={M}"] = row
     all_calls = {f"{M}x{N}x{K}": round(per_call_us[(M, N, K)], 2) for (M, N, K) in calls}
 
@@ -388,7 +455,13 @@ def main() -> int:
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": round(traffic) if traffic is not None else None,
                      "kernel": dominant, "launches_per_step": len(dom_calls), "avg_launch_us": round(dom_us, 3),
-                     "alg_bytes_per_launch": round(dom_bytes), "code_hash": code_hash},
+                     "alg_bytes_per_launch": round(dom_bytes), "code_hash": code_hash,
+                     "achievable": {"GB/s": round(achievable, 1), "frac": round(achieved / achievable, 4),
+                                    "basis": "the same launches at each shape's plain-read time of its weight "
+                                             "(skinny_gemm_calib_read, graph replay, best grid)"}},
+        "ceilings": {"read": {f"{N}x{K}": v for (N, K), v in ceil["read"].items()},
+                     "mfma_bf16_tflops": round(ceil["mfma_bf16_tflops"], 1),
+                     "mfma_bf16_frac_of_peak": round(ceil["mfma_bf16_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)},
         "per_m": detail,
         "per_call_us": all_calls,
     }

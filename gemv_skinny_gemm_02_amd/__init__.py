@@ -33,6 +33,7 @@ __all__ = [
     "skinny_gemm_run_variant", "skinny_gemm_query", "skinny_gemm_load_table", "skinny_gemm_load_table_as",
     "skinny_gemm_identity", "skinny_gemm_table_status", "skinny_gemm_num_variants",
     "skinny_gemm_variant_name", "skinny_gemm_variant_supports", "variants", "default_table_path",
+    "skinny_gemm_calib_read", "skinny_gemm_calib_mfma", "CALIB_MFMA_FLOPS_PER_ITER_WG",
 ]
 
 OPS = {"bf16": 0, "gated": 1, "fp8_tensor": 2, "a8w8_block": 3, "a8w8_quant": 4,
@@ -114,6 +115,10 @@ def load() -> ctypes.CDLL:
         lib.skinny_gemm_variant_supports.restype = i
         lib.skinny_gemm_run_variant.argtypes = [i, i, vp, vp, vp, fp, fp, vp, i, i, i, vp]
         lib.skinny_gemm_run_variant.restype = i
+        lib.skinny_gemm_calib_read.argtypes = [vp, ctypes.c_size_t, i, vp, vp]
+        lib.skinny_gemm_calib_read.restype = i
+        lib.skinny_gemm_calib_mfma.argtypes = [i, i, vp, vp]
+        lib.skinny_gemm_calib_mfma.restype = i
         _LIB = lib
         return lib
 
@@ -396,3 +401,33 @@ def skinny_gemm_variant_supports(op, i: int, M: int) -> bool:
 
 def variants(op=0) -> list:
     return [skinny_gemm_variant_name(op, i) for i in range(skinny_gemm_num_variants(op))]
+
+
+# ------------------------------------------------------ measurement helpers
+CALIB_MFMA_FLOPS_PER_ITER_WG = 4 * 8 * 32768   # 4 waves x 8 MFMA 32x32x16 per round
+
+
+def _sink(sink, like_device):
+    if sink is None:
+        sink = torch.empty(256, dtype=torch.int32, device=like_device)
+    if sink.dtype != torch.int32 or sink.numel() < 256 or not sink.is_cuda or not sink.is_contiguous():
+        raise ValueError("sink must be a contiguous int32 device tensor of at least 256 words")
+    return sink
+
+
+def skinny_gemm_calib_read(buf: torch.Tensor, grid: int, sink=None, stream=None) -> None:
+    """Read every byte of the contiguous device tensor `buf` once with `grid`
+    workgroups (a measurement kernel: it computes nothing of the linear)."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    sink = _sink(sink, buf.device)
+    _check(load().skinny_gemm_calib_read(buf.data_ptr(), buf.numel() * buf.element_size(), int(grid),
+                                         sink.data_ptr(), _stream(stream)))
+
+
+def skinny_gemm_calib_mfma(grid: int, iters: int, sink=None, stream=None) -> int:
+    """Run grid * iters rounds of 4 waves x 8 bf16 MFMA (a measurement kernel);
+    returns the flops it issues."""
+    sink = _sink(sink, torch.device("cuda", torch.cuda.current_device()))
+    _check(load().skinny_gemm_calib_mfma(int(grid), int(iters), sink.data_ptr(), _stream(stream)))
+    return int(grid) * int(iters) * CALIB_MFMA_FLOPS_PER_ITER_WG

@@ -48,6 +48,7 @@ struct Args {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -1332,5 +1333,10 @@ template <> const TileRow* tlds_table<OP_PACKED + OP_A8W8Q>();
 // Writes the fragment-packed copy of W [G*N, K] (G = 2 for the gated form)
 // for op into Wp (packed_weight_bytes(op, N, K) bytes), on stream s.
 hipError_t launch_pack(int op, const void* W, void* Wp, int N, int K, hipStream_t s);
+
+// Measurement kernels (calib.hip): a read stream of n16 16-byte pieces over
+// `grid` workgroups, and `iters` rounds of 8 bf16 32x32x16 MFMA chains per wave.
+hipError_t launch_calib_read(const void* buf, unsigned long long n16, int grid, unsigned* sink, hipStream_t s);
+hipError_t launch_calib_mfma(int grid, int iters, unsigned* sink, hipStream_t s);
 
 }  // namespace skg

@@ -233,6 +233,30 @@ skg_status skinny_gemm_run_variant(int op, int variant, const int* knobs,
                                    const float* s1, void* y, int M, int N, int K,
                                    hipStream_t stream);
 
+/* Measurement helpers.  They compute nothing of the linear: they give the
+ * rates a kernel on this device can reach, against which the linear's
+ * kernels are reported (the pages report decode-GEMM rates against the
+ * device's bandwidth: Decode optimization round 3, "Retained change 2").
+ *
+ * skinny_gemm_calib_read: one launch of `grid` workgroups of 256 threads
+ * that read every byte of buf[0, bytes) once with 16-byte non-temporal loads
+ * (each workgroup one contiguous slice, 8 loads per thread in flight).  buf
+ * is device memory, 16-byte aligned, bytes a nonzero multiple of 16; grid in
+ * 1..65536.  sink is 256 device words that the kernel writes only if the
+ * words it read fold (xor) to one NaN pattern, so callers ignore its value.
+ *
+ * skinny_gemm_calib_mfma: one launch of `grid` workgroups of 4 waves, each
+ * wave issuing iters x 8 v_mfma_f32_32x32x16_bf16 (32768 flops each) on
+ * register operands: grid * 4 * iters * 8 * 32768 flops.  grid in 1..65536,
+ * iters in 1..2^20; sink as above.
+ *
+ * Both are stream-ordered, allocate nothing and return the usual statuses
+ * (EINVAL for sizes out of range and host or short buffers, EUNSUPPORTED for
+ * misalignment, ELAUNCH). */
+skg_status skinny_gemm_calib_read(const void* buf, size_t bytes, int grid, unsigned* sink,
+                                  hipStream_t stream);
+skg_status skinny_gemm_calib_mfma(int grid, int iters, unsigned* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
