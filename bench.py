@@ -284,6 +284,47 @@ def measure_ceilings(args, torch, skg, shapes, wp_dev, stream):
     return {"read": read, "mfma_bf16_tflops": mfma_tflops}
 
 
+def measure_mid_m(args, torch, skg, synth, shapes, wp_dev, stream, ceil):
+    """Mid-M rows (speculative verification and drafting) on the sweep shapes:
+    µs per call of the packed form through table dispatch, graph replay over
+    the same rotated weight copies as the step.  As context, the vendor GEMM
+    (torch.nn.functional.linear, hipBLASLt) timed the same way on the same
+    buffers read as row-major [N, K] bf16 weights: its speed does not depend on
+    the values, so no further copies are needed."""
+    import torch.nn.functional as F
+    out = {}
+    Mmax = max(synth.MID_M)
+    for (N, K) in shapes:
+        x = torch.from_numpy(synth.make_bf16(Mmax, 16, K, seed=0).x.view(np.int16)).view(torch.bfloat16).cuda()
+        ws = wp_dev[(N, K)]
+        R = len(ws)
+        n = max(args.per_call_min, 2 * R)
+        rm = [w.data.view(torch.bfloat16).view(N, K) for w in ws]
+        row = {}
+        for M in synth.MID_M:
+            xm = x[:M]
+            y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            ours = _graph_us(torch, stream, n, lambda i: skg.skinny_gemm_bf16_packed(xm, ws[i % R], y=y),
+                             args.per_call_replays)
+            torch.mm(xm, rm[0].t(), out=y)           # the vendor library sets itself up outside capture
+            torch.cuda.synchronize()
+            vendor = _graph_us(torch, stream, n, lambda i: torch.mm(xm, rm[i % R].t(), out=y), args.per_call_replays)
+            nbytes = alg_bytes(M, N, K)
+            tfl = 2 * M * N * K / (ours * 1e-6) / 1e12
+            floor_us = max(ceil["read"][(N, K)]["us"], 2 * M * N * K / (ceil["mfma_bf16_tflops"] * 1e12) * 1e6)
+            row[str(M)] = {"us": round(ours, 2), "GB/s": round(nbytes / (ours * 1e-6) / 1e9, 1),
+                           "TFLOP/s": round(tfl, 1), "hbm_frac": round(nbytes / (ours * 1e-6) / 1e9 / HBM_PEAK_GBS, 3),
+                           "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+                           "ceiling_frac": round(floor_us / ours, 3),
+                           "variant": skg.skinny_gemm_query("bf16_packed", M, N, K)[0],
+                           "vendor_us": round(vendor, 2)}
+        out[f"{N}x{K}"] = row
+        log(f"mid-M {N}x{K}:", {m: (v["us"], v["vendor_us"]) for m, v in row.items()})
+    return {"rows": list(synth.MID_M), "form": "bf16_packed, table dispatch", "shapes": out,
+            "ceiling": "max(read time of the weight, flops at the MFMA-loop rate)",
+            "vendor": "torch.mm (hipBLASLt), bf16, same rotated buffers, graph replay: context only"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -297,6 +338,7 @@ def main() -> int:
                     help="skip the per-call graph timings (profiling runs: keeps every dispatch of a kernel "
                          "in the step's shape mix)")
     ap.add_argument("--per-call-min", type=int, default=64, help="min launches per per-call graph")
+    ap.add_argument("--no-mid-m", action="store_true", help="skip the mid-M rows (144..512) report")
     ap.add_argument("--no-row-major", action="store_true",
                     help="skip the row-major step (profiling runs of the packed layout)")
     args = ap.parse_args()
@@ -399,6 +441,8 @@ def main() -> int:
     # ------------------------------------ achievable ceilings on this device
     ceil = measure_ceilings(args, torch, skg, shapes, wp_dev, stream)
 
+    mid = None if args.no_mid_m else measure_mid_m(args, torch, skg, synth, shapes, wp_dev, stream, ceil)
+
     # --------------------------- a copy of known size (counter calibration)
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -463,6 +507,7 @@ def main() -> int:
                      "mfma_bf16_tflops": round(ceil["mfma_bf16_tflops"], 1),
                      "mfma_bf16_frac_of_peak": round(ceil["mfma_bf16_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)},
         "per_m": detail,
+        "mid_m": mid,
         "per_call_us": all_calls,
     }
     if not args.no_cpu_baseline:

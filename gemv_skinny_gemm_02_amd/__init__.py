@@ -24,7 +24,7 @@ import threading
 import torch
 
 __all__ = [
-    "SkinnyGemmError", "lib_path", "load", "OPS",
+    "SkinnyGemmError", "lib_path", "load", "OPS", "BUCKETS",
     "skinny_gemm_bf16", "skinny_gemm_gated", "skinny_gemm_fp8_tensor", "skinny_gemm_a8w8_block",
     "skinny_gemm_a8w8_block_quant",
     "PackedWeight", "skinny_gemm_packed_weight_bytes", "skinny_gemm_pack_weight", "skinny_gemm_bf16_packed",
@@ -36,6 +36,10 @@ __all__ = [
     "skinny_gemm_calib_read", "skinny_gemm_calib_mfma", "CALIB_MFMA_FLOPS_PER_ITER_WG",
 ]
 
+# Rows buckets of dispatch (the library's list): M rounds up to the next one;
+# M above the last uses the untuned tile default.
+BUCKETS = (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 64, 96, 128, 144, 160, 176, 192, 208, 224, 240, 256,
+           288, 320, 352, 384, 416, 448, 480, 512)
 OPS = {"bf16": 0, "gated": 1, "fp8_tensor": 2, "a8w8_block": 3, "a8w8_quant": 4,
        "bf16_packed": 5, "gated_packed": 6, "fp8_tensor_packed": 7, "a8w8_block_packed": 8, "a8w8_quant_packed": 9}
 PACKED = 5            # op id offset of the forms that take a fragment-packed weight

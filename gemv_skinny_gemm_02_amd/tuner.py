@@ -1,7 +1,7 @@
 """Measuring tuner and promotion for the per-device dispatch table.
 
-    python -m gemv_skinny_gemm_02_amd.tuner tune  --store STORE.jsonl [--ops bf16,gated,...] [--quick]
-    python -m gemv_skinny_gemm_02_amd.tuner promote --store STORE.jsonl --out TABLE.json
+    python -m gemv_skinny_gemm_02_amd.tuner tune  --store STORE.jsonl [--ops bf16,gated,...] [--rows decode|mid|all] [--quick]
+    python -m gemv_skinny_gemm_02_amd.tuner promote --store STORE.jsonl --out TABLE.json [--merge OLD_TABLE.json]
 
 `tune` runs on the GPU.  For every key (op, rows bucket, N, K) of the workload
 set it runs every compiled variant that can serve the bucket, checks its
@@ -43,11 +43,19 @@ def log(*a):
 
 
 # ------------------------------------------------------------ workload keys
-def workload_keys(ops):
-    """(op, M, N, K) for every configured workload shape."""
+def workload_keys(ops, rows="decode"):
+    """(op, M, N, K) for every configured workload shape.  rows: "decode" (the
+    decode rows of each form), "mid" (the mid-M rows, bf16 sweep shapes only)
+    or "all"."""
     sys.path.insert(0, ROOT)
     import synth
     keys = []
+    if rows in ("mid", "all"):
+        for op in ("bf16", "bf16_packed"):
+            if op in ops:
+                keys += [(op, M, N, K) for (N, K) in synth.SWEEP_NK for M in synth.MID_M]
+        if rows == "mid":
+            return keys
     if "bf16" in ops:
         keys += [("bf16", M, N, K) for (N, K) in synth.SWEEP_NK for M in synth.SWEEP_M]
     if "gated" in ops:
@@ -72,7 +80,8 @@ def base_op(op):
 
 
 def bucket_of(M):
-    for b in (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 64, 96, 128):
+    from gemv_skinny_gemm_02_amd import BUCKETS
+    for b in BUCKETS:
         if M <= b:
             return b
     return 0
@@ -118,7 +127,7 @@ def _close_bf16(a, b):
     return d <= 2.0 ** -7 * mx and fro <= 5e-3
 
 
-def tune(store, ops, quick=False, rotation_gib=1.0, replays=5, only_m=None):
+def tune(store, ops, quick=False, rotation_gib=1.0, replays=5, only_m=None, rows="decode"):
     import torch
 
     import gemv_skinny_gemm_02_amd as skg
@@ -130,7 +139,7 @@ def tune(store, ops, quick=False, rotation_gib=1.0, replays=5, only_m=None):
     # measured triples are skipped on a rerun; a recorded failure is retried
     done = {(r["identity"], r["op"], r["rows"], r["N"], r["K"], r["variant"]) for r in read_store(store)
             if "us" in r}
-    keys = workload_keys(ops)
+    keys = workload_keys(ops, rows)
     if only_m:
         keys = [k for k in keys if k[1] in only_m]
     stream = torch.cuda.current_stream()
@@ -215,8 +224,10 @@ def tune(store, ops, quick=False, rotation_gib=1.0, replays=5, only_m=None):
     return 0
 
 
-def promote(store, out, identity=None):
-    """Write the table from the store (pure function of the store)."""
+def promote(store, out, identity=None, merge=None):
+    """Write the table from the store (pure function of the store).  merge: an
+    existing table of the same identity whose entries for keys the store does
+    not measure are kept as they are."""
     recs = [r for r in read_store(store) if "us" in r and r.get("parity_vs_default")]
     if not recs:
         raise SystemExit("store holds no usable measurements")
@@ -250,6 +261,15 @@ def promote(store, out, identity=None):
                         "measured_M": slot[choice]["M"], "us": round(slot[choice]["us"], 3),
                         "candidates": {r["variant"]: {"us": round(r["us"], 3)} for r in cands}})
     idd = dict(kv.split("=", 1) for kv in ident.split(";"))
+    if merge:
+        with open(merge) as f:
+            old = json.load(f)
+        if old.get("identity") != idd:
+            raise SystemExit(f"{merge}: identity {old.get('identity')} differs from the store's {idd}")
+        have = {(e["op"], e["rows"], e["N"], e["K"]) for e in entries}
+        kept = [e for e in old["entries"] if (e["op"], e["rows"], e["N"], e["K"]) not in have]
+        entries = sorted(kept + entries, key=lambda e: (order[e["op"]], e["N"], e["K"], e["rows"]))
+        log(f"merged: {len(kept)} entries kept from {merge}")
     table = {"format": "skinny_gemm_table", "version": 1, "identity": idd,
              "rule": f"non-default choice only at >= {KEEP_GAIN:.0%} gain over the built-in default",
              "entries": entries}
@@ -272,16 +292,18 @@ def main(argv=None):
     t.add_argument("--quick", action="store_true")
     t.add_argument("--rotation-gib", type=float, default=1.0)
     t.add_argument("--only-m", default="")
+    t.add_argument("--rows", default="decode", choices=("decode", "mid", "all"))
     p = sub.add_parser("promote")
     p.add_argument("--store", required=True)
     p.add_argument("--out", required=True)
     p.add_argument("--identity", default=None)
+    p.add_argument("--merge", default=None, help="existing table whose other entries are kept")
     a = ap.parse_args(argv)
     if a.mode == "tune":
         os.environ.setdefault("SKINNY_GEMM_TABLE", "/nonexistent/skinny_gemm.json")  # measure the true defaults
         only = [int(v) for v in a.only_m.split(",") if v]
-        return tune(a.store, a.ops.split(","), a.quick, a.rotation_gib, only_m=only)
-    return promote(a.store, a.out, a.identity)
+        return tune(a.store, a.ops.split(","), a.quick, a.rotation_gib, only_m=only, rows=a.rows)
+    return promote(a.store, a.out, a.identity, a.merge)
 
 
 if __name__ == "__main__":

@@ -49,12 +49,14 @@
  *           returns the calling thread's text for its last non-OK status.  A
  *           fault inside a kernel surfaces at the caller's next synchronisation.
  * Dispatch. Each call rounds M up to its rows bucket {1,2,3,4,6,8,12,16,24,32,
- *           64,96,128} and looks (op, bucket, N, K) up in the per-device table
- *           (Decode optimization round 3, "Retained change 2": padded-M
- *           lookup with no nearest fallback; mstar PR #1104, "What changed": one
- *           per-device table).  A miss, an absent table or a refused table uses
- *           the built-in default for the op and bucket.  M above 128 uses the
- *           MFMA tile path in chunks of 128 rows.
+ *           64,96,128}, or for mid-M rows {144,160,...,256} (steps of 16) and
+ *           {288,320,...,512} (steps of 32), and looks (op, bucket, N, K) up in
+ *           the per-device table (Decode optimization round 3, "Retained
+ *           change 2": padded-M lookup with no nearest fallback; mstar PR
+ *           #1104, "What changed": one per-device table).  A miss, an absent
+ *           table or a refused table uses the built-in default for the op and
+ *           bucket; M above 512 uses the untuned default.  Rows above 128 run
+ *           on the MFMA tile path in launch rows of at most 128.
  * Threads.  GEMM calls are reentrant.  skinny_gemm_load_table must not run
  *           concurrently with other calls.
  * Workspace. Variants that split K across workgroups keep fp32 partials in a

@@ -17,6 +17,8 @@ TID_X, TID_W, TID_WU = 1, 2, 3
 # Shape sets of the workloads (rows M of the decode linear, W as [N, K]).
 CONFIG1 = (1, 4096, 4096)
 SWEEP_M = (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 64, 96, 128)
+# mid-M rows (speculative verification and drafting) on the same (N, K)
+MID_M = (144, 192, 256, 384, 512)
 SWEEP_NK = ((4096, 4096), (6144, 4096), (4096, 12288), (2048, 2048), (1024, 1024))
 GATED_M = (1, 3, 6, 8, 12, 16, 32)
 GATED_NK = (12288, 4096)            # per half: Wg and Wu are each [N, K]

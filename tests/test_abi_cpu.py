@@ -62,9 +62,9 @@ def test_variants_and_buckets():
     names = skg.variants("bf16")
     assert names == skg.variants("a8w8_block") and len(names) == skg.skinny_gemm_num_variants(0)
     assert any(n.startswith("gemv_") for n in names) and any(n.startswith("tile_") for n in names)
-    # every op has a variant for every M in 1..300
+    # every op has a variant for every M in 1..600
     for op in skg.OPS:
-        for M in range(1, 301):
+        for M in range(1, 601):
             assert any(skg.skinny_gemm_variant_supports(op, i, M) for i in range(len(names))), (op, M)
     # GEMV variants never claim rows above 16; the bf16 tile variants serve
     # every bucket from one row
@@ -89,6 +89,32 @@ def test_table_engaged_lookup_and_buckets(tmp_path):
     assert skg.skinny_gemm_query("bf16", 8, 4096, 4095)[1] == "default"
     assert skg.skinny_gemm_query("gated", 13, 12288, 4096) == ("tile_f2_k4_p4", "table")
     assert skg.skinny_gemm_query("fp8_tensor", 8, 4096, 4096)[1] == "default"
+
+
+def test_mid_m_buckets(tmp_path):
+    """The binding's bucket list is the library's: a table entry at every
+    bucket engages, rows between buckets are refused, and M above 128 rounds
+    up to its mid-M bucket (steps of 16 to 256, of 32 to 512)."""
+    assert skg.BUCKETS[:13] == (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 64, 96, 128)
+    assert skg.BUCKETS[13:] == tuple(range(144, 257, 16)) + tuple(range(288, 513, 32))
+    ident = _identity()
+    tile = "tlds_f1_s1_p4"
+    entries = [{"op": "bf16", "rows": b, "N": 4096, "K": 4096, "choice": tile} for b in skg.BUCKETS if b >= 16]
+    p = _write(tmp_path, ident, entries)
+    skg.skinny_gemm_load_table_as(p, ident)
+    assert skg.skinny_gemm_table_status()[1].startswith(f"engaged {len(entries)} shapes")
+    for M in (129, 144, 145, 200, 256, 257, 300, 511, 512):
+        assert skg.skinny_gemm_query("bf16", M, 4096, 4096) == (tile, "table"), M
+    assert skg.skinny_gemm_query("bf16", 513, 4096, 4096)[1] == "default"
+    for rows in (130, 250, 260, 500, 600):
+        bad = entries + [{"op": "bf16", "rows": rows, "N": 4096, "K": 4096, "choice": tile}]
+        code = f"""
+import gemv_skinny_gemm_02_amd as skg
+skg.skinny_gemm_load_table_as({_write(tmp_path, ident, bad, name=f"b{rows}.json")!r}, {ident!r})
+assert not skg.skinny_gemm_table_status()[0]
+"""
+        r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+        assert r.returncode == 0 and "is not a rows bucket" in r.stderr, (rows, r.stderr)
 
 
 @pytest.mark.parametrize("case,needle", [

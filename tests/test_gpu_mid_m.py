@@ -1,0 +1,63 @@
+"""Mid-M rows (144 .. 512: speculative verification and drafting) on the GPU:
+every tile variant of the bf16 form, row-major and packed, on a ragged small
+shape element by element, and table dispatch at the full sweep shapes on
+sampled output columns, against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import gemv_skinny_gemm_02_amd as skg
+import oracle
+import synth
+from gpu_util import assert_parity, dev_bf16, host_bits, reference, run, run_packed, say, to_device, to_device_packed
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    skg.load()
+
+
+@pytest.mark.parametrize("op", ["bf16", "bf16_packed"])
+def test_every_variant_mid_m(op):
+    """M = 300 spans three launch rows of 128 with a ragged last one; N and K
+    are ragged against every tile."""
+    N, K = 257, 1032
+    names = skg.variants(op)
+    for M in (129, 300):
+        p = synth.make_bf16(M, N, K, seed=5)
+        dev = to_device_packed(p) if op.endswith("_packed") else to_device(p)
+        ref = reference(p)
+        ran = 0
+        for i, name in enumerate(names):
+            if not skg.skinny_gemm_variant_supports(op, i, M):
+                continue
+            say(f"{op} M={M} N={N} K={K} variant={name}")
+            y = run_packed(p, dev, variant=name) if op.endswith("_packed") else run(p, dev, variant=name)
+            torch.cuda.synchronize()
+            assert_parity(host_bits(y), ref, f"{op} {name} M={M}")
+            ran += 1
+        assert ran > 0
+
+
+def test_mid_m_full_shapes():
+    """Table dispatch at every mid-M workload row on the five sweep shapes, both
+    layouts, sampled columns."""
+    for (N, K) in synth.SWEEP_NK:
+        base = synth.make_bf16(max(synth.MID_M), N, K, seed=0)
+        w = dev_bf16(base.w)
+        wp = skg.skinny_gemm_pack_weight("bf16", w)
+        for M in synth.MID_M:
+            x = dev_bf16(base.x[:M])
+            cols = synth.rows_of(N, 48, seed=M)
+            ref = oracle.linear_bf16(base.x[:M], base.w, cols=cols)
+            say(f"bf16 mid M={M} N={N} K={K} -> {skg.skinny_gemm_query('bf16', M, N, K)}, "
+                f"packed -> {skg.skinny_gemm_query('bf16_packed', M, N, K)}")
+            y = skg.skinny_gemm_bf16(x, w)
+            yp = skg.skinny_gemm_bf16_packed(x, wp)
+            torch.cuda.synchronize()
+            assert_parity(host_bits(y)[:, cols], ref, f"bf16 M={M} N={N} K={K}")
+            assert_parity(host_bits(yp)[:, cols], ref, f"bf16_packed M={M} N={N} K={K}")
