@@ -439,9 +439,10 @@ def main() -> int:
             del g
 
     # ------------------------------------ achievable ceilings on this device
-    ceil = measure_ceilings(args, torch, skg, shapes, wp_dev, stream)
+    # (profiling runs skip them, so that every dispatch profiled is the step's)
+    ceil = None if args.no_per_call else measure_ceilings(args, torch, skg, shapes, wp_dev, stream)
 
-    mid = None if args.no_mid_m else measure_mid_m(args, torch, skg, synth, shapes, wp_dev, stream, ceil)
+    mid = None if (args.no_mid_m or ceil is None) else measure_mid_m(args, torch, skg, synth, shapes, wp_dev, stream, ceil)
 
     # --------------------------- a copy of known size (counter calibration)
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -455,8 +456,10 @@ def main() -> int:
     dom_bytes = sum(alg_bytes(*c) for c in dom_calls) / len(dom_calls)
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     # the same launch mix at each shape's read ceiling (weight bytes read alone)
-    dom_ceil_us = sum(ceil["read"][(N, K)]["us"] for (_, N, K) in dom_calls) / len(dom_calls)
-    achievable = dom_bytes / (dom_ceil_us * 1e-6) / 1e9
+    achievable = None
+    if ceil is not None:
+        dom_ceil_us = sum(ceil["read"][(N, K)]["us"] for (_, N, K) in dom_calls) / len(dom_calls)
+        achievable = dom_bytes / (dom_ceil_us * 1e-6) / 1e9
     code_hash = lib_code_hash()
     traffic = read_counters(dominant, code_hash)
     detail = {}
@@ -468,9 +471,10 @@ def main() -> int:
             gbs = alg_bytes(*c) / (us * 1e-6) / 1e9
             tfl = 2 * M * N * K / (us * 1e-6) / 1e12
             row[f"{N}x{K}"] = {"us": round(us, 2), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
-                               "read_ceiling_frac": round(ceil["read"][(N, K)]["us"] / us, 3),
-                               "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
-                               "mfma_ceiling_frac": round(tfl / ceil["mfma_bf16_tflops"], 4), "variant": choice[c][0]}
+                               "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4), "variant": choice[c][0]}
+            if ceil is not None:
+                row[f"{N}x{K}"]["read_ceiling_frac"] = round(ceil["read"][(N, K)]["us"] / us, 3)
+                row[f"{N}x{K}"]["mfma_ceiling_frac"] = round(tfl / ceil["mfma_bf16_tflops"], 4)
         detail[f"M={M}"] = row
     all_calls = {f"{M}x{N}x{K}": round(per_call_us[(M, N, K)], 2) for (M, N, K) in calls}
 
@@ -500,12 +504,14 @@ def main() -> int:
                      "traffic": round(traffic) if traffic is not None else None,
                      "kernel": dominant, "launches_per_step": len(dom_calls), "avg_launch_us": round(dom_us, 3),
                      "alg_bytes_per_launch": round(dom_bytes), "code_hash": code_hash,
-                     "achievable": {"GB/s": round(achievable, 1), "frac": round(achieved / achievable, 4),
-                                    "basis": "the same launches at each shape's plain-read time of its weight "
-                                             "(skinny_gemm_calib_read, graph replay, best grid)"}},
-        "ceilings": {"read": {f"{N}x{K}": v for (N, K), v in ceil["read"].items()},
-                     "mfma_bf16_tflops": round(ceil["mfma_bf16_tflops"], 1),
-                     "mfma_bf16_frac_of_peak": round(ceil["mfma_bf16_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)},
+                     "achievable": None if achievable is None else
+                     {"GB/s": round(achievable, 1), "frac": round(achieved / achievable, 4),
+                      "basis": "the same launches at each shape's plain-read time of its weight "
+                               "(skinny_gemm_calib_read, graph replay, best grid)"}},
+        "ceilings": None if ceil is None else
+        {"read": {f"{N}x{K}": v for (N, K), v in ceil["read"].items()},
+         "mfma_bf16_tflops": round(ceil["mfma_bf16_tflops"], 1),
+         "mfma_bf16_frac_of_peak": round(ceil["mfma_bf16_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)},
         "per_m": detail,
         "mid_m": mid,
         "per_call_us": all_calls,
