@@ -325,6 +325,42 @@ def measure_mid_m(args, torch, skg, synth, shapes, wp_dev, stream, ceil):
             "vendor": "torch.mm (hipBLASLt), bf16, same rotated buffers, graph replay: context only"}
 
 
+def measure_small_n(args, torch, skg, synth, stream):
+    """Small-N bf16 weights (N = 64 .. 2048, K = 4096): µs per call of both
+    layouts through table dispatch, and the read ceiling of each weight, all
+    in graph replay over >= 1 GiB of rotated copies."""
+    sink = torch.empty(256, dtype=torch.int32, device="cuda")
+    out = {}
+    Mmax = max(synth.SMALLN_M)
+    for (N, K) in synth.SMALLN_NK:
+        p = synth.make_bf16(Mmax, N, K, seed=0)
+        x = torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).cuda()
+        w0 = torch.from_numpy(p.w.view(np.int16)).view(torch.bfloat16).cuda()
+        R = max(2, math.ceil(args.rotation_gib * 2**30 / (2 * N * K)))
+        ws = [w0] + [w0.clone() for _ in range(R - 1)]
+        wps = [skg.skinny_gemm_pack_weight("bf16", w0) for _ in range(R)]
+        n = max(args.per_call_min, 2 * R)
+        ceil_us = min(_graph_us(torch, stream, n, lambda i: skg.skinny_gemm_calib_read(ws[i % R], g, sink),
+                                args.per_call_replays) for g in (256, 512, 1024))
+        row = {}
+        for M in synth.SMALLN_M:
+            xm = x[:M]
+            y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            rm = _graph_us(torch, stream, n, lambda i: skg.skinny_gemm_bf16(xm, ws[i % R], y=y), args.per_call_replays)
+            pk = _graph_us(torch, stream, n, lambda i: skg.skinny_gemm_bf16_packed(xm, wps[i % R], y=y),
+                           args.per_call_replays)
+            row[str(M)] = {"row_major_us": round(rm, 2), "packed_us": round(pk, 2),
+                           "read_ceiling_frac": round(ceil_us / min(rm, pk), 3),
+                           "row_major_variant": skg.skinny_gemm_query("bf16", M, N, K)[0],
+                           "packed_variant": skg.skinny_gemm_query("bf16_packed", M, N, K)[0]}
+        out[f"{N}x{K}"] = {"read_ceiling_us": round(ceil_us, 3), "rows": row}
+        log(f"small-N {N}x{K}: ceiling {ceil_us:.2f} us,", {m: (v["row_major_us"], v["packed_us"]) for m, v in row.items()})
+        del ws, wps, w0
+        torch.cuda.empty_cache()
+    return {"form": "bf16, table dispatch, row-major and packed", "shapes": out,
+            "read_ceiling_frac": "read ceiling of the weight / the faster layout's call"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -339,6 +375,7 @@ def main() -> int:
                          "in the step's shape mix)")
     ap.add_argument("--per-call-min", type=int, default=64, help="min launches per per-call graph")
     ap.add_argument("--no-mid-m", action="store_true", help="skip the mid-M rows (144..512) report")
+    ap.add_argument("--no-small-n", action="store_true", help="skip the small-N (N = 64..2048) report")
     ap.add_argument("--no-row-major", action="store_true",
                     help="skip the row-major step (profiling runs of the packed layout)")
     args = ap.parse_args()
@@ -443,6 +480,7 @@ def main() -> int:
     ceil = None if args.no_per_call else measure_ceilings(args, torch, skg, shapes, wp_dev, stream)
 
     mid = None if (args.no_mid_m or ceil is None) else measure_mid_m(args, torch, skg, synth, shapes, wp_dev, stream, ceil)
+    small_n = None if (args.no_small_n or ceil is None) else measure_small_n(args, torch, skg, synth, stream)
 
     # --------------------------- a copy of known size (counter calibration)
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -514,6 +552,7 @@ def main() -> int:
          "mfma_bf16_frac_of_peak": round(ceil["mfma_bf16_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)},
         "per_m": detail,
         "mid_m": mid,
+        "small_n": small_n,
         "per_call_us": all_calls,
     }
     if not args.no_cpu_baseline:

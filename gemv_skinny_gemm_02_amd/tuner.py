@@ -45,8 +45,8 @@ def log(*a):
 # ------------------------------------------------------------ workload keys
 def workload_keys(ops, rows="decode"):
     """(op, M, N, K) for every configured workload shape.  rows: "decode" (the
-    decode rows of each form), "mid" (the mid-M rows, bf16 sweep shapes only)
-    or "all"."""
+    decode rows of each form), "mid" (the mid-M rows, bf16 sweep shapes only),
+    "smalln" (the small-N bf16 shapes) or "all"."""
     sys.path.insert(0, ROOT)
     import synth
     keys = []
@@ -54,8 +54,12 @@ def workload_keys(ops, rows="decode"):
         for op in ("bf16", "bf16_packed"):
             if op in ops:
                 keys += [(op, M, N, K) for (N, K) in synth.SWEEP_NK for M in synth.MID_M]
-        if rows == "mid":
-            return keys
+    if rows in ("smalln", "all"):
+        for op in ("bf16", "bf16_packed"):
+            if op in ops:
+                keys += [(op, M, N, K) for (N, K) in synth.SMALLN_NK for M in synth.SMALLN_M]
+    if rows in ("mid", "smalln"):
+        return keys
     if "bf16" in ops:
         keys += [("bf16", M, N, K) for (N, K) in synth.SWEEP_NK for M in synth.SWEEP_M]
     if "gated" in ops:
@@ -292,7 +296,7 @@ def main(argv=None):
     t.add_argument("--quick", action="store_true")
     t.add_argument("--rotation-gib", type=float, default=1.0)
     t.add_argument("--only-m", default="")
-    t.add_argument("--rows", default="decode", choices=("decode", "mid", "all"))
+    t.add_argument("--rows", default="decode", choices=("decode", "mid", "smalln", "all"))
     p = sub.add_parser("promote")
     p.add_argument("--store", required=True)
     p.add_argument("--out", required=True)

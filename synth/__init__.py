@@ -25,10 +25,10 @@ its 248k x 4096 vocabulary head, DeepSeek-V4-flash's A8W8 block-scale layers):
 """
 from .gen import (CHUNK, normal_f32, bf16_bits, e4m3fn_bytes, make_bf16,
                   make_gated, make_fp8_tensor, make_a8w8_block, make_a8w8_quant, BLOCK,
-                  rows_of, SWEEP_M, MID_M, SWEEP_NK, GATED_M, GATED_NK, HEAD_M,
+                  rows_of, SWEEP_M, MID_M, SMALLN_NK, SMALLN_M, SWEEP_NK, GATED_M, GATED_NK, HEAD_M,
                   HEAD_NK, A8W8_M, A8W8_NK, CONFIG1)
 
 __all__ = ["CHUNK", "normal_f32", "bf16_bits", "e4m3fn_bytes", "make_bf16",
            "make_gated", "make_fp8_tensor", "make_a8w8_block", "make_a8w8_quant", "BLOCK",
-           "rows_of", "SWEEP_M", "MID_M", "SWEEP_NK", "GATED_M", "GATED_NK", "HEAD_M",
+           "rows_of", "SWEEP_M", "MID_M", "SMALLN_NK", "SMALLN_M", "SWEEP_NK", "GATED_M", "GATED_NK", "HEAD_M",
            "HEAD_NK", "A8W8_M", "A8W8_NK", "CONFIG1"]

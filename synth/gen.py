@@ -19,6 +19,9 @@ CONFIG1 = (1, 4096, 4096)
 SWEEP_M = (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 64, 96, 128)
 # mid-M rows (speculative verification and drafting) on the same (N, K)
 MID_M = (144, 192, 256, 384, 512)
+# small-N bf16 weights (too few rows to fill the CUs by N-split alone)
+SMALLN_NK = ((64, 4096), (256, 4096), (512, 4096), (1024, 4096), (2048, 4096))
+SMALLN_M = (1, 4, 8, 16, 32, 64, 128)
 SWEEP_NK = ((4096, 4096), (6144, 4096), (4096, 12288), (2048, 2048), (1024, 1024))
 GATED_M = (1, 3, 6, 8, 12, 16, 32)
 GATED_NK = (12288, 4096)            # per half: Wg and Wu are each [N, K]

@@ -1,7 +1,8 @@
-"""Mid-M rows (144 .. 512: speculative verification and drafting) on the GPU:
-every tile variant of the bf16 form, row-major and packed, on a ragged small
-shape element by element, and table dispatch at the full sweep shapes on
-sampled output columns, against the CPU oracle."""
+"""Mid-M rows (144 .. 512: speculative verification and drafting) and small-N
+weights on the GPU: every tile variant of the bf16 form, row-major and packed,
+on a ragged small shape element by element; table dispatch at the full sweep
+shapes on sampled output columns, and at the small-N shapes on every output;
+all against the CPU oracle."""
 import numpy as np
 import pytest
 import torch
@@ -61,3 +62,26 @@ def test_mid_m_full_shapes():
             torch.cuda.synchronize()
             assert_parity(host_bits(y)[:, cols], ref, f"bf16 M={M} N={N} K={K}")
             assert_parity(host_bits(yp)[:, cols], ref, f"bf16_packed M={M} N={N} K={K}")
+
+
+def test_small_n_full_shapes():
+    """Small-N bf16 weights (N = 64 .. 2048, K = 4096), table dispatch, both
+    layouts, every output against the oracle; and two calls in a row give the
+    same bits (the cross-workgroup K split adds its partials in a fixed
+    order)."""
+    for (N, K) in synth.SMALLN_NK:
+        base = synth.make_bf16(max(synth.SMALLN_M), N, K, seed=0)
+        w = dev_bf16(base.w)
+        wp = skg.skinny_gemm_pack_weight("bf16", w)
+        for M in synth.SMALLN_M:
+            x = dev_bf16(base.x[:M])
+            ref = oracle.linear_bf16(base.x[:M], base.w)
+            say(f"bf16 small-N M={M} N={N} K={K} -> {skg.skinny_gemm_query('bf16', M, N, K)}, "
+                f"packed -> {skg.skinny_gemm_query('bf16_packed', M, N, K)}")
+            y, y2 = skg.skinny_gemm_bf16(x, w), skg.skinny_gemm_bf16(x, w)
+            yp, yp2 = skg.skinny_gemm_bf16_packed(x, wp), skg.skinny_gemm_bf16_packed(x, wp)
+            torch.cuda.synchronize()
+            assert_parity(host_bits(y), ref, f"bf16 M={M} N={N} K={K}")
+            assert_parity(host_bits(yp), ref, f"bf16_packed M={M} N={N} K={K}")
+            assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+            assert torch.equal(yp.view(torch.int16), yp2.view(torch.int16))
