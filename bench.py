@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+READ_GRIDS = (512, 1024, 2048, 4096, 8192)   # workgroup counts tried for a read ceiling
 METRIC = "achieved HBM GB/s and µs/call at M=1/8/128; fraction of MI355X roofline"
 
 
@@ -251,7 +252,7 @@ def _graph_us(torch, stream, n, enqueue, replays):
 def measure_ceilings(args, torch, skg, shapes, wp_dev, stream):
     """What a kernel can reach here: per weight size, the fastest plain read of
     the same rotated weight copies (the library's read-stream kernel, graph
-    replay as for the calls, best of three grid sizes); and the bf16 MFMA rate
+    replay as for the calls, best of five grid sizes); and the bf16 MFMA rate
     of a register-only MFMA loop on every CU."""
     sink = torch.empty(256, dtype=torch.int32, device="cuda")
     read = {}
@@ -260,14 +261,16 @@ def measure_ceilings(args, torch, skg, shapes, wp_dev, stream):
         R = len(bufs)
         n = max(args.per_call_min, 2 * R)
         best = None
-        for grid in (512, 1024, 2048):
-            us = _graph_us(torch, stream, n, lambda i: skg.skinny_gemm_calib_read(bufs[i % R], grid, sink),
-                           args.per_call_replays)
-            if best is None or us < best[0]:
-                best = (us, grid)
+        for grid in READ_GRIDS:
+            for sweep in (False, True):
+                us = _graph_us(torch, stream, n,
+                               lambda i: skg.skinny_gemm_calib_read(bufs[i % R], grid, sink, sweep=sweep),
+                               args.per_call_replays)
+                if best is None or us < best[0]:
+                    best = (us, grid, sweep)
         nbytes = bufs[0].numel()
         read[(N, K)] = {"bytes": nbytes, "us": round(best[0], 3), "GB/s": round(nbytes / (best[0] * 1e-6) / 1e9, 1),
-                        "grid": best[1]}
+                        "grid": best[1], "order": "sweep" if best[2] else "slices"}
     grid, iters = 8 * 256, 2048
     flops = skg.skinny_gemm_calib_mfma(grid, iters, sink)       # warm-up
     torch.cuda.synchronize()
@@ -340,8 +343,8 @@ def measure_small_n(args, torch, skg, synth, stream):
         ws = [w0] + [w0.clone() for _ in range(R - 1)]
         wps = [skg.skinny_gemm_pack_weight("bf16", w0) for _ in range(R)]
         n = max(args.per_call_min, 2 * R)
-        ceil_us = min(_graph_us(torch, stream, n, lambda i: skg.skinny_gemm_calib_read(ws[i % R], g, sink),
-                                args.per_call_replays) for g in (256, 512, 1024))
+        ceil_us = min(_graph_us(torch, stream, n, lambda i: skg.skinny_gemm_calib_read(ws[i % R], g, sink, sweep=sw),
+                                args.per_call_replays) for g in (256, 512, 1024) for sw in (False, True))
         row = {}
         for M in synth.SMALLN_M:
             xm = x[:M]
@@ -361,6 +364,114 @@ def measure_small_n(args, torch, skg, synth, stream):
             "read_ceiling_frac": "read ceiling of the weight / the faster layout's call"}
 
 
+def form_alg_bytes(form, M, N, K):
+    """Algorithmic bytes of one call of a form: the weight once (gate and up
+    rows for the gated form), x once, its scales once, y once."""
+    kb, nb = -(-K // 128), -(-N // 128)
+    if form == "gated":
+        return 4 * N * K + 2 * M * K + 2 * M * N
+    if form == "fp8_tensor":
+        return N * K + 2 * M * K + 2 * M * N + 4
+    if form == "a8w8_quant":          # bf16 x in; the x scales are not handed out here
+        return N * K + 2 * M * K + 4 * nb * kb + 2 * M * N
+    return N * K + M * K + 4 * M * kb + 4 * nb * kb + 2 * M * N
+
+
+def measure_forms(args, torch, skg, synth, stream):
+    """The other forms at their workload shapes: gate/up 12288 x 4096, the
+    248320 x 4096 fp8 head, and A8W8 (and A8W8 with x quantised in the call) at
+    (32768, 1024) and (8192, 4096).  µs per call of the row-major and packed
+    weights through table dispatch, graph replay over >= 1 GiB of rotated
+    weight copies, against the read ceiling of the weight.  Inputs are drawn on
+    the device from torch's seeded generator with the workload distributions
+    (x ~ N(0,1), W ~ N(0,0.02), fp8 scales amax/448); the values do not change
+    the time of these kernels, and the oracle checks them in the tests."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    sink = torch.empty(256, dtype=torch.int32, device="cuda")
+
+    def normal(shape, std):
+        return torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32) * std
+
+    def e4m3(v, rows, cols):
+        # per-block scale amax/448 over [rows, cols] blocks of v, and the codes
+        R_, C_ = v.shape
+        pr, pc = -(-R_ // rows) * rows, -(-C_ // cols) * cols
+        vp = torch.zeros((pr, pc), device="cuda")
+        vp[:R_, :C_] = v
+        blk = vp.view(pr // rows, rows, pc // cols, cols)
+        sc = blk.abs().amax(dim=(1, 3)) / 448.0
+        sc = torch.where(sc > 0, sc, torch.ones_like(sc))
+        q = (blk / sc[:, None, :, None]).clamp(-448, 448).view(pr, pc)[:R_, :C_]
+        return q.to(torch.float8_e4m3fn).contiguous(), sc.float().contiguous()
+
+    cases = [("gated", synth.GATED_NK, synth.GATED_M), ("fp8_tensor", synth.HEAD_NK, synth.HEAD_M)]
+    cases += [("a8w8_block", nk, synth.A8W8_M) for nk in synth.A8W8_NK]
+    cases += [("a8w8_quant", nk, synth.A8W8_M) for nk in synth.A8W8_NK]
+    out = {}
+    for form, (N, K), Ms in cases:
+        Mmax = max(Ms)
+        s0 = s1 = None
+        if form == "gated":
+            w0 = normal((2 * N, K), 0.02).to(torch.bfloat16)
+        elif form == "fp8_tensor":
+            # drawn twice in the same row blocks from the same seed (the fp32
+            # weight would be 4 GB): once for amax, once to quantise
+            w0 = torch.empty((N, K), dtype=torch.float8_e4m3fn, device="cuda")
+            amax = torch.zeros((), device="cuda")
+            gen.manual_seed(1)
+            for r0 in range(0, N, 16384):
+                amax = torch.maximum(amax, normal((min(16384, N - r0), K), 0.02).abs().max())
+            sc = (amax / 448.0).reshape(1).float()
+            gen.manual_seed(1)
+            for r0 in range(0, N, 16384):
+                w0[r0:r0 + 16384] = (normal((min(16384, N - r0), K), 0.02) / sc).clamp(-448, 448).to(torch.float8_e4m3fn)
+            s0 = sc
+        else:
+            w0, s1 = e4m3(normal((N, K), 0.02), 128, 128)
+        xf = normal((Mmax, K), 1.0)
+        if form == "a8w8_block":
+            x, s0 = e4m3(xf, 1, 128)
+        else:
+            x = xf.to(torch.bfloat16)
+        wbytes = w0.numel() * w0.element_size()
+        R = max(2, math.ceil(args.rotation_gib * 2**30 / wbytes))
+        ws = [w0] + [w0.clone() for _ in range(R - 1)]
+        wps = [skg.skinny_gemm_pack_weight(form, w0) for _ in range(R)]
+        n = max(args.per_call_min, 2 * R)
+        ceil_us = min(_graph_us(torch, stream, n, lambda i: skg.skinny_gemm_calib_read(ws[i % R], g, sink, sweep=sw),
+                                args.per_call_replays) for g in READ_GRIDS for sw in (False, True))
+        rows = {}
+        for M in Ms:
+            xm = x[:M]
+            s0m = s0[:M] if form == "a8w8_block" else s0
+            y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            if form == "gated":
+                f_rm = lambda i: skg.skinny_gemm_gated(xm, ws[i % R], y=y)
+                f_pk = lambda i: skg.skinny_gemm_gated_packed(xm, wps[i % R], y=y)
+            elif form == "fp8_tensor":
+                f_rm = lambda i: skg.skinny_gemm_fp8_tensor(xm, ws[i % R], s0m, y=y)
+                f_pk = lambda i: skg.skinny_gemm_fp8_tensor_packed(xm, wps[i % R], s0m, y=y)
+            elif form == "a8w8_block":
+                f_rm = lambda i: skg.skinny_gemm_a8w8_block(xm, ws[i % R], s0m, s1, y=y)
+                f_pk = lambda i: skg.skinny_gemm_a8w8_block_packed(xm, wps[i % R], s0m, s1, y=y)
+            else:
+                f_rm = lambda i: skg.skinny_gemm_a8w8_block_quant(xm, ws[i % R], s1, y=y)
+                f_pk = lambda i: skg.skinny_gemm_a8w8_block_quant_packed(xm, wps[i % R], s1, y=y)
+            rm = _graph_us(torch, stream, n, f_rm, args.per_call_replays)
+            pk = _graph_us(torch, stream, n, f_pk, args.per_call_replays)
+            best = min(rm, pk)
+            gbs = form_alg_bytes(form, M, N, K) / (best * 1e-6) / 1e9
+            rows[str(M)] = {"row_major_us": round(rm, 2), "packed_us": round(pk, 2), "GB/s": round(gbs, 1),
+                            "hbm_frac": round(gbs / HBM_PEAK_GBS, 3), "read_ceiling_frac": round(ceil_us / best, 3)}
+        key = f"{form} {N}x{K}"
+        out[key] = {"weight_bytes": wbytes, "read_ceiling_us": round(ceil_us, 3), "rows": rows}
+        log(f"{key}: ceiling {ceil_us:.2f} us,", {m: (v["row_major_us"], v["packed_us"]) for m, v in rows.items()})
+        del ws, wps, w0, x, xf
+        torch.cuda.empty_cache()
+    return {"dispatch": "table", "GB/s": "algorithmic bytes / the faster layout's µs", "shapes": out}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -376,6 +487,7 @@ def main() -> int:
     ap.add_argument("--per-call-min", type=int, default=64, help="min launches per per-call graph")
     ap.add_argument("--no-mid-m", action="store_true", help="skip the mid-M rows (144..512) report")
     ap.add_argument("--no-small-n", action="store_true", help="skip the small-N (N = 64..2048) report")
+    ap.add_argument("--no-forms", action="store_true", help="skip the gated / fp8 head / A8W8 report")
     ap.add_argument("--no-row-major", action="store_true",
                     help="skip the row-major step (profiling runs of the packed layout)")
     args = ap.parse_args()
@@ -481,6 +593,7 @@ def main() -> int:
 
     mid = None if (args.no_mid_m or ceil is None) else measure_mid_m(args, torch, skg, synth, shapes, wp_dev, stream, ceil)
     small_n = None if (args.no_small_n or ceil is None) else measure_small_n(args, torch, skg, synth, stream)
+    forms = None if (args.no_forms or ceil is None) else measure_forms(args, torch, skg, synth, stream)
 
     # --------------------------- a copy of known size (counter calibration)
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -545,7 +658,7 @@ def main() -> int:
                      "achievable": None if achievable is None else
                      {"GB/s": round(achievable, 1), "frac": round(achieved / achievable, 4),
                       "basis": "the same launches at each shape's plain-read time of its weight "
-                               "(skinny_gemm_calib_read, graph replay, best grid)"}},
+                               "(skinny_gemm_calib_read, graph replay, best of 512..8192 workgroups in slices or one sweep)"}},
         "ceilings": None if ceil is None else
         {"read": {f"{N}x{K}": v for (N, K), v in ceil["read"].items()},
          "mfma_bf16_tflops": round(ceil["mfma_bf16_tflops"], 1),
@@ -553,6 +666,7 @@ def main() -> int:
         "per_m": detail,
         "mid_m": mid,
         "small_n": small_n,
+        "forms": forms,
         "per_call_us": all_calls,
     }
     if not args.no_cpu_baseline:

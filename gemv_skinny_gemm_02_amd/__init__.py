@@ -119,7 +119,7 @@ def load() -> ctypes.CDLL:
         lib.skinny_gemm_variant_supports.restype = i
         lib.skinny_gemm_run_variant.argtypes = [i, i, vp, vp, vp, fp, fp, vp, i, i, i, vp]
         lib.skinny_gemm_run_variant.restype = i
-        lib.skinny_gemm_calib_read.argtypes = [vp, ctypes.c_size_t, i, vp, vp]
+        lib.skinny_gemm_calib_read.argtypes = [vp, ctypes.c_size_t, i, i, vp, vp]
         lib.skinny_gemm_calib_read.restype = i
         lib.skinny_gemm_calib_mfma.argtypes = [i, i, vp, vp]
         lib.skinny_gemm_calib_mfma.restype = i
@@ -419,14 +419,15 @@ def _sink(sink, like_device):
     return sink
 
 
-def skinny_gemm_calib_read(buf: torch.Tensor, grid: int, sink=None, stream=None) -> None:
+def skinny_gemm_calib_read(buf: torch.Tensor, grid: int, sink=None, stream=None, sweep: bool = False) -> None:
     """Read every byte of the contiguous device tensor `buf` once with `grid`
-    workgroups (a measurement kernel: it computes nothing of the linear)."""
+    workgroups, a slice each or (sweep) all together (a measurement kernel: it
+    computes nothing of the linear)."""
     if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
         raise ValueError("buf must be a contiguous device tensor")
     sink = _sink(sink, buf.device)
     _check(load().skinny_gemm_calib_read(buf.data_ptr(), buf.numel() * buf.element_size(), int(grid),
-                                         sink.data_ptr(), _stream(stream)))
+                                         1 if sweep else 0, sink.data_ptr(), _stream(stream)))
 
 
 def skinny_gemm_calib_mfma(grid: int, iters: int, sink=None, stream=None) -> int:

@@ -481,15 +481,17 @@ skg_status skinny_gemm_pack_weight(int op, const void* W, void* W_packed, int N,
 
 const char* skinny_gemm_last_error(void) { return g_err.c_str(); }
 
-skg_status skinny_gemm_calib_read(const void* buf, size_t bytes, int grid, unsigned* sink, hipStream_t stream) {
+skg_status skinny_gemm_calib_read(const void* buf, size_t bytes, int grid, int sweep, unsigned* sink,
+                                  hipStream_t stream) {
   if (grid < 1 || grid > 65536) return fail(SKG_EINVAL, "grid %d outside 1..65536", grid);
+  if (sweep != 0 && sweep != 1) return fail(SKG_EINVAL, "sweep must be 0 or 1 (%d)", sweep);
   if (bytes == 0 || bytes % 16 || (reinterpret_cast<uintptr_t>(buf) & 15) || (reinterpret_cast<uintptr_t>(sink) & 3))
     return fail(SKG_EUNSUPPORTED, "buf must be 16-byte aligned, its size a nonzero multiple of 16, sink 4-byte aligned");
   const Buf bb{buf, bytes, "buf"}, bs{sink, 256 * sizeof(unsigned), "sink"};
   for (const Buf* b : {&bb, &bs})
     if (skg_status st = check_device_range(*b)) return st;
   if (overlap(bb, bs)) return fail(SKG_EINVAL, "sink overlaps buf");
-  const hipError_t e = launch_calib_read(buf, (unsigned long long)(bytes / 16), grid, sink, stream);
+  const hipError_t e = launch_calib_read(buf, (unsigned long long)(bytes / 16), grid, sweep, sink, stream);
   return e == hipSuccess ? SKG_OK : fail(SKG_ELAUNCH, "calib read launch: %s", hipGetErrorString(e));
 }
 

@@ -2,10 +2,11 @@
 // device can reach, against which the linear's kernels are reported.  They
 // compute nothing of the linear.
 //
-//  * read_kernel: every workgroup streams one contiguous slice of a buffer
-//    with 16-byte non-temporal loads, 8 per thread in flight (256 threads),
-//    and folds the words into one value that is stored only if it equals a
-//    constant no ordinary data hits (so the loads stay live).
+//  * read_kernel: the grid reads a buffer once with 16-byte non-temporal
+//    loads, 8 per thread in flight (256 threads), each workgroup one
+//    contiguous slice or the whole grid in one sweep, and folds the words into
+//    one value that is stored only if it equals a constant no ordinary data
+//    hits (so the loads stay live).
 //  * mfma_kernel: every wave runs `iters` rounds of 8 independent
 //    v_mfma_f32_32x32x16_bf16 chains on register operands, then stores one
 //    value per thread only if it equals the same constant.  (Measured on
@@ -21,18 +22,30 @@ namespace {
 
 constexpr unsigned kNever = 0x7fc0dead;   // a NaN pattern no fold of the data is expected to give
 
+// SWEEP false: workgroup b reads the b-th contiguous slice.  SWEEP true: the
+// whole grid sweeps the buffer together (piece t + j*T for thread t of T), so
+// the addresses in flight stay in one moving window.
+template <bool SWEEP>
 __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ p, unsigned long long n16,
                                                    unsigned* sink) {
   constexpr int U = 8;
-  const unsigned long long per = (n16 + gridDim.x - 1) / gridDim.x;
-  const unsigned long long b0 = (unsigned long long)blockIdx.x * per;
-  const unsigned long long b1 = b0 + per < n16 ? b0 + per : n16;
+  unsigned long long b0, b1, step;
+  if constexpr (SWEEP) {
+    b0 = (unsigned long long)blockIdx.x * 256;
+    b1 = n16;
+    step = (unsigned long long)gridDim.x * 256;
+  } else {
+    const unsigned long long per = (n16 + gridDim.x - 1) / gridDim.x;
+    b0 = (unsigned long long)blockIdx.x * per;
+    b1 = b0 + per < n16 ? b0 + per : n16;
+    step = 256;
+  }
   unsigned acc = 0;
-  for (unsigned long long i = b0 + threadIdx.x; i < b1; i += 256 * U) {
+  for (unsigned long long i = b0 + threadIdx.x; i < b1; i += step * U) {
     u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const unsigned long long j = i + (unsigned long long)u * 256;
+      const unsigned long long j = i + (unsigned long long)u * step;
       v[u] = j < b1 ? load_nt(p + j) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
@@ -64,8 +77,12 @@ __global__ __launch_bounds__(256) void mfma_kernel(int iters, unsigned* sink) {
 
 }  // namespace
 
-hipError_t launch_calib_read(const void* buf, unsigned long long n16, int grid, unsigned* sink, hipStream_t s) {
-  hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(256), 0, s, static_cast<const u32x4*>(buf), n16, sink);
+hipError_t launch_calib_read(const void* buf, unsigned long long n16, int grid, int sweep, unsigned* sink,
+                             hipStream_t s) {
+  if (sweep)
+    hipLaunchKernelGGL(read_kernel<true>, dim3(grid), dim3(256), 0, s, static_cast<const u32x4*>(buf), n16, sink);
+  else
+    hipLaunchKernelGGL(read_kernel<false>, dim3(grid), dim3(256), 0, s, static_cast<const u32x4*>(buf), n16, sink);
   return hipGetLastError();
 }
 

@@ -1335,8 +1335,9 @@ template <> const TileRow* tlds_table<OP_PACKED + OP_A8W8Q>();
 hipError_t launch_pack(int op, const void* W, void* Wp, int N, int K, hipStream_t s);
 
 // Measurement kernels (calib.hip): a read stream of n16 16-byte pieces over
-// `grid` workgroups, and `iters` rounds of 8 bf16 32x32x16 MFMA chains per wave.
-hipError_t launch_calib_read(const void* buf, unsigned long long n16, int grid, unsigned* sink, hipStream_t s);
+// `grid` workgroups (slice per workgroup, or a grid-wide sweep), and `iters` rounds of 8 bf16 32x32x16 MFMA chains per wave.
+hipError_t launch_calib_read(const void* buf, unsigned long long n16, int grid, int sweep, unsigned* sink,
+                             hipStream_t s);
 hipError_t launch_calib_mfma(int grid, int iters, unsigned* sink, hipStream_t s);
 
 }  // namespace skg

@@ -241,10 +241,11 @@ skg_status skinny_gemm_run_variant(int op, int variant, const int* knobs,
  * device's bandwidth: Decode optimization round 3, "Retained change 2").
  *
  * skinny_gemm_calib_read: one launch of `grid` workgroups of 256 threads
- * that read every byte of buf[0, bytes) once with 16-byte non-temporal loads
- * (each workgroup one contiguous slice, 8 loads per thread in flight).  buf
- * is device memory, 16-byte aligned, bytes a nonzero multiple of 16; grid in
- * 1..65536.  sink is 256 device words that the kernel writes only if the
+ * that read every byte of buf[0, bytes) once with 16-byte non-temporal loads,
+ * 8 loads per thread in flight: sweep 0, each workgroup one contiguous slice;
+ * sweep 1, the whole grid one sweep (thread t of T reads pieces t, t + T, ...).
+ * buf is device memory, 16-byte aligned, bytes a nonzero multiple of 16; grid
+ * in 1..65536.  sink is 256 device words that the kernel writes only if the
  * words it read fold (xor) to one NaN pattern, so callers ignore its value.
  *
  * skinny_gemm_calib_mfma: one launch of `grid` workgroups of 4 waves, each
@@ -255,7 +256,7 @@ skg_status skinny_gemm_run_variant(int op, int variant, const int* knobs,
  * Both are stream-ordered, allocate nothing and return the usual statuses
  * (EINVAL for sizes out of range and host or short buffers, EUNSUPPORTED for
  * misalignment, ELAUNCH). */
-skg_status skinny_gemm_calib_read(const void* buf, size_t bytes, int grid, unsigned* sink,
+skg_status skinny_gemm_calib_read(const void* buf, size_t bytes, int grid, int sweep, unsigned* sink,
                                   hipStream_t stream);
 skg_status skinny_gemm_calib_mfma(int grid, int iters, unsigned* sink, hipStream_t stream);
 

@@ -258,21 +258,23 @@ def test_calib_kernels_statuses():
     sink = torch.zeros(256, dtype=torch.int32, device="cuda")
     s = _stream()
     say("calib read 1 MiB, grid 64")
-    assert _raw("skinny_gemm_calib_read", buf.data_ptr(), buf.numel(), 64, sink.data_ptr(), s)[0] == 0
+    assert _raw("skinny_gemm_calib_read", buf.data_ptr(), buf.numel(), 64, 0, sink.data_ptr(), s)[0] == 0
     skg.skinny_gemm_calib_read(buf, 2048, sink)
+    skg.skinny_gemm_calib_read(buf, 300, sink, sweep=True)
     flops = skg.skinny_gemm_calib_mfma(8, 16, sink)
     assert flops == 8 * 16 * 4 * 8 * 32768
     torch.cuda.synchronize()
     assert int(sink.abs().sum()) == 0            # zero data never folds to the sink pattern
     host = np.zeros(1024, dtype=np.uint8)
-    st, msg = _raw("skinny_gemm_calib_read", host.ctypes.data, 1024, 4, sink.data_ptr(), s)
+    st, msg = _raw("skinny_gemm_calib_read", host.ctypes.data, 1024, 4, 0, sink.data_ptr(), s)
     assert st == 1 and "device memory" in msg
-    assert _raw("skinny_gemm_calib_read", buf.data_ptr() + 8, 1024, 4, sink.data_ptr(), s)[0] == 2
-    assert _raw("skinny_gemm_calib_read", buf.data_ptr(), 1000, 4, sink.data_ptr(), s)[0] == 2
-    assert _raw("skinny_gemm_calib_read", buf.data_ptr(), 8 << 30, 4, sink.data_ptr(), s)[0] == 1   # past the allocation
-    assert _raw("skinny_gemm_calib_read", buf.data_ptr(), 1024, 0, sink.data_ptr(), s)[0] == 1
+    assert _raw("skinny_gemm_calib_read", buf.data_ptr() + 8, 1024, 4, 0, sink.data_ptr(), s)[0] == 2
+    assert _raw("skinny_gemm_calib_read", buf.data_ptr(), 1000, 4, 0, sink.data_ptr(), s)[0] == 2
+    assert _raw("skinny_gemm_calib_read", buf.data_ptr(), 8 << 30, 4, 0, sink.data_ptr(), s)[0] == 1   # past the allocation
+    assert _raw("skinny_gemm_calib_read", buf.data_ptr(), 1024, 0, 0, sink.data_ptr(), s)[0] == 1
+    assert _raw("skinny_gemm_calib_read", buf.data_ptr(), 1024, 4, 2, sink.data_ptr(), s)[0] == 1
     hsink = np.zeros(256, dtype=np.int32)
-    assert _raw("skinny_gemm_calib_read", buf.data_ptr(), 1024, 4, hsink.ctypes.data, s)[0] == 1
+    assert _raw("skinny_gemm_calib_read", buf.data_ptr(), 1024, 4, 0, hsink.ctypes.data, s)[0] == 1
     assert _raw("skinny_gemm_calib_mfma", 0, 16, sink.data_ptr(), s)[0] == 1
     assert _raw("skinny_gemm_calib_mfma", 8, 0, sink.data_ptr(), s)[0] == 1
     assert _raw("skinny_gemm_calib_mfma", 8, 16, hsink.ctypes.data, s)[0] == 1
