@@ -48,3 +48,26 @@ def test_read_counters(tmp_path, monkeypatch):
     assert bench.read_counters("void skg::k<0>(skg::Args)", "abc") == (100.0 / 0.5 + 10.0) * 1024
     assert bench.read_counters("void skg::k<1>(skg::Args)", "abc") is None     # kernel not profiled
     assert bench.read_counters("void skg::k<0>(skg::Args)", "other") is None   # sources changed since
+
+
+@pytest.mark.parametrize("form", ["bf16", "gated", "fp8_tensor", "a8w8_block", "a8w8_quant"])
+def test_alg_bytes_agree(form):
+    """The bench's algorithmic bytes per call are the tuner's, for every form,
+    and the weight term dominates as the formulas say (W once; x, scales and y
+    once each)."""
+    from gemv_skinny_gemm_02_amd import tuner
+    for (M, N, K) in [(1, 4096, 4096), (64, 8192, 4096), (3, 248320, 4096), (16, 32768, 1024), (5, 257, 1040)]:
+        want = tuner.alg_bytes(form, M, N, K)
+        got = bench.alg_bytes(M, N, K) if form == "bf16" else bench.form_alg_bytes(form, M, N, K)
+        assert got == want, (form, M, N, K)
+    # the weight alone, in bytes: 2NK (bf16), 4NK (gate and up), NK (fp8)
+    wb = {"bf16": 2, "gated": 4, "fp8_tensor": 1, "a8w8_block": 1, "a8w8_quant": 1}[form]
+    assert tuner.alg_bytes(form, 1, 4096, 4096) - wb * 4096 * 4096 < 0.01 * wb * 4096 * 4096
+
+
+def test_bench_gpus_flag_refuses_more_than_one():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
