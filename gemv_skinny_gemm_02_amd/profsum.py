@@ -3,6 +3,7 @@
     python -m gemv_skinny_gemm_02_amd.profsum trace KERNEL_STATS.csv [--cmd CMD]
     python -m gemv_skinny_gemm_02_amd.profsum counters --fetch FETCH.csv --write WRITE.csv \
         --code-hash HASH [--cmd CMD]
+    python -m gemv_skinny_gemm_02_amd.profsum mfma COUNTERS.csv [--cmd CMD]
 
 `trace` prints the per-kernel call count and average/min/max duration from a
 `--kernel-trace --stats` run.  `counters` turns two `--pmc FETCH_SIZE` and
@@ -10,7 +11,9 @@
 both counters on the run's 256 MiB device-to-device copy (a copy of known size
 reads and writes 262144 KiB): the factor is what the counter reads for that
 copy divided by 262144.  HBM bytes per launch = FETCH/fetch_factor +
-WRITE/write_factor, in KiB.
+WRITE/write_factor, in KiB.  `mfma` summarises a `--pmc MfmaUtil
+SQ_INSTS_VALU_MFMA_MOPS_BF16` run: MFMA utilisation and issued bf16 MFMA flops
+per kernel.
 """
 from __future__ import annotations
 
@@ -72,6 +75,27 @@ def counters_summary(fetch: str, write: str, code_hash: str, cmd: str | None) ->
     return "\n".join(out) + "\n"
 
 
+def mfma_summary(path: str, cmd: str | None) -> str:
+    """Per kernel: the mean MfmaUtil (MFMA-busy cycles over the dispatch's
+    active cycles times the SIMD count, percent) and the bf16 MFMA flops it
+    issued per dispatch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)."""
+    util = _per_kernel(path, "MfmaUtil")
+    mops = _per_kernel(path, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    out = []
+    if cmd:
+        out.append(f"# command: {cmd}")
+    out.append("# kernel | dispatches | MfmaUtil % (mean) | MfmaUtil % (max) | bf16 MFMA GFLOP issued per dispatch (mean)")
+    for name in sorted(set(util) | set(mops)):
+        if not name.startswith("void skg::"):
+            continue
+        u = util.get(name, [])
+        m = mops.get(name, [])
+        out.append(f"kernel {name} | {max(len(u), len(m))} | "
+                   f"{statistics.fmean(u) if u else float('nan'):.2f} | {max(u) if u else float('nan'):.2f} | "
+                   f"{statistics.fmean(m) * 512 / 1e9 if m else float('nan'):.4f}")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -83,9 +107,14 @@ def main(argv=None) -> int:
     c.add_argument("--write", required=True)
     c.add_argument("--code-hash", required=True)
     c.add_argument("--cmd")
+    m = sub.add_parser("mfma")
+    m.add_argument("counters")
+    m.add_argument("--cmd")
     a = ap.parse_args(argv)
     if a.mode == "trace":
         sys.stdout.write(trace_summary(a.stats, a.cmd))
+    elif a.mode == "mfma":
+        sys.stdout.write(mfma_summary(a.counters, a.cmd))
     else:
         sys.stdout.write(counters_summary(a.fetch, a.write, a.code_hash, a.cmd))
     return 0
