@@ -211,7 +211,8 @@ constexpr uint32_t fnv1a(const char* s, uint32_t h = 2166136261u) {
   return h;
 }
 constexpr const char kSpaceText[] =
-    "buckets=1,2,3,4,6,8,12,16,24,32,64,96,128;gemv_mt=1,2,3,4,6,8,12,16;tile_fm=1,2,4,6,8;tile_min=1;"
+    "buckets=1,2,3,4,6,8,12,16,24,32,64,96,128,144,160,176,192,208,224,240,256,288,320,352,384,416,448,480,512;"
+    "gemv_mt=1,2,3,4,6,8,12,16;tile_fm=1,2,4,6,8;tile_min=1;"
 #define SKG_GEMV(name, R, KS, U) "G:" #name "," #R "," #KS "," #U ";"
 #define SKG_TILE(name, FN, KS, U) "T:" #name "," #FN "," #KS "," #U ";"
 #define SKG_TLDS(name, FN, S, P, MC, NW, KW, XD) "L:" #name "," #FN "," #S "," #P "," #MC "," #NW "," #KW "," #XD ";"

@@ -4,6 +4,7 @@
     python -m gemv_skinny_gemm_02_amd.profsum counters --fetch FETCH.csv --write WRITE.csv \
         --code-hash HASH [--cmd CMD]
     python -m gemv_skinny_gemm_02_amd.profsum mfma COUNTERS.csv [--cmd CMD]
+    python -m gemv_skinny_gemm_02_amd.profsum pmc COUNTERS.csv [MORE.csv ...] [--cmd CMD]
 
 `trace` prints the per-kernel call count and average/min/max duration from a
 `--kernel-trace --stats` run.  `counters` turns two `--pmc FETCH_SIZE` and
@@ -96,6 +97,30 @@ def mfma_summary(path: str, cmd: str | None) -> str:
     return "\n".join(out) + "\n"
 
 
+def pmc_summary(paths, cmd: str | None) -> str:
+    """Per kernel, the mean per dispatch of every counter in one or more
+    `--pmc` runs (one column per counter)."""
+    vals = defaultdict(lambda: defaultdict(list))
+    names = []
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            c = r["Counter_Name"]
+            if c not in names:
+                names.append(c)
+            vals[r["Kernel_Name"]][c].append(float(r["Counter_Value"]))
+    out = []
+    if cmd:
+        out.append(f"# command: {cmd}")
+    out.append("# kernel | dispatches | " + " | ".join(names) + "   (mean per dispatch)")
+    for k in sorted(vals):
+        if not k.startswith("void skg::"):
+            continue
+        n = max(len(v) for v in vals[k].values())
+        cells = [f"{statistics.fmean(vals[k][c]):.6g}" if vals[k].get(c) else "nan" for c in names]
+        out.append(f"kernel {k} | {n} | " + " | ".join(cells))
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -107,12 +132,17 @@ def main(argv=None) -> int:
     c.add_argument("--write", required=True)
     c.add_argument("--code-hash", required=True)
     c.add_argument("--cmd")
+    q = sub.add_parser("pmc")
+    q.add_argument("counters", nargs="+")
+    q.add_argument("--cmd")
     m = sub.add_parser("mfma")
     m.add_argument("counters")
     m.add_argument("--cmd")
     a = ap.parse_args(argv)
     if a.mode == "trace":
         sys.stdout.write(trace_summary(a.stats, a.cmd))
+    elif a.mode == "pmc":
+        sys.stdout.write(pmc_summary(a.counters, a.cmd))
     elif a.mode == "mfma":
         sys.stdout.write(mfma_summary(a.counters, a.cmd))
     else:

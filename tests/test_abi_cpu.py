@@ -252,3 +252,12 @@ def test_defaults_follow_the_rows_rule():
     assert q("bf16", 128, 4096, 12288) == "tlds_w8_f1_s4_p4_m4"
     assert q("bf16", 32, 12288, 4096) == "tlds_f1_s2_p4"
     assert q("gated", 32, 12288, 4096) == "tlds_f1_s1_p4"
+
+def test_selection_token_names_the_buckets():
+    """The text the selection-space token hashes lists exactly the rows
+    buckets dispatch uses (a table tuned for another bucket list is refused)."""
+    src = open(os.path.join(ROOT, "gemv_skinny_gemm_02_amd", "csrc", "variants.hpp")).read()
+    arr = re.search(r"kBuckets\[\]\s*=\s*\{([^}]*)\}", src).group(1)
+    buckets = tuple(int(v) for v in arr.replace("\n", " ").split(",") if v.strip())
+    text = re.search(r'"buckets=([0-9,]+);', src).group(1)
+    assert tuple(int(v) for v in text.split(",")) == buckets == skg.BUCKETS
