@@ -143,3 +143,44 @@ def test_pack_refusals():
     assert lib.skinny_gemm_pack_weight(0, w.data_ptr(), buf.data_ptr(), 64, 252, s) == 2          # K multiple
     assert lib.skinny_gemm_pack_weight(17, w.data_ptr(), buf.data_ptr(), 64, 256, s) == 1         # op
     assert skg.skinny_gemm_packed_weight_bytes("bf16", 64, 252) == 0
+
+
+def test_packed_other_forms_full_shapes():
+    """The gate/up 12288 x 4096, the 248320 x 4096 fp8 head and A8W8 with x
+    quantised in the call, at full size on packed weights through table
+    dispatch, as the benchmark times them; sampled columns (the quantising
+    form's x scales bit for bit)."""
+    N, K = synth.GATED_NK
+    base = synth.make_gated(max(synth.GATED_M), N, K, seed=0)
+    wp = skg.skinny_gemm_pack_weight("gated", dev_bf16(base.w))
+    for M in synth.GATED_M:
+        say(f"gated_packed M={M} N={N} K={K} -> {skg.skinny_gemm_query('gated_packed', M, N, K)}")
+        y = skg.skinny_gemm_gated_packed(dev_bf16(base.x[:M]), wp)
+        torch.cuda.synchronize()
+        cols = synth.rows_of(N, 64, seed=M)
+        assert_parity(host_bits(y)[:, cols], oracle.linear_gated(base.x[:M], base.w, cols=cols),
+                      f"gated_packed M={M}")
+    del wp
+    N, K = synth.HEAD_NK
+    head = synth.make_fp8_tensor(max(synth.HEAD_M), N, K, seed=0)
+    wp = skg.skinny_gemm_pack_weight("fp8_tensor", dev_fp8(head.w))
+    s = torch.from_numpy(np.ascontiguousarray(head.s0, dtype=np.float32)).cuda()
+    for M in synth.HEAD_M:
+        say(f"fp8_tensor_packed M={M} N={N} K={K} -> {skg.skinny_gemm_query('fp8_tensor_packed', M, N, K)}")
+        y = skg.skinny_gemm_fp8_tensor_packed(dev_bf16(head.x[:M]), wp, s)
+        torch.cuda.synchronize()
+        cols = synth.rows_of(N, 256, seed=M)
+        assert_parity(host_bits(y)[:, cols], oracle.linear_fp8_tensor(head.x[:M], head.w, head.s0, cols=cols),
+                      f"fp8_tensor_packed M={M}")
+    del wp
+    for (N, K) in synth.A8W8_NK:
+        for M in synth.A8W8_M:
+            p = synth.make_a8w8_quant(M, N, K, seed=0)
+            say(f"a8w8_quant_packed M={M} N={N} K={K} -> {skg.skinny_gemm_query('a8w8_quant_packed', M, N, K)}")
+            x, wpk, xs, ws = to_device_packed(p)
+            y = skg.skinny_gemm_a8w8_block_quant_packed(x, wpk, ws, x_scales=xs)
+            torch.cuda.synchronize()
+            cols = synth.rows_of(N, 64, seed=M)
+            assert_parity(host_bits(y)[:, cols], reference(p, cols=cols), f"a8w8_quant_packed M={M} N={N} K={K}")
+            _, want = oracle.quantize_a8w8_x(p.x)
+            assert np.array_equal(xs.cpu().numpy().view(np.uint32), want.view(np.uint32)), f"x scales M={M}"
