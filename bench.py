@@ -138,6 +138,43 @@ def cpu_baseline(calls, host, seconds: float):
                       f"{len(calls)} calls in step order), float64, {dt:.1f} s"}
 
 
+def cpu_oracle_per_config(seconds: float):
+    """The oracle, as it stands, on one call of each form at M = 1, each on a
+    row sample of its weight (the oracle's work is per weight row), repeated
+    for `seconds` with one BLAS thread and with all of them; algorithmic bytes
+    of the sampled call per second."""
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_info, threadpool_limits
+    all_threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    cases = [
+        ("bf16 4096x4096", "bf16", synth.make_bf16(1, 4096, 4096, seed=0), 4096,
+         lambda p: oracle.linear_bf16(p.x, p.w)),
+        ("gated 12288x4096 (2048 of 12288 rows)", "gated", synth.make_gated(1, 2048, 4096, seed=0), 2048,
+         lambda p: oracle.linear_gated(p.x, p.w)),
+        ("fp8 head 248320x4096 (8192 of 248320 rows)", "fp8_tensor", synth.make_fp8_tensor(1, 8192, 4096, seed=0), 8192,
+         lambda p: oracle.linear_fp8_tensor(p.x, p.w, p.s0)),
+        ("a8w8 8192x4096", "a8w8_block", synth.make_a8w8_block(1, 8192, 4096, seed=0), 8192,
+         lambda p: oracle.linear_a8w8_block(p.x, p.s0, p.w, p.s1)),
+        ("a8w8, x quantised, 8192x4096", "a8w8_quant", synth.make_a8w8_quant(1, 8192, 4096, seed=0), 8192,
+         lambda p: oracle.linear_a8w8_quant(p.x, p.w, p.s1)),
+    ]
+    out = {}
+    for name, form, p, n_rows, fn in cases:
+        nbytes = alg_bytes(1, n_rows, 4096) if form == "bf16" else form_alg_bytes(form, 1, n_rows, 4096)
+        row = {"sample": f"M=1, {n_rows} weight rows, K=4096", "alg_bytes": nbytes}
+        for threads in (1, all_threads):
+            with threadpool_limits(limits=threads, user_api="blas"):
+                calls, t0 = 0, time.perf_counter()
+                while calls == 0 or time.perf_counter() - t0 < seconds:
+                    fn(p)
+                    calls += 1
+                dt = time.perf_counter() - t0
+            row[f"GB/s_{threads}_threads"] = round(nbytes * calls / dt / 1e9, 4)
+        out[name] = row
+    return {"threads": all_threads, "configs": out}
+
+
 def measure_step(args, torch, skg, calls, Ms, stream, launch, op, step_bytes):
     """Time args.steps steps of `calls` launched by `launch(call, copy)` (table
     dispatch of form `op`): returns the step time, its rate and the dominant
@@ -672,6 +709,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(calls, host, args.cpu_seconds)
+        out["cpu_oracle_per_config"] = cpu_oracle_per_config(1.5)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
