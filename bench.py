@@ -328,10 +328,9 @@ def measure_mid_m(args, torch, skg, synth, shapes, wp_dev, stream, ceil):
     """Mid-M rows (speculative verification and drafting) on the sweep shapes:
     µs per call of the packed form through table dispatch, graph replay over
     the same rotated weight copies as the step.  As context, the vendor GEMM
-    (torch.nn.functional.linear, hipBLASLt) timed the same way on the same
-    buffers read as row-major [N, K] bf16 weights: its speed does not depend on
-    the values, so no further copies are needed."""
-    import torch.nn.functional as F
+    (torch.mm of x and the transposed weight, hipBLASLt) timed the same way on
+    the same buffers read as row-major [N, K] bf16 weights: its speed does not
+    depend on the values, so no further copies are needed."""
     out = {}
     Mmax = max(synth.MID_M)
     for (N, K) in shapes:
