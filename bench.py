@@ -416,7 +416,7 @@ def form_alg_bytes(form, M, N, K):
 def measure_forms(args, torch, skg, synth, stream):
     """The other forms at their workload shapes: gate/up 12288 x 4096, the
     248320 x 4096 fp8 head, and A8W8 (and A8W8 with x quantised in the call) at
-    (32768, 1024) and (8192, 4096).  µs per call of the row-major and packed
+    (32768, 1024) and (8192, 4096), A8W8 also at the mid-M rows 144 .. 512.  µs per call of the row-major and packed
     weights through table dispatch, graph replay over >= 1 GiB of rotated
     weight copies, against the read ceiling of the weight.  Inputs are drawn on
     the device from torch's seeded generator with the workload distributions
@@ -442,7 +442,7 @@ def measure_forms(args, torch, skg, synth, stream):
         return q.to(torch.float8_e4m3fn).contiguous(), sc.float().contiguous()
 
     cases = [("gated", synth.GATED_NK, synth.GATED_M), ("fp8_tensor", synth.HEAD_NK, synth.HEAD_M)]
-    cases += [("a8w8_block", nk, synth.A8W8_M) for nk in synth.A8W8_NK]
+    cases += [("a8w8_block", nk, tuple(synth.A8W8_M) + tuple(synth.MID_M)) for nk in synth.A8W8_NK]
     cases += [("a8w8_quant", nk, synth.A8W8_M) for nk in synth.A8W8_NK]
     out = {}
     for form, (N, K), Ms in cases:

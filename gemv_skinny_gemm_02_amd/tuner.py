@@ -45,7 +45,8 @@ def log(*a):
 # ------------------------------------------------------------ workload keys
 def workload_keys(ops, rows="decode"):
     """(op, M, N, K) for every configured workload shape.  rows: "decode" (the
-    decode rows of each form), "mid" (the mid-M rows, bf16 sweep shapes only),
+    decode rows of each form), "mid" (the mid-M rows: bf16 sweep shapes and the
+    A8W8 shapes),
     "smalln" (the small-N bf16 shapes) or "all"."""
     sys.path.insert(0, ROOT)
     import synth
@@ -54,6 +55,9 @@ def workload_keys(ops, rows="decode"):
         for op in ("bf16", "bf16_packed"):
             if op in ops:
                 keys += [(op, M, N, K) for (N, K) in synth.SWEEP_NK for M in synth.MID_M]
+        for op in ("a8w8_block", "a8w8_block_packed"):
+            if op in ops:
+                keys += [(op, M, N, K) for (N, K) in synth.A8W8_NK for M in synth.MID_M]
     if rows in ("smalln", "all"):
         for op in ("bf16", "bf16_packed"):
             if op in ops:

@@ -237,8 +237,9 @@ skg_status skinny_gemm_run_variant(int op, int variant, const int* knobs,
 
 /* Measurement helpers.  They compute nothing of the linear: they give the
  * rates a kernel on this device can reach, against which the linear's
- * kernels are reported (the pages report decode-GEMM rates against the
- * device's bandwidth: Decode optimization round 3, "Retained change 2").
+ * kernels are reported (the pages weigh decode kernels by a per-launch
+ * latency floor against bandwidth: Decode optimization round 3, "Profiling:
+ * why M=1-8 decode is dispatch-bound").
  *
  * skinny_gemm_calib_read: one launch of `grid` workgroups of 256 threads
  * that read every byte of buf[0, bytes) once with 16-byte non-temporal loads,

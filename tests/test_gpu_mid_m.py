@@ -10,7 +10,8 @@ import torch
 import gemv_skinny_gemm_02_amd as skg
 import oracle
 import synth
-from gpu_util import assert_parity, dev_bf16, host_bits, reference, run, run_packed, say, to_device, to_device_packed
+from gpu_util import (assert_parity, dev_bf16, dev_f32, dev_fp8, host_bits, reference, run, run_packed, say, to_device,
+                      to_device_packed)
 
 pytestmark = pytest.mark.gpu
 
@@ -85,3 +86,45 @@ def test_small_n_full_shapes():
             assert_parity(host_bits(yp), ref, f"bf16_packed M={M} N={N} K={K}")
             assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
             assert torch.equal(yp.view(torch.int16), yp2.view(torch.int16))
+
+
+@pytest.mark.parametrize("op", ["a8w8_block", "a8w8_block_packed"])
+def test_every_a8w8_variant_mid_m(op):
+    """A8W8 block scale at mid-M rows (the verify and drafter rows of the A8W8
+    tables), every variant, ragged N and K, element by element."""
+    N, K = 257, 1040
+    names = skg.variants(op)
+    for M in (129, 300):
+        p = synth.make_a8w8_block(M, N, K, seed=6)
+        dev = to_device_packed(p) if op.endswith("_packed") else to_device(p)
+        ref = reference(p)
+        ran = 0
+        for i, name in enumerate(names):
+            if not skg.skinny_gemm_variant_supports(op, i, M):
+                continue
+            say(f"{op} M={M} N={N} K={K} variant={name}")
+            y = run_packed(p, dev, variant=name) if op.endswith("_packed") else run(p, dev, variant=name)
+            torch.cuda.synchronize()
+            assert_parity(host_bits(y), ref, f"{op} {name} M={M}")
+            ran += 1
+        assert ran > 0
+
+
+def test_a8w8_mid_m_full_shapes():
+    """Table dispatch of A8W8 at every mid-M workload row on (32768, 1024) and
+    (8192, 4096), both layouts, sampled columns."""
+    for (N, K) in synth.A8W8_NK:
+        base = synth.make_a8w8_block(max(synth.MID_M), N, K, seed=0)
+        w, ws = dev_fp8(base.w), dev_f32(base.s1)
+        wp = skg.skinny_gemm_pack_weight("a8w8_block", w)
+        for M in synth.MID_M:
+            x, xs = dev_fp8(base.x[:M]), dev_f32(base.s0[:M])
+            cols = synth.rows_of(N, 48, seed=M)
+            ref = oracle.linear_a8w8_block(base.x[:M], base.s0[:M], base.w, base.s1, cols=cols)
+            say(f"a8w8 mid M={M} N={N} K={K} -> {skg.skinny_gemm_query('a8w8_block', M, N, K)}, "
+                f"packed -> {skg.skinny_gemm_query('a8w8_block_packed', M, N, K)}")
+            y = skg.skinny_gemm_a8w8_block(x, w, xs, ws)
+            yp = skg.skinny_gemm_a8w8_block_packed(x, wp, xs, ws)
+            torch.cuda.synchronize()
+            assert_parity(host_bits(y)[:, cols], ref, f"a8w8_block M={M} N={N} K={K}")
+            assert_parity(host_bits(yp)[:, cols], ref, f"a8w8_block_packed M={M} N={N} K={K}")
