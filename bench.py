@@ -516,7 +516,7 @@ def main() -> int:
     ap.add_argument("--rotation-gib", type=float, default=1.0, help="bytes of W copies per shape")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--per-call-replays", type=int, default=5, help="graph replays per call shape")
+    ap.add_argument("--per-call-replays", type=int, default=7, help="graph replays per call shape")
     ap.add_argument("--no-per-call", action="store_true",
                     help="skip the per-call graph timings (profiling runs: keeps every dispatch of a kernel "
                          "in the step's shape mix)")
@@ -599,13 +599,23 @@ def main() -> int:
 
     if args.no_per_call:
         per_call_us = dict(rough_us)
+        per_call_spread, per_call_eager = {}, {}
     else:
         # ------------------------------------------- per-call time (graph replay)
-        per_call_us = {}
+        per_call_us, per_call_spread, per_call_eager = {}, {}, {}
         for c in calls:
             M, N, K = c
             R = len(wp_dev[(N, K)])
             n = max(args.per_call_min, 2 * R)
+            # eager: n launches from the host, no graph, between two events
+            launch(c, 0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(n):
+                launch(c, i)
+            b.record(stream)
+            b.synchronize()
+            per_call_eager[c] = a.elapsed_time(b) * 1e3 / n
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for i in range(n):
@@ -621,6 +631,8 @@ def main() -> int:
                 b.synchronize()
                 ts.append(a.elapsed_time(b) * 1e3 / n)
             per_call_us[c] = statistics.median(ts)
+            ts.sort()
+            per_call_spread[c] = (ts[0], ts[min(len(ts) - 1, int(math.ceil(0.9 * len(ts))) - 1)])
             del g
 
     # ------------------------------------ achievable ceilings on this device
@@ -659,11 +671,16 @@ def main() -> int:
             tfl = 2 * M * N * K / (us * 1e-6) / 1e12
             row[f"{N}x{K}"] = {"us": round(us, 2), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
                                "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4), "variant": choice[c][0]}
+            if c in per_call_spread:
+                row[f"{N}x{K}"]["us_min"] = round(per_call_spread[c][0], 2)
+                row[f"{N}x{K}"]["us_p90"] = round(per_call_spread[c][1], 2)
+                row[f"{N}x{K}"]["eager_us"] = round(per_call_eager[c], 2)
             if ceil is not None:
                 row[f"{N}x{K}"]["read_ceiling_frac"] = round(ceil["read"][(N, K)]["us"] / us, 3)
                 row[f"{N}x{K}"]["mfma_ceiling_frac"] = round(tfl / ceil["mfma_bf16_tflops"], 4)
         detail[f"M={M}"] = row
     all_calls = {f"{M}x{N}x{K}": round(per_call_us[(M, N, K)], 2) for (M, N, K) in calls}
+    all_eager = {f"{M}x{N}x{K}": round(v, 2) for (M, N, K), v in per_call_eager.items()}
 
     out = {
         "metric": METRIC,
@@ -704,6 +721,7 @@ def main() -> int:
         "small_n": small_n,
         "forms": forms,
         "per_call_us": all_calls,
+        "per_call_eager_us": all_eager or None,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

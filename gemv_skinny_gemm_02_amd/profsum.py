@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 output for this library's kernels.
 
-    python -m gemv_skinny_gemm_02_amd.profsum trace KERNEL_STATS.csv [--cmd CMD]
+    python -m gemv_skinny_gemm_02_amd.profsum trace KERNEL_STATS.csv [--dispatches KERNEL_TRACE.csv] [--cmd CMD]
     python -m gemv_skinny_gemm_02_amd.profsum counters --fetch FETCH.csv --write WRITE.csv \
         --code-hash HASH [--cmd CMD]
     python -m gemv_skinny_gemm_02_amd.profsum mfma COUNTERS.csv [--cmd CMD]
@@ -28,15 +28,24 @@ COPY_KIB = 256 * 1024
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
-def trace_summary(path: str, cmd: str | None) -> str:
+def trace_summary(path: str, cmd: str | None, dispatches: str | None = None) -> str:
+    """Per kernel from the --stats file; with the per-dispatch trace file also
+    the median device duration."""
     rows = list(csv.DictReader(open(path)))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    med = {}
+    if dispatches:
+        durs = defaultdict(list)
+        for r in csv.DictReader(open(dispatches)):
+            durs[r["Kernel_Name"]].append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+        med = {k: statistics.median(v) for k, v in durs.items()}
     out = []
     if cmd:
         out.append(f"# command: {cmd}")
-    out.append("# kernel | calls | avg_us | min_us | max_us | total_ms | percent")
+    out.append("# kernel | calls | avg_us | median_us | min_us | max_us | total_ms | percent")
     for r in rows:
-        out.append(f"{r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | {float(r['MinNs']) / 1e3:.3f} | "
+        m = f"{med[r['Name']] / 1e3:.3f}" if r["Name"] in med else "nan"
+        out.append(f"{r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | {m} | {float(r['MinNs']) / 1e3:.3f} | "
                    f"{float(r['MaxNs']) / 1e3:.3f} | {float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f}")
     return "\n".join(out) + "\n"
 
@@ -126,6 +135,7 @@ def main(argv=None) -> int:
     sub = ap.add_subparsers(dest="mode", required=True)
     t = sub.add_parser("trace")
     t.add_argument("stats")
+    t.add_argument("--dispatches", help="the per-dispatch kernel trace csv, for the median")
     t.add_argument("--cmd")
     c = sub.add_parser("counters")
     c.add_argument("--fetch", required=True)
@@ -140,7 +150,7 @@ def main(argv=None) -> int:
     m.add_argument("--cmd")
     a = ap.parse_args(argv)
     if a.mode == "trace":
-        sys.stdout.write(trace_summary(a.stats, a.cmd))
+        sys.stdout.write(trace_summary(a.stats, a.cmd, a.dispatches))
     elif a.mode == "pmc":
         sys.stdout.write(pmc_summary(a.counters, a.cmd))
     elif a.mode == "mfma":
