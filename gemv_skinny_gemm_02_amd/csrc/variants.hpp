@@ -18,7 +18,8 @@ enum Family : int { FAM_GEMV = 0, FAM_TILE = 1, FAM_TLDS = 2 };
 // nearest fallback: Decode optimization round 3, "Retained change 2";
 // rows 3, 6 and 12 as in mstar PR #1102, "What changed").  Above the decode
 // rows, the mid-M rows of speculative verification and drafting: steps of 16
-// up to 256 and of 32 up to 512 (the padded-M buckets of the same section).
+// up to 256 and of 32 up to 512 (the padded-M grid the verify and drafter
+// rows were tuned at: the same page, "Retained change 3").
 constexpr int kBuckets[] = {1,   2,   3,   4,   6,   8,   12,  16,  24,  32,  64,  96,  128, 144, 160,
                             176, 192, 208, 224, 240, 256, 288, 320, 352, 384, 416, 448, 480, 512};
 constexpr int kNumBuckets = sizeof(kBuckets) / sizeof(kBuckets[0]);

@@ -50,7 +50,9 @@
  *           fault inside a kernel surfaces at the caller's next synchronisation.
  * Dispatch. Each call rounds M up to its rows bucket {1,2,3,4,6,8,12,16,24,32,
  *           64,96,128}, or for mid-M rows {144,160,...,256} (steps of 16) and
- *           {288,320,...,512} (steps of 32), and looks (op, bucket, N, K) up in
+ *           {288,320,...,512} (steps of 32: the verify and drafter grid of
+ *           Decode optimization round 3, "Retained change 3"), and looks
+ *           (op, bucket, N, K) up in
  *           the per-device table (Decode optimization round 3, "Retained
  *           change 2": padded-M lookup with no nearest fallback; mstar PR
  *           #1104, "What changed": one per-device table).  A miss, an absent

@@ -94,7 +94,9 @@ def test_table_engaged_lookup_and_buckets(tmp_path):
 def test_mid_m_buckets(tmp_path):
     """The binding's bucket list is the library's: a table entry at every
     bucket engages, rows between buckets are refused, and M above 128 rounds
-    up to its mid-M bucket (steps of 16 to 256, of 32 to 512)."""
+    up to its mid-M bucket (steps of 16 to 256, of 32 to 512: the grid the
+    decode page tunes its verify and drafter rows at, Decode optimization
+    round 3, "Retained change 3")."""
     assert skg.BUCKETS[:13] == (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 64, 96, 128)
     assert skg.BUCKETS[13:] == tuple(range(144, 257, 16)) + tuple(range(288, 513, 32))
     ident = _identity()
