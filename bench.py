@@ -18,9 +18,12 @@ Beside the nominal peaks it reports what a kernel can reach on the device: the
 fastest plain read of each shape's rotated weight copies and the rate of a
 register-only bf16 MFMA loop (the library's measurement kernels).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--detail PATH] [--verbose]
 
-Prints one JSON line on stdout; progress goes to stderr.
+Prints one compact JSON line on stdout (the headline metric, the dominant
+kernel's roofline, the CPU oracle's rate and the M = 1/8/128 calls); the
+per-call, mid-M, small-N and other-form reports go to the file named by
+--detail.  Progress goes to stderr with --verbose.
 """
 from __future__ import annotations
 
@@ -44,8 +47,12 @@ READ_GRIDS = (512, 1024, 2048, 4096, 8192)   # workgroup counts tried for a read
 METRIC = "achieved HBM GB/s and µs/call at M=1/8/128; fraction of MI355X roofline"
 
 
+VERBOSE = False
+
+
 def log(*a):
-    print(*a, file=sys.stderr, flush=True)
+    if VERBOSE:
+        print(*a, file=sys.stderr, flush=True)
 
 
 def alg_bytes(M, N, K):
@@ -111,31 +118,61 @@ def read_counters(kernel: str, code_hash: str):
     return (fetch_kib / ff + write_kib / wf) * 1024.0
 
 
-def cpu_baseline(calls, host, seconds: float):
-    """The oracle, as it stands, run over the step's calls in step order,
-    pass after pass, until `seconds` of CPU time have been spent (the last pass
-    may stop part-way); reported as algorithmic bytes per second."""
-    import oracle
+def host_cores() -> int:
+    """CPU cores this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def blas_threads() -> int:
+    """Threads of the BLAS pool the oracle's float64 products run on."""
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
-        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
-    ncalls, nbytes, t0 = 0, 0, time.perf_counter()
-    while True:
-        for (M, N, K) in calls:
-            xb, wb = host[(N, K)]
-            oracle.linear_bf16(xb[:M], wb)
-            nbytes += alg_bytes(M, N, K)
-            ncalls += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{ncalls} oracle.linear_bf16 calls ({ncalls / len(calls):.2f} passes over the step's "
-                      f"{len(calls)} calls in step order), float64, {dt:.1f} s"}
+        return int(os.environ.get("OMP_NUM_THREADS", "1"))
+
+
+def cpu_baseline(calls, host, seconds: float, runs: int = 3):
+    """The oracle, as it stands, run over the step's calls in step order, pass
+    after pass, for `seconds` of wall time per run (the last pass may stop
+    part-way): the median of `runs` runs, in algorithmic bytes per second.
+    Beside it, the two parts of the oracle's work timed apart on one weight of
+    each shape: decoding the bf16 weight to float64, and the float64 product
+    (one call at M = 8)."""
+    import oracle
+    rates, ncalls_all = [], []
+    for _ in range(runs):
+        ncalls, nbytes, t0 = 0, 0, time.perf_counter()
+        done = False
+        while not done:
+            for (M, N, K) in calls:
+                xb, wb = host[(N, K)]
+                oracle.linear_bf16(xb[:M], wb)
+                nbytes += alg_bytes(M, N, K)
+                ncalls += 1
+                if time.perf_counter() - t0 >= seconds:
+                    done = True
+                    break
+        rates.append(nbytes / (time.perf_counter() - t0) / 1e9)
+        ncalls_all.append(ncalls)
+    split = {}
+    for (N, K), (xb, wb) in host.items():
+        t0 = time.perf_counter()
+        wd = oracle.dec_bf16(wb)
+        t1 = time.perf_counter()
+        _ = oracle.dec_bf16(xb[:8]) @ wd.T
+        t2 = time.perf_counter()
+        split[f"{N}x{K}"] = {"decode_s": round(t1 - t0, 4), "product_s_M8": round(t2 - t1, 4)}
+        del wd
+    threads = min(blas_threads(), host_cores())
+    return {"value": round(statistics.median(rates), 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"median of {runs} runs of {seconds:.0f} s, each the step's {len(calls)} calls in order "
+                      f"({min(ncalls_all)}-{max(ncalls_all)} calls), oracle.linear_bf16 in float64 on "
+                      f"{threads} BLAS threads of {host_cores()} host cores",
+            "runs_GBs": [round(r, 4) for r in rates], "decode_vs_product": split}
 
 
 def cpu_oracle_per_config(seconds: float):
@@ -145,8 +182,8 @@ def cpu_oracle_per_config(seconds: float):
     of the sampled call per second."""
     import oracle
     import synth
-    from threadpoolctl import threadpool_info, threadpool_limits
-    all_threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    from threadpoolctl import threadpool_limits
+    all_threads = min(blas_threads(), host_cores())
     cases = [
         ("bf16 4096x4096", "bf16", synth.make_bf16(1, 4096, 4096, seed=0), 4096,
          lambda p: oracle.linear_bf16(p.x, p.w)),
@@ -173,6 +210,38 @@ def cpu_oracle_per_config(seconds: float):
             row[f"GB/s_{threads}_threads"] = round(nbytes * calls / dt / 1e9, 4)
         out[name] = row
     return {"threads": all_threads, "configs": out}
+
+
+WORKLOAD = ("bf16 decode-linear sweep, seed 0: M in {1,2,3,4,6,8,12,16,24,32,64,96,128} x (N,K) in "
+            "{4096x4096, 6144x4096, 4096x12288, 2048x2048, 1024x1024}, x~N(0,1), W~N(0,0.02), 65 calls/step, "
+            "packed weights rotated past the Infinity Cache")
+
+
+def make_line(value, ms_step, steps, warmup, ncalls, roofline, per_m, cpu=None) -> dict:
+    """The one JSON line the benchmark prints: the headline metric and its
+    configuration, the dominant kernel's roofline, the M = 1/8/128 calls as
+    [µs, GB/s] per shape, and the CPU oracle's rate (added when measured).
+    Everything else goes to the detail file, so that the line stays short."""
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "calls_per_step": ncalls},
+        "roofline": roofline,
+        "per_m_us_gbs": per_m,
+    }
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    return line
 
 
 def measure_step(args, torch, skg, calls, Ms, stream, launch, op, step_bytes):
@@ -266,6 +335,17 @@ def measure_step(args, torch, skg, calls, Ms, stream, launch, op, step_bytes):
             "rough_us": rough_us, "ms_step": ms_step, "dom_us": dom_us, "value": value}
 
 
+_WS_BYTES = [0]
+
+
+def ensure_ws(skg, need: int) -> None:
+    """Register a larger device split-K workspace when `need` exceeds the
+    current one (the binding keeps the old one alive)."""
+    if need > _WS_BYTES[0]:
+        skg.skinny_gemm_set_device_workspace(max(need, 1 << 20))
+        _WS_BYTES[0] = max(need, 1 << 20)
+
+
 def _graph_us(torch, stream, n, enqueue, replays):
     """Median µs per launch of a graph of n launches enqueue(i)."""
     g = torch.cuda.CUDAGraph()
@@ -324,6 +404,42 @@ def measure_ceilings(args, torch, skg, shapes, wp_dev, stream):
     return {"read": read, "mfma_bf16_tflops": mfma_tflops}
 
 
+def measure_host_cost(torch, skg, x_dev, wp_dev, y_dev, stream, n=2000):
+    """Host cost of an eager call: µs per launch of n back-to-back launches
+    from the host (no graph), for a near-empty kernel (one workgroup of the
+    MFMA measurement kernel) and for the packed bf16 call on 1024 x 1024 at
+    M = 1, each through the Python binding and through the bare C entry
+    point with its arguments prepared once."""
+    import ctypes
+    lib = skg.load()
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    M, N, K = 1, 1024, 1024
+    x, wp, y = x_dev[K][:M], wp_dev[(N, K)][0], y_dev[(M, N)]
+    sp = stream.cuda_stream
+    xp, wpp, yp, skp = x.data_ptr(), wp.data.data_ptr(), y.data_ptr(), sink.data_ptr()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        host_us = (time.perf_counter() - t0) * 1e6 / n
+        b.synchronize()
+        return round(a.elapsed_time(b) * 1e3 / n, 3), round(host_us, 3)
+
+    rows = {
+        "empty_kernel_binding": timed(lambda: skg.skinny_gemm_calib_mfma(1, 1, sink)),
+        "empty_kernel_c": timed(lambda: lib.skinny_gemm_calib_mfma(1, 1, skp, sp)),
+        "bf16_packed_1024_M1_binding": timed(lambda: skg.skinny_gemm_bf16_packed(x, wp, y=y)),
+        "bf16_packed_1024_M1_c": timed(lambda: lib.skinny_gemm_bf16_packed(xp, wpp, None, yp, M, N, K, sp)),
+    }
+    return {"launches": n, "unit": "µs per launch: (device events, host issue time)", "rows": rows}
+
+
 def measure_mid_m(args, torch, skg, synth, shapes, wp_dev, stream, ceil):
     """Mid-M rows (speculative verification and drafting) on the sweep shapes:
     µs per call of the packed form through table dispatch, graph replay over
@@ -333,6 +449,7 @@ def measure_mid_m(args, torch, skg, synth, shapes, wp_dev, stream, ceil):
     depend on the values, so no further copies are needed."""
     out = {}
     Mmax = max(synth.MID_M)
+    ensure_ws(skg, max(skg.skinny_gemm_workspace_bytes("bf16_packed", M, N, K) for (N, K) in shapes for M in synth.MID_M))
     for (N, K) in shapes:
         x = torch.from_numpy(synth.make_bf16(Mmax, 16, K, seed=0).x.view(np.int16)).view(torch.bfloat16).cuda()
         ws = wp_dev[(N, K)]
@@ -371,6 +488,8 @@ def measure_small_n(args, torch, skg, synth, stream):
     sink = torch.empty(256, dtype=torch.int32, device="cuda")
     out = {}
     Mmax = max(synth.SMALLN_M)
+    ensure_ws(skg, max(skg.skinny_gemm_workspace_bytes(op, M, N, K) for (N, K) in synth.SMALLN_NK
+                       for M in synth.SMALLN_M for op in ("bf16", "bf16_packed")))
     for (N, K) in synth.SMALLN_NK:
         p = synth.make_bf16(Mmax, N, K, seed=0)
         x = torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).cuda()
@@ -447,6 +566,8 @@ def measure_forms(args, torch, skg, synth, stream):
     out = {}
     for form, (N, K), Ms in cases:
         Mmax = max(Ms)
+        ensure_ws(skg, max(skg.skinny_gemm_workspace_bytes(op, M, N, K) for M in Ms
+                           for op in (form, form + "_packed")))
         s0 = s1 = None
         if form == "gated":
             w0 = normal((2 * N, K), 0.02).to(torch.bfloat16)
@@ -526,7 +647,11 @@ def main() -> int:
     ap.add_argument("--no-forms", action="store_true", help="skip the gated / fp8 head / A8W8 report")
     ap.add_argument("--no-row-major", action="store_true",
                     help="skip the row-major step (profiling runs of the packed layout)")
+    ap.add_argument("--detail", default=None, help="write the full report (JSON) to this file")
+    ap.add_argument("--verbose", action="store_true", help="progress on stderr")
     args = ap.parse_args()
+    global VERBOSE
+    VERBOSE = args.verbose
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: the skinny linear is measured on one MI355X "
@@ -575,6 +700,9 @@ def main() -> int:
 
     stream = torch.cuda.current_stream()
     step_bytes = sum(alg_bytes(*c) for c in calls)
+    # the split-K workspace of the device: the largest any call here needs
+    # (the forms, mid-M and small-N reports register their own when larger)
+    ensure_ws(skg, max(skg.skinny_gemm_workspace_bytes(op, *c) for c in calls for op in ("bf16", "bf16_packed")))
 
     def launcher(packed):
         def launch(c, copy):
@@ -635,6 +763,8 @@ def main() -> int:
             per_call_spread[c] = (ts[0], ts[min(len(ts) - 1, int(math.ceil(0.9 * len(ts))) - 1)])
             del g
 
+    host_cost = None if args.no_per_call else measure_host_cost(torch, skg, x_dev, wp_dev, y_dev, stream)
+
     # ------------------------------------ achievable ceilings on this device
     # (profiling runs skip them, so that every dispatch profiled is the step's)
     ceil = None if args.no_per_call else measure_ceilings(args, torch, skg, shapes, wp_dev, stream)
@@ -662,8 +792,9 @@ def main() -> int:
     code_hash = lib_code_hash()
     traffic = read_counters(dominant, code_hash)
     detail = {}
+    compact = {}
     for M in (1, 8, 128):
-        row = {}
+        row, crow = {}, {}
         for (N, K) in shapes:
             c = (M, N, K)
             us = per_call_us[c]
@@ -671,6 +802,7 @@ def main() -> int:
             tfl = 2 * M * N * K / (us * 1e-6) / 1e12
             row[f"{N}x{K}"] = {"us": round(us, 2), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
                                "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4), "variant": choice[c][0]}
+            crow[f"{N}x{K}"] = [round(us, 2), round(gbs)]
             if c in per_call_spread:
                 row[f"{N}x{K}"]["us_min"] = round(per_call_spread[c][0], 2)
                 row[f"{N}x{K}"]["us_p90"] = round(per_call_spread[c][1], 2)
@@ -679,44 +811,35 @@ def main() -> int:
                 row[f"{N}x{K}"]["read_ceiling_frac"] = round(ceil["read"][(N, K)]["us"] / us, 3)
                 row[f"{N}x{K}"]["mfma_ceiling_frac"] = round(tfl / ceil["mfma_bf16_tflops"], 4)
         detail[f"M={M}"] = row
+        compact[str(M)] = crow
     all_calls = {f"{M}x{N}x{K}": round(per_call_us[(M, N, K)], 2) for (M, N, K) in calls}
     all_eager = {f"{M}x{N}x{K}": round(v, 2) for (M, N, K), v in per_call_eager.items()}
 
-    out = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "bf16 decode-linear sweep: M in {1,2,3,4,6,8,12,16,24,32,64,96,128} x (N,K) in "
-                               "{(4096,4096),(6144,4096),(4096,12288),(2048,2048),(1024,1024)}, x~N(0,1), "
-                               "W~N(0,0.02), seed 0, 65 calls per step, weights rotated past the Infinity Cache",
-                   "weight_layout": "fragment-packed (skinny_gemm_pack_weight once per weight copy, before "
-                                    "timing; the same bytes)",
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": round(traffic) if traffic is not None else None,
+                "kernel": dominant, "launches_per_step": len(dom_calls), "avg_launch_us": round(dom_us, 3),
+                "alg_bytes_per_launch": round(dom_bytes)}
+    line = make_line(value, ms_step, args.steps, args.warmup, len(calls), roofline, compact)
+    full = {
+        **line,
+        "config": {"workload": WORKLOAD, "weight_layout": "fragment-packed (skinny_gemm_pack_weight once per weight "
+                                                          "copy, before timing; the same bytes)",
                    "calls_per_step": len(calls), "alg_bytes_per_step": step_bytes, "device": dev_name,
                    "table": skg.skinny_gemm_table_status()[1]},
         "row_major": row_major,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": round(traffic) if traffic is not None else None,
-                     "kernel": dominant, "launches_per_step": len(dom_calls), "avg_launch_us": round(dom_us, 3),
-                     "alg_bytes_per_launch": round(dom_bytes), "code_hash": code_hash,
+        "roofline": {**roofline, "code_hash": code_hash,
                      "achievable": None if achievable is None else
                      {"GB/s": round(achievable, 1), "frac": round(achieved / achievable, 4),
                       "basis": "the same launches at each shape's plain-read time of its weight "
-                               "(skinny_gemm_calib_read, graph replay, best of 512..8192 workgroups in slices or one sweep)"}},
+                               "(skinny_gemm_calib_read, graph replay, best of 512..8192 workgroups in slices or "
+                               "one sweep)"}},
         "ceilings": None if ceil is None else
         {"read": {f"{N}x{K}": v for (N, K), v in ceil["read"].items()},
          "mfma_bf16_tflops": round(ceil["mfma_bf16_tflops"], 1),
          "mfma_bf16_frac_of_peak": round(ceil["mfma_bf16_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)},
         "per_m": detail,
+        "host_cost": host_cost,
         "mid_m": mid,
         "small_n": small_n,
         "forms": forms,
@@ -725,11 +848,17 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        out["cpu_baseline"] = cpu_baseline(calls, host, args.cpu_seconds)
-        out["cpu_oracle_per_config"] = cpu_oracle_per_config(1.5)
+        cb = cpu_baseline(calls, host, args.cpu_seconds / 3)
+        full["cpu_baseline"] = cb
+        full["cpu_oracle_per_config"] = cpu_oracle_per_config(1.5)
+        line["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
     else:
-        out["cpu_baseline"] = None
-    print(json.dumps(out), flush=True)
+        full["cpu_baseline"] = line["cpu_baseline"] = None
+    if args.detail:
+        os.makedirs(os.path.dirname(os.path.abspath(args.detail)), exist_ok=True)
+        with open(args.detail, "w") as f:
+            json.dump(full, f, indent=1)
+    print(json.dumps(line, separators=(",", ":")), flush=True)
     return 0
 
 

@@ -14,6 +14,13 @@ Entry points (see include/skinny_gemm.h for the contract):
     skinny_gemm_a8w8_block(x, W, x_scales, w_scales)
     skinny_gemm_a8w8_block_quant(x, W, w_scales)   bf16 x quantised in the call
 each returning y [M, N] bf16 (or writing into ``y=``).
+
+Variants that split K across workgroups need a split-K workspace: device
+memory the caller registers once, per stream (skinny_gemm_set_workspace) or
+per device (skinny_gemm_set_device_workspace); skinny_gemm_workspace_bytes
+says how much a call needs.  The binding keeps every workspace tensor it
+registered alive until the process ends, so that graphs captured with it stay
+valid.
 """
 from __future__ import annotations
 
@@ -34,6 +41,8 @@ __all__ = [
     "skinny_gemm_identity", "skinny_gemm_table_status", "skinny_gemm_num_variants",
     "skinny_gemm_variant_name", "skinny_gemm_variant_supports", "variants", "default_table_path",
     "skinny_gemm_calib_read", "skinny_gemm_calib_mfma", "CALIB_MFMA_FLOPS_PER_ITER_WG",
+    "skinny_gemm_workspace_bytes", "skinny_gemm_variant_workspace_bytes", "skinny_gemm_set_workspace",
+    "skinny_gemm_set_device_workspace",
 ]
 
 # Rows buckets of dispatch (the library's list): M rounds up to the next one;
@@ -123,6 +132,14 @@ def load() -> ctypes.CDLL:
         lib.skinny_gemm_calib_read.restype = i
         lib.skinny_gemm_calib_mfma.argtypes = [i, i, vp, vp]
         lib.skinny_gemm_calib_mfma.restype = i
+        lib.skinny_gemm_workspace_bytes.argtypes = [i, i, i, i]
+        lib.skinny_gemm_workspace_bytes.restype = ctypes.c_size_t
+        lib.skinny_gemm_variant_workspace_bytes.argtypes = [i, i, i, i]
+        lib.skinny_gemm_variant_workspace_bytes.restype = ctypes.c_size_t
+        lib.skinny_gemm_set_workspace.argtypes = [vp, vp, ctypes.c_size_t]
+        lib.skinny_gemm_set_workspace.restype = i
+        lib.skinny_gemm_set_device_workspace.argtypes = [vp, ctypes.c_size_t, vp]
+        lib.skinny_gemm_set_device_workspace.restype = i
         _LIB = lib
         return lib
 
@@ -405,6 +422,66 @@ def skinny_gemm_variant_supports(op, i: int, M: int) -> bool:
 
 def variants(op=0) -> list:
     return [skinny_gemm_variant_name(op, i) for i in range(skinny_gemm_num_variants(op))]
+
+
+# ------------------------------------------------------ split-K workspace
+_HELD = []            # every workspace tensor registered through the binding
+
+
+def _opi(op) -> int:
+    return OPS[op] if isinstance(op, str) else int(op)
+
+
+def skinny_gemm_workspace_bytes(op, M: int, N: int, K: int) -> int:
+    """Bytes of split-K workspace the call (op, M, N, K) needs under the
+    current dispatch (0 if none)."""
+    return int(load().skinny_gemm_workspace_bytes(_opi(op), M, N, K))
+
+
+def skinny_gemm_variant_workspace_bytes(op, variant, M: int, N: int) -> int:
+    """Bytes of split-K workspace one variant needs at M rows and N outputs."""
+    if isinstance(variant, str):
+        variant = variants(op).index(variant)
+    return int(load().skinny_gemm_variant_workspace_bytes(_opi(op), int(variant), M, N))
+
+
+def _ws_tensor(ws, device):
+    if ws is None:
+        return None
+    if isinstance(ws, int):
+        n = max(int(ws), 256 << 10)
+        ws = torch.empty((n + 255) // 256 * 256, dtype=torch.uint8, device=device)
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("a workspace is a byte count or a contiguous device tensor")
+    return ws
+
+
+def skinny_gemm_set_workspace(ws, stream=None) -> torch.Tensor | None:
+    """Register a split-K workspace for the calls on `stream` (default: the
+    current stream): a device tensor, or a byte count to allocate one of;
+    None removes the stream's registration.  Returns the tensor."""
+    t = _ws_tensor(ws, torch.device("cuda", torch.cuda.current_device()))
+    _check(load().skinny_gemm_set_workspace(_stream(stream), t.data_ptr() if t is not None else None,
+                                            t.numel() * t.element_size() if t is not None else 0))
+    if t is not None:
+        _HELD.append(t)
+    return t
+
+
+def skinny_gemm_set_device_workspace(ws, stream=None) -> torch.Tensor | None:
+    """Register the current device's split-K workspace (used by every stream
+    without one of its own): a device tensor, or a byte count to allocate one
+    of; None removes it.  Its counters are cleared on `stream` (default: the
+    current stream), which is synchronised before returning so that calls on
+    any stream see them cleared.  Returns the tensor."""
+    t = _ws_tensor(ws, torch.device("cuda", torch.cuda.current_device()))
+    _check(load().skinny_gemm_set_device_workspace(t.data_ptr() if t is not None else None,
+                                                   t.numel() * t.element_size() if t is not None else 0,
+                                                   _stream(stream)))
+    if t is not None:
+        _HELD.append(t)
+        torch.cuda.synchronize()
+    return t
 
 
 # ------------------------------------------------------ measurement helpers

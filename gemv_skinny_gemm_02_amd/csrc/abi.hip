@@ -1,27 +1,49 @@
 // abi.hip -- the C entry points declared in include/skinny_gemm.h: argument
-// checks, dispatch (rows bucket -> table or default variant), launch.
+// checks, dispatch (rows bucket -> table or default variant), the split-K
+// workspaces, launch.
+//
+// A GEMM call allocates nothing, frees nothing and never synchronises: the
+// only device memory it touches beyond its arguments is the split-K workspace
+// that the caller registered (skinny_gemm_set_workspace).  Which kernel runs is
+// a pure function of (op, rows bucket, N, K, table).
 #include <dlfcn.h>
 
+#include <atomic>
 #include <cctype>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <set>
 #include <string>
 #include <tuple>
+#include <unordered_map>
+#include <vector>
 
 #include "kernels.hpp"
 #include "skinny_gemm.h"
 #include "table.hpp"
+
+// Split-K workspace layout: kSplitCounters arrival
+// counters (one per output tile, zero between calls), then the fp32 partials
+// [S][G][M][N] of the call.
+constexpr size_t kCntBytes = (size_t)skg::kSplitCounters * sizeof(unsigned);
 
 namespace skg {
 
 __global__ void zero_kernel(unsigned short* y, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     y[i] = 0;
+}
+
+// Clears n words (the arrival counters of a workspace).  A kernel, not
+// hipMemsetAsync, so that it is an ordinary node if a caller captures it.
+__global__ void zero_words_kernel(unsigned* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
 }
 
 namespace {
@@ -38,9 +60,22 @@ skg_status fail(skg_status st, const char* fmt, ...) {
   return st;
 }
 
-std::mutex g_mu;
-Table g_table;
-bool g_table_tried = false;  // a load (explicit or lazy) has happened
+// ------------------------------------------------- process-wide settings
+// Read once: the dispatch override and the dispatch log.
+struct Settings {
+  int force = -1;    // $SKINNY_GEMM_FORCE as a variant index, or -1
+  bool log = false;  // $SKINNY_GEMM_LOG set and not "0"
+};
+const Settings& settings() {
+  static const Settings s = [] {
+    Settings t;
+    t.force = forced_variant();
+    const char* lg = std::getenv("SKINNY_GEMM_LOG");
+    t.log = lg && *lg && *lg != '0';
+    return t;
+  }();
+  return s;
+}
 
 std::string hex32(uint32_t v) {
   char b[16];
@@ -59,7 +94,7 @@ std::string self_dir() {
 }
 
 // Device facts for the identity and the default table path.
-bool device_facts(std::string* arch, std::string* product, std::string* hipver) {
+bool device_facts(std::string* arch, std::string* hipver) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) { (void)hipGetLastError(); return false; }
   hipDeviceProp_t p;
@@ -67,17 +102,6 @@ bool device_facts(std::string* arch, std::string* product, std::string* hipver) 
   std::string a = p.gcnArchName;
   const size_t c = a.find(':');
   *arch = c == std::string::npos ? a : a.substr(0, c);
-  std::string name = p.name, low;
-  for (char ch : name) low.push_back(static_cast<char>(std::tolower(static_cast<unsigned char>(ch))));
-  *product = "unknown";
-  for (size_t i = 0; i + 2 < low.size(); ++i) {
-    if (low[i] == 'm' && low[i + 1] == 'i' && std::isdigit(static_cast<unsigned char>(low[i + 2]))) {
-      size_t j = i + 2;
-      while (j < low.size() && std::isalnum(static_cast<unsigned char>(low[j]))) ++j;
-      *product = low.substr(i, j - i);
-      break;
-    }
-  }
   int rt = 0;
   if (hipRuntimeGetVersion(&rt) != hipSuccess) { (void)hipGetLastError(); rt = 0; }
   *hipver = std::to_string(rt);
@@ -90,60 +114,109 @@ std::string compiler_token() { return hex32(fnv1a(__clang_version__ " hip " SKG_
 
 std::string space_token() { return hex32(kSpaceToken); }
 
-bool self_identity(Identity* id, std::string* product) {
-  std::string arch, prod, hipv;
-  if (!device_facts(&arch, &prod, &hipv)) return false;
+bool self_identity(Identity* id) {
+  std::string arch, hipv;
+  if (!device_facts(&arch, &hipv)) return false;
   id->arch = arch;
   id->hip = hipv;
   id->cc = compiler_token();
   id->space = space_token();
-  if (product) *product = prod;
   return true;
 }
 
-// Lazy table load on the first dispatch: $SKINNY_GEMM_TABLE, else the table
-// installed beside the library for this device.  Caller holds g_mu.
-void ensure_table_locked() {
-  if (g_table_tried) return;
-  g_table_tried = true;
-  Identity id;
-  std::string product;
-  if (!self_identity(&id, &product)) return;
-  std::string path;
-  if (const char* e = std::getenv("SKINNY_GEMM_TABLE"); e && *e) path = e;
-  else path = self_dir() + "/configs/" + id.arch + "/skinny_gemm.json";
-  (void)product;
-  FILE* f = std::fopen(path.c_str(), "rb");
-  if (!f) return;  // no table: defaults
-  std::fclose(f);
-  std::string err;
-  if (g_table.load(path, id, &err) != 0)
-    std::fprintf(stderr, "skinny_gemm: table %s not loaded: %s; built-in defaults stay in effect\n", path.c_str(),
-                 err.c_str());
+// ------------------------------------------------------------ dispatch
+// One immutable table snapshot plus the decisions taken under it.  A load
+// builds a new snapshot and publishes it; the old one is kept (never freed),
+// so a call that read the old pointer keeps a valid object.  Loads must not
+// run concurrently with calls (the header says so); the snapshot makes the
+// calls themselves lock-free on the table.
+struct Snapshot {
+  Table table;
+  mutable std::mutex mu;                                   // guards `cache`
+  mutable std::unordered_map<uint64_t, int> cache;         // (op, bucket, N, K) -> variant
+};
+
+std::mutex g_mu;                                            // serialises loads
+std::vector<std::unique_ptr<Snapshot>> g_snapshots;        // every snapshot ever published
+std::atomic<const Snapshot*> g_snap{nullptr};
+
+void publish(std::unique_ptr<Snapshot> s) {   // caller holds g_mu
+  g_snap.store(s.get(), std::memory_order_release);
+  g_snapshots.push_back(std::move(s));
 }
 
-std::set<std::tuple<int, int, int, int, int>> g_logged;
+// The first dispatch loads $SKINNY_GEMM_TABLE, else the table installed beside
+// the library for this device.  Caller holds g_mu.
+void lazy_load_locked() {
+  auto s = std::make_unique<Snapshot>();
+  Identity id;
+  if (self_identity(&id)) {
+    std::string path;
+    if (const char* e = std::getenv("SKINNY_GEMM_TABLE"); e && *e) path = e;
+    else path = self_dir() + "/configs/" + id.arch + "/skinny_gemm.json";
+    if (FILE* f = std::fopen(path.c_str(), "rb")) {
+      std::fclose(f);
+      std::string err;
+      if (s->table.load(path, id, &err) != 0)
+        std::fprintf(stderr, "skinny_gemm: table %s not loaded: %s; built-in defaults stay in effect\n",
+                     path.c_str(), err.c_str());
+    }
+  }
+  publish(std::move(s));
+}
 
-Decision decide(int op, int M, int N, int K) {
+const Snapshot* snapshot() {
+  const Snapshot* s = g_snap.load(std::memory_order_acquire);
+  if (s) return s;
   std::lock_guard<std::mutex> lk(g_mu);
-  ensure_table_locked();
+  if (!g_snap.load(std::memory_order_relaxed)) lazy_load_locked();
+  return g_snap.load(std::memory_order_acquire);
+}
+
+// The dispatch decision: the override, else the table entry of the rows
+// bucket, else the built-in default.  Every M of one rows bucket compiles to
+// the same kernels, so a decision depends on (op, bucket, N, K) only.
+Decision decide(int op, int M, int N, int K) {
+  const Snapshot* snap = snapshot();
+  const Settings& cfg = settings();
+  const int b = bucket_of(M);                              // 0: above the last bucket
+  const uint64_t key = ((uint64_t)(unsigned)op << 58) ^ ((uint64_t)(unsigned)b << 48) ^
+                       ((uint64_t)(unsigned)N << 24) ^ (uint64_t)(unsigned)K;
+  const bool keyable = N < (1 << 24) && K < (1 << 24);
+  {
+    std::lock_guard<std::mutex> lk(snap->mu);
+    if (keyable) {
+      const auto it = snap->cache.find(key);
+      if (it != snap->cache.end())
+        return Decision{it->second, it->second == cfg.force ? "force" : "cached"};
+    }
+  }
   Decision d{-1, "default"};
-  const int fv = forced_variant();
-  if (fv >= 0 && variant_supports(op, fv, M)) {
-    d = Decision{fv, "force"};
+  if (cfg.force >= 0 && variant_supports(op, cfg.force, M)) {
+    d = Decision{cfg.force, "force"};
   } else {
-    const int b = bucket_of(M);
-    const int tv = b ? g_table.lookup(op, b, N, K) : -1;
+    const int tv = b ? snap->table.lookup(op, b, N, K) : -1;
     if (tv >= 0 && variant_supports(op, tv, M)) d = Decision{tv, "table"};
     else d = Decision{default_variant(op, M, N, K), "default"};
   }
-  if (const char* lg = std::getenv("SKINNY_GEMM_LOG"); lg && *lg && *lg != '0') {
-    const auto key = std::make_tuple(op, bucket_of(M), N, K, d.variant);
-    if (g_logged.insert(key).second)
-      std::fprintf(stderr, "skinny_gemm: %s M=%d(bucket %d) N=%d K=%d -> %s [%s]\n", op_name(op), M, bucket_of(M), N,
-                   K, d.variant >= 0 ? kVariants[d.variant].name : "none", d.source);
+  if (keyable) {
+    std::lock_guard<std::mutex> lk(snap->mu);
+    snap->cache.emplace(key, d.variant);
   }
+  if (cfg.log)
+    std::fprintf(stderr, "skinny_gemm: %s M=%d(bucket %d) N=%d K=%d -> %s [%s]\n", op_name(op), M, b, N, K,
+                 d.variant >= 0 ? kVariants[d.variant].name : "none", d.source);
   return d;
+}
+
+// Where a decision came from, for skinny_gemm_query (not cached: the query
+// states the source).
+const char* decision_source(int op, int M, int N, int K, int v) {
+  const Settings& cfg = settings();
+  if (cfg.force >= 0 && v == cfg.force) return "force";
+  const int b = bucket_of(M);
+  const int tv = b ? snapshot()->table.lookup(op, b, N, K) : -1;
+  return tv == v ? "table" : "default";
 }
 
 // ---------------------------------------------------------- argument checks
@@ -254,17 +327,31 @@ LaunchFn variant_fn(int op, int v, int M) {
   return t ? t[fi].f[fm] : nullptr;
 }
 
-// ------------------------------------------------------ split-K workspace
-// fp32 partials of the tlds variants with S > 1: one buffer per device,
-// allocated (kWsInit bytes, or more when a call needs it) by the first call
-// on the device that is not under graph capture, and kept for the life of
-// the process.  Calls on one stream are ordered, so they share it safely;
-// calls that run concurrently on different streams of one device race on it.
-constexpr size_t kWsCap = 256ull << 20;
-constexpr size_t kWsInit = 64ull << 20;
-constexpr size_t kCntBytes = (size_t)kSplitCounters * sizeof(unsigned);  // counters precede the partials
+// Bytes of split-K partials variant v of op needs for M rows (0: none), and
+// whether its output tiles fit the arrival counters.
+size_t partial_bytes(int op, int v, int M, int N) {
+  if (v < 0 || kVariants[v].family != FAM_TLDS) return 0;
+  return (size_t)tlds_ws_bytes(op, kVariants[v].p1, M, N);
+}
+bool tiles_fit(int op, int v, int M, int N) {
+  (void)op;
+  const int fm = M > kMaxBucket ? kNumTileFM - 1 : tile_fm_index(M);
+  const VariantDesc& d = kVariants[v];
+  return tlds_tiles(d.p0, d.p4 / d.p5, tlds_fm(kTileFM[fm], d.p3), M, N) <= (unsigned long long)kSplitCounters;
+}
+
+// ------------------------------------------------- registered workspaces
+// Caller-owned device buffers for the split-K partials, registered per
+// (device, stream) or per device (any stream of it that has none of its own).
+struct WsReg {
+  int dev;
+  bool any;            // the device-wide registration
+  hipStream_t stream;  // when !any
+  char* p;
+  size_t bytes;
+};
 std::mutex g_ws_mu;
-std::map<int, std::pair<void*, size_t>> g_ws;
+std::vector<WsReg> g_ws;
 
 bool capturing(hipStream_t s) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -275,65 +362,58 @@ bool capturing(hipStream_t s) {
   return cs != hipStreamCaptureStatusNone;
 }
 
-float* workspace(hipStream_t s, size_t bytes, std::string* why) {
-  if (bytes > kWsCap) {
-    *why = "split-K partials of " + std::to_string(bytes) + " bytes exceed the " + std::to_string(kWsCap) +
-           "-byte workspace cap";
-    return nullptr;
-  }
+skg_status clear_counters(void* p, hipStream_t s) {
+  hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, s, static_cast<unsigned*>(p),
+                     (size_t)kSplitCounters);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? SKG_OK : fail(SKG_ELAUNCH, "clearing the split-K counters: %s", hipGetErrorString(e));
+}
+
+skg_status register_ws(bool any, hipStream_t stream, void* ws, size_t bytes) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
-    *why = "no current device";
-    return nullptr;
+    return fail(SKG_EINVAL, "no current HIP device");
+  }
+  if (ws) {
+    if (bytes < kCntBytes) return fail(SKG_EINVAL, "a workspace needs at least %zu bytes (has %zu)", kCntBytes, bytes);
+    if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(SKG_EUNSUPPORTED, "the workspace must be 256-byte aligned");
+    if (skg_status st = check_device_range(Buf{ws, bytes, "workspace"})) return st;
+    if (capturing(stream)) return fail(SKG_EINVAL, "register a workspace outside graph capture");
+    if (skg_status st = clear_counters(ws, stream)) return st;
   }
   std::lock_guard<std::mutex> lk(g_ws_mu);
-  auto& e = g_ws[dev];
-  if (e.first && e.second >= bytes + kCntBytes) return static_cast<float*>(e.first);
-  if (capturing(s)) {
-    *why = "the split-K workspace must be allocated outside graph capture (make one call eagerly first)";
-    return nullptr;
-  }
-  if (e.first) {
-    (void)hipDeviceSynchronize();   // the old buffer may still be in use
-    (void)hipFree(e.first);
-    e = {nullptr, 0};
-  }
-  const size_t want = std::max(bytes + kCntBytes, kWsInit);
-  void* p = nullptr;
-  if (hipMalloc(&p, want) != hipSuccess) {
-    (void)hipGetLastError();
-    *why = "hipMalloc of the split-K workspace failed";
-    return nullptr;
-  }
-  // the arrival counters start at zero; each launch leaves them at zero
-  if (hipMemset(p, 0, kCntBytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-    (void)hipGetLastError();
-    (void)hipFree(p);
-    *why = "clearing the split-K counters failed";
-    return nullptr;
-  }
-  e = {p, want};
-  return static_cast<float*>(p);
+  for (size_t i = 0; i < g_ws.size(); ++i)
+    if (g_ws[i].dev == dev && g_ws[i].any == any && (any || g_ws[i].stream == stream)) {
+      g_ws.erase(g_ws.begin() + (long)i);
+      break;
+    }
+  if (ws) g_ws.push_back(WsReg{dev, any, any ? nullptr : stream, static_cast<char*>(ws), bytes});
+  return SKG_OK;
 }
 
-// The first call on a device (outside capture) allocates the workspace so
-// that later captured calls find it.
-void prime_workspace(hipStream_t s) {
+// The workspace for a call on `stream` of the current device: its own, else
+// the device's; {nullptr, 0} if neither.
+std::pair<char*, size_t> find_ws(hipStream_t stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
-    return;
+    return {nullptr, 0};
   }
-  {
-    std::lock_guard<std::mutex> lk(g_ws_mu);
-    if (g_ws.count(dev)) return;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  const WsReg* anyr = nullptr;
+  for (const WsReg& r : g_ws) {
+    if (r.dev != dev) continue;
+    if (!r.any && r.stream == stream) return {r.p, r.bytes};
+    if (r.any) anyr = &r;
   }
-  std::string why;
-  (void)workspace(s, kWsInit, &why);
+  return anyr ? std::make_pair(anyr->p, anyr->bytes) : std::make_pair((char*)nullptr, (size_t)0);
 }
 
-skg_status launch(int op, int v, const Args& a_in, hipStream_t s) {
+// ------------------------------------------------------------------ launch
+enum class WsFrom { kRegistered };
+
+skg_status launch(int op, int v, const Args& a_in, hipStream_t s, WsFrom from) {
   Args a = a_in;
   if (a.K == 0) {
     const size_t n = (size_t)a.M * a.N;
@@ -343,53 +423,51 @@ skg_status launch(int op, int v, const Args& a_in, hipStream_t s) {
     return e == hipSuccess ? SKG_OK : fail(SKG_ELAUNCH, "zero fill launch: %s", hipGetErrorString(e));
   }
   const LaunchFn fn = v >= 0 ? variant_fn(op, v, a.M) : nullptr;
-  if (fn && kVariants[v].family == FAM_TLDS) {
-    const size_t need = (size_t)tlds_ws_bytes(op, kVariants[v].p1, a.M, a.N);
-    if (need) {
-      const int fm = a.M > kMaxBucket ? kNumTileFM - 1 : tile_fm_index(a.M);
-      if (tlds_tiles(kVariants[v].p0, kVariants[v].p4 / kVariants[v].p5, tlds_fm(kTileFM[fm], kVariants[v].p3), a.M,
-                     a.N) >
-          (unsigned long long)kSplitCounters)
-        return fail(SKG_EUNSUPPORTED, "%s: more output tiles than split-K counters", kVariants[v].name);
-      std::string why;
-      float* base = workspace(s, need, &why);
-      if (!base) return fail(SKG_EUNSUPPORTED, "%s: %s", kVariants[v].name, why.c_str());
-      a.cnt = reinterpret_cast<unsigned*>(base);
-      a.ws = reinterpret_cast<float*>(reinterpret_cast<char*>(base) + kCntBytes);
-    }
+  if (!fn)
+    return fail(SKG_EUNSUPPORTED, "variant %s is not compiled for %s at M=%d", v >= 0 ? kVariants[v].name : "(none)",
+                op_name(op), a.M);
+  if (const size_t need = partial_bytes(op, v, a.M, a.N)) {
+    if (!tiles_fit(op, v, a.M, a.N))
+      return fail(SKG_EUNSUPPORTED, "%s: more output tiles than split-K counters", kVariants[v].name);
+    char* base = nullptr;
+    (void)from;
+    const auto ws = find_ws(s);
+    if (!ws.first || ws.second < need + kCntBytes)
+      return fail(SKG_EUNSUPPORTED,
+                  "%s at M=%d N=%d needs a split-K workspace of %zu bytes on this stream (registered: %zu); "
+                  "see skinny_gemm_set_workspace",
+                  kVariants[v].name, a.M, a.N, need + kCntBytes, ws.second);
+    base = ws.first;
+    a.cnt = reinterpret_cast<unsigned*>(base);
+    a.ws = reinterpret_cast<float*>(base + kCntBytes);
   }
-  if (fn && op == OP_A8W8 && kVariants[v].family == FAM_GEMV) {
+  if (op == OP_A8W8 && kVariants[v].family == FAM_GEMV) {
     const size_t smem = (size_t)(kGemvMT[gemv_mt_index(a.M)] + 1) * a.kb * sizeof(float);
     if (smem > 64 * 1024)
       return fail(SKG_EUNSUPPORTED, "K=%d needs %zu bytes of A8W8 scale staging (limit 65536)", a.K, smem);
   }
-  if (!fn)
-    return fail(SKG_EUNSUPPORTED, "variant %s is not compiled for %s at M=%d", v >= 0 ? kVariants[v].name : "(none)",
-                op_name(op), a.M);
   const hipError_t e = fn(a, s);
   if (e != hipSuccess)
     return fail(SKG_ELAUNCH, "%s %s launch: %s", op_name(op), kVariants[v].name, hipGetErrorString(e));
   return SKG_OK;
 }
 
-skg_status run_op(int op, const void* x, const void* w, const float* s0, const float* s1, void* y, int M, int N,
-                  int K, hipStream_t s, float* xs_out = nullptr) {
+Args make_args(int op, const void* x, const void* w, const float* s0, const float* s1, void* y, int M, int N,
+               int K, float* xs_out) {
   const int base = op_base(op);
   Args a{x, w, s0, s1, y, M, N, K, (K + 127) / 128, nullptr, nullptr, base == OP_A8W8Q ? xs_out : nullptr};
   if (base != OP_FP8T && base != OP_A8W8) a.s0 = nullptr;
   if (base != OP_A8W8 && base != OP_A8W8Q) a.s1 = nullptr;
+  return a;
+}
+
+skg_status run_op(int op, const void* x, const void* w, const float* s0, const float* s1, void* y, int M, int N,
+                  int K, hipStream_t s, float* xs_out, WsFrom from) {
+  const Args a = make_args(op, x, w, s0, s1, y, M, N, K, xs_out);
   if (skg_status st = validate(op, a)) return st;
   if (M == 0 || N == 0) return SKG_OK;
-  prime_workspace(s);
   const Decision d = decide(op, M, N, K);
-  skg_status st = launch(op, d.variant, a, s);
-  if (st == SKG_EUNSUPPORTED && d.variant >= 0 && kVariants[d.variant].family == FAM_TLDS) {
-    // no split-K workspace here (e.g. first call under graph capture): the
-    // untuned default without a K split needs none
-    const int fb = default_variant_no_ws(op, M, N, K);
-    if (fb >= 0 && fb != d.variant) st = launch(op, fb, a, s);
-  }
-  return st;
+  return launch(op, d.variant, a, s, from);
 }
 
 int copy_out(const std::string& s, char* buf, int len) {
@@ -407,53 +485,71 @@ extern "C" {
 
 skg_status skinny_gemm_bf16(const void* x, const void* W, const float* scales, void* y, int M, int N, int K,
                             hipStream_t stream) {
-  return run_op(OP_BF16, x, W, scales, nullptr, y, M, N, K, stream);
+  return run_op(OP_BF16, x, W, scales, nullptr, y, M, N, K, stream, nullptr, WsFrom::kRegistered);
 }
 
 skg_status skinny_gemm_gated(const void* x, const void* W, const float* scales, void* y, int M, int N, int K,
                              hipStream_t stream) {
-  return run_op(OP_GATED, x, W, scales, nullptr, y, M, N, K, stream);
+  return run_op(OP_GATED, x, W, scales, nullptr, y, M, N, K, stream, nullptr, WsFrom::kRegistered);
 }
 
 skg_status skinny_gemm_fp8_tensor(const void* x, const void* W, const float* scales, void* y, int M, int N, int K,
                                   hipStream_t stream) {
-  return run_op(OP_FP8T, x, W, scales, nullptr, y, M, N, K, stream);
+  return run_op(OP_FP8T, x, W, scales, nullptr, y, M, N, K, stream, nullptr, WsFrom::kRegistered);
 }
 
 skg_status skinny_gemm_a8w8_block(const void* x, const void* W, const float* x_scales, const float* w_scales,
                                   void* y, int M, int N, int K, hipStream_t stream) {
-  return run_op(OP_A8W8, x, W, x_scales, w_scales, y, M, N, K, stream);
+  return run_op(OP_A8W8, x, W, x_scales, w_scales, y, M, N, K, stream, nullptr, WsFrom::kRegistered);
 }
 
 skg_status skinny_gemm_a8w8_block_quant(const void* x, const void* W, const float* w_scales, float* x_scales_out,
                                         void* y, int M, int N, int K, hipStream_t stream) {
-  return run_op(OP_A8W8Q, x, W, nullptr, w_scales, y, M, N, K, stream, x_scales_out);
+  return run_op(OP_A8W8Q, x, W, nullptr, w_scales, y, M, N, K, stream, x_scales_out, WsFrom::kRegistered);
 }
 
 skg_status skinny_gemm_bf16_packed(const void* x, const void* W_packed, const float* scales, void* y, int M, int N,
                                    int K, hipStream_t stream) {
-  return run_op(OP_PACKED + OP_BF16, x, W_packed, scales, nullptr, y, M, N, K, stream);
+  return run_op(OP_PACKED + OP_BF16, x, W_packed, scales, nullptr, y, M, N, K, stream, nullptr, WsFrom::kRegistered);
 }
 
 skg_status skinny_gemm_gated_packed(const void* x, const void* W_packed, const float* scales, void* y, int M, int N,
                                     int K, hipStream_t stream) {
-  return run_op(OP_PACKED + OP_GATED, x, W_packed, scales, nullptr, y, M, N, K, stream);
+  return run_op(OP_PACKED + OP_GATED, x, W_packed, scales, nullptr, y, M, N, K, stream, nullptr,
+                WsFrom::kRegistered);
 }
 
 skg_status skinny_gemm_fp8_tensor_packed(const void* x, const void* W_packed, const float* scales, void* y, int M,
                                          int N, int K, hipStream_t stream) {
-  return run_op(OP_PACKED + OP_FP8T, x, W_packed, scales, nullptr, y, M, N, K, stream);
+  return run_op(OP_PACKED + OP_FP8T, x, W_packed, scales, nullptr, y, M, N, K, stream, nullptr, WsFrom::kRegistered);
 }
 
 skg_status skinny_gemm_a8w8_block_packed(const void* x, const void* W_packed, const float* x_scales,
                                          const float* w_scales, void* y, int M, int N, int K, hipStream_t stream) {
-  return run_op(OP_PACKED + OP_A8W8, x, W_packed, x_scales, w_scales, y, M, N, K, stream);
+  return run_op(OP_PACKED + OP_A8W8, x, W_packed, x_scales, w_scales, y, M, N, K, stream, nullptr,
+                WsFrom::kRegistered);
 }
 
 skg_status skinny_gemm_a8w8_block_quant_packed(const void* x, const void* W_packed, const float* w_scales,
                                                float* x_scales_out, void* y, int M, int N, int K,
                                                hipStream_t stream) {
-  return run_op(OP_PACKED + OP_A8W8Q, x, W_packed, nullptr, w_scales, y, M, N, K, stream, x_scales_out);
+  return run_op(OP_PACKED + OP_A8W8Q, x, W_packed, nullptr, w_scales, y, M, N, K, stream, x_scales_out,
+                WsFrom::kRegistered);
+}
+
+size_t skinny_gemm_workspace_bytes(int op, int M, int N, int K) {
+  if (!op_name(op) || M <= 0 || N <= 0 || K <= 0 || K % op_k_multiple(op)) return 0;
+  const Decision d = decide(op, M, N, K);
+  const size_t need = partial_bytes(op, d.variant, M, N);
+  return need ? need + kCntBytes : 0;
+}
+
+skg_status skinny_gemm_set_workspace(hipStream_t stream, void* workspace, size_t bytes) {
+  return register_ws(false, stream, workspace, bytes);
+}
+
+skg_status skinny_gemm_set_device_workspace(void* workspace, size_t bytes, hipStream_t stream) {
+  return register_ws(true, stream, workspace, bytes);
 }
 
 size_t skinny_gemm_packed_weight_bytes(int op, int N, int K) {
@@ -507,11 +603,10 @@ skg_status skinny_gemm_calib_mfma(int grid, int iters, unsigned* sink, hipStream
 
 skg_status skinny_gemm_load_table(const char* path) {
   std::lock_guard<std::mutex> lk(g_mu);
-  g_table_tried = true;
+  auto s = std::make_unique<Snapshot>();
   Identity id;
-  std::string product;
-  if (!self_identity(&id, &product)) {
-    g_table.clear();
+  if (!self_identity(&id)) {
+    publish(std::move(s));
     return fail(SKG_ETABLE, "no HIP device: cannot establish the table identity");
   }
   std::string p;
@@ -519,37 +614,45 @@ skg_status skinny_gemm_load_table(const char* path) {
   else if (const char* e = std::getenv("SKINNY_GEMM_TABLE"); e && *e) p = e;
   else p = self_dir() + "/configs/" + id.arch + "/skinny_gemm.json";
   std::string err;
-  if (g_table.load(p, id, &err) != 0) return fail(SKG_ETABLE, "%s", err.c_str());
+  const int rc = s->table.load(p, id, &err);
+  publish(std::move(s));
+  if (rc != 0) return fail(SKG_ETABLE, "%s", err.c_str());
   return SKG_OK;
 }
 
 skg_status skinny_gemm_load_table_as(const char* path, const char* identity) {
   std::lock_guard<std::mutex> lk(g_mu);
-  g_table_tried = true;
+  auto s = std::make_unique<Snapshot>();
   Identity id;
   if (!identity || !Identity::parse(identity, &id)) {
-    g_table.clear();
+    publish(std::move(s));
     return fail(SKG_EINVAL, "identity must read arch=..;hip=..;cc=..;space=..");
   }
   if (!path || !*path) {
-    g_table.clear();
+    publish(std::move(s));
     return SKG_OK;  // explicit "no table"
   }
   std::string err;
-  if (g_table.load(path, id, &err) != 0) return fail(SKG_ETABLE, "%s", err.c_str());
+  const int rc = s->table.load(path, id, &err);
+  publish(std::move(s));
+  if (rc != 0) return fail(SKG_ETABLE, "%s", err.c_str());
   return SKG_OK;
 }
 
 skg_status skinny_gemm_identity(char* buf, int len) {
   Identity id;
-  if (!self_identity(&id, nullptr)) return fail(SKG_EUNSUPPORTED, "no HIP device");
+  if (!self_identity(&id)) return fail(SKG_EUNSUPPORTED, "no HIP device");
   return copy_out(id.str(), buf, len);
 }
 
 int skinny_gemm_table_status(char* buf, int len) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  if (buf && len > 0) std::snprintf(buf, (size_t)len, "%s", g_table.status().c_str());
-  return g_table.engaged() ? 1 : 0;
+  const Snapshot* s = g_snap.load(std::memory_order_acquire);
+  if (!s) {
+    if (buf && len > 0) std::snprintf(buf, (size_t)len, "%s", "none");
+    return 0;
+  }
+  if (buf && len > 0) std::snprintf(buf, (size_t)len, "%s", s->table.status().c_str());
+  return s->table.engaged() ? 1 : 0;
 }
 
 skg_status skinny_gemm_query(int op, int M, int N, int K, char* buf, int len) {
@@ -557,7 +660,7 @@ skg_status skinny_gemm_query(int op, int M, int N, int K, char* buf, int len) {
   if (M <= 0 || N <= 0 || K < 0) return fail(SKG_EINVAL, "query needs M, N > 0 and K >= 0");
   const Decision d = decide(op, M, N, K);
   if (d.variant < 0) return fail(SKG_EUNSUPPORTED, "no variant for M=%d", M);
-  return copy_out(std::string(kVariants[d.variant].name) + " " + d.source, buf, len);
+  return copy_out(std::string(kVariants[d.variant].name) + " " + decision_source(op, M, N, K, d.variant), buf, len);
 }
 
 int skinny_gemm_num_variants(int op) { return op_name(op) ? kNumVariants : 0; }
@@ -578,16 +681,19 @@ skg_status skinny_gemm_run_variant(int op, int variant, const int* knobs, const 
   if (!op_name(op)) return fail(SKG_EINVAL, "unknown op %d", op);
   if (variant < 0 || variant >= kNumVariants) return fail(SKG_EINVAL, "no variant %d", variant);
   if (knobs) return fail(SKG_EINVAL, "knobs are reserved: pass NULL");
-  Args a{x, W, s0, s1, y, M, N, K, (K + 127) / 128, nullptr, nullptr, nullptr};
-  const int base = op_base(op);
-  if (base == OP_A8W8Q) a.xs_out = const_cast<float*>(s0);   // its s0 is the x-scale output
-  if (base != OP_FP8T && base != OP_A8W8) a.s0 = nullptr;
-  if (base != OP_A8W8 && base != OP_A8W8Q) a.s1 = nullptr;
+  float* xs_out = op_base(op) == OP_A8W8Q ? const_cast<float*>(s0) : nullptr;   // its s0 is the x-scale output
+  const Args a = make_args(op, x, W, s0, s1, y, M, N, K, xs_out);
   if (skg_status st = validate(op, a)) return st;
   if (M == 0 || N == 0) return SKG_OK;
   if (!variant_supports(op, variant, M))
     return fail(SKG_EUNSUPPORTED, "variant %s does not run %s at M=%d", kVariants[variant].name, op_name(op), M);
-  return launch(op, variant, a, stream);
+  return launch(op, variant, a, stream, WsFrom::kRegistered);
+}
+
+size_t skinny_gemm_variant_workspace_bytes(int op, int variant, int M, int N) {
+  if (!op_name(op) || variant < 0 || variant >= kNumVariants || M <= 0 || N <= 0) return 0;
+  const size_t need = partial_bytes(op, variant, M, N);
+  return need ? need + kCntBytes : 0;
 }
 
 }  // extern "C"

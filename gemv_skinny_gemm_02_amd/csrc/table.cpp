@@ -267,11 +267,11 @@ int Table::load(const std::string& path, const Identity& self, std::string* err)
   };
   const std::string t_arch = field("arch"), t_hip = field("hip"), t_cc = field("cc"), t_space = field("space");
   if (t_space.empty())
-    return refuse("made before the kernel selection space was tracked - the kernels have changed since: "
-                  "run the tuner again");
+    return refuse("its identity has no selection-space token, so it predates the current kernel list: "
+                  "re-tune for this build");
   if (t_space != self.space)
-    return refuse("made for kernel selection space " + t_space + ", this build is " + self.space +
-                  " (the kernels changed): run the tuner again");
+    return refuse("its selection-space token " + t_space + " differs from this build's " + self.space +
+                  " (the kernel list changed): re-tune for this build");
   if (t_arch != self.arch) return refuse("made for " + t_arch + ", this device is " + self.arch);
   if (t_hip != self.hip)
     return refuse("tuned on HIP runtime " + t_hip + ", this process loaded " + self.hip +
@@ -471,7 +471,5 @@ int default_pick(int op, int M, int N, int K, bool allow_ws) {
 }  // namespace
 
 int default_variant(int op, int M, int N, int K) { return default_pick(op, M, N, K, true); }
-
-int default_variant_no_ws(int op, int M, int N, int K) { return default_pick(op, M, N, K, false); }
 
 }  // namespace skg

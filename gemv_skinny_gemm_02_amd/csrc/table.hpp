@@ -56,8 +56,6 @@ int variant_from_name(const std::string& s);
 // Built-in default for (op, M, N, K): the untuned entry point a table is
 // measured against.
 int default_variant(int op, int M, int N, int K);
-// The default among variants that need no split-K workspace.
-int default_variant_no_ws(int op, int M, int N, int K);
 
 // The dispatch override: $SKINNY_GEMM_FORCE=<variant name>, or -1.
 int forced_variant();

@@ -15,10 +15,10 @@ checkpoint.
 
 `promote` is a pure function of the store.  For each key the built-in default
 is the incumbent; a different variant is chosen only when its time is at least
-2 % below the default's (mstar PR #1104, "What changed": a size leaves what
-the tree serves only for a 2 % gain; every candidate is re-measured against
-the incumbent's real entry point: Decode optimization round 3, "Rejected
-paths", and Strata PR #1297, item 4, the true-default baseline).  The table
+2 % below the default's (the promote threshold of mstar PR #1104, "What
+changed"; candidates are measured against the incumbent's own entry point as
+in Decode optimization round 3, "Rejected paths", and Strata PR #1297, item 4,
+the true-default baseline).  The table
 keeps every candidate's time beside the choice, so moving a size is a one-word
 edit.
 """
@@ -143,6 +143,9 @@ def tune(store, ops, quick=False, rotation_gib=1.0, replays=5, only_m=None, rows
 
     torch.cuda.set_device(0)
     skg.load()
+    # split-K partials of up to 256 MiB (a candidate that needs more is
+    # recorded as refused), plus the arrival counters
+    skg.skinny_gemm_set_device_workspace((256 << 20) + (256 << 10))
     ident = skg.skinny_gemm_identity()
     # measured triples are skipped on a rerun; a recorded failure is retried
     done = {(r["identity"], r["op"], r["rows"], r["N"], r["K"], r["variant"]) for r in read_store(store)

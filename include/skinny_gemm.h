@@ -31,12 +31,13 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Memory.   Every tensor argument is a DEVICE pointer to caller-owned memory,
- *           contiguous and row-major.  bf16 is passed as its 16-bit pattern,
- *           fp8 as OCP e4m3fn bytes (1 sign, 4 exponent with bias 7, 3 fraction
+ *           contiguous and row-major; the caller allocates and frees it.
+ *           bf16 is passed as its 16-bit pattern, fp8 as OCP e4m3fn bytes (1 sign, 4 exponent with bias 7, 3 fraction
  *           bits; largest finite 448; 0x7F/0xFF are NaN), scales as float32.
  *           x and W must be 16-byte aligned.  y must not overlap any input.
- *           The library never frees, syncs on or reads caller memory from the
- *           host; every call is ordered on `stream` (NULL = the null stream).
+ *           The library never allocates, frees, syncs on or reads device
+ *           memory from the host; every call is ordered on `stream` (NULL =
+ *           the null stream) and can be captured into a HIP graph.
  * Sizes.    M, N, K >= 0.  M == 0 or N == 0 is a no-op that returns OK.
  *           K == 0 writes y = 0 (the empty sum).  K must be a multiple of 8 for
  *           bf16 weights and of 16 for fp8 weights (one 16-byte load per lane).
@@ -61,14 +62,21 @@
  *           on the MFMA tile path in launch rows of at most 128.
  * Threads.  GEMM calls are reentrant.  skinny_gemm_load_table must not run
  *           concurrently with other calls.
- * Workspace. Variants that split K across workgroups keep fp32 partials in a
- *           per-device buffer the library allocates once (64 MiB, more if a
- *           call needs it, at most 256 MiB) on the first call on the device
- *           that is not under graph capture; it lives until the process
- *           ends.  Calls on one stream share it safely.  Calls that run
- *           concurrently on different streams of one device race on it.  A
- *           call that would need to allocate it while the stream is being
- *           captured uses a variant that needs no workspace instead.
+ * Workspace. Some variants split K across workgroups and pass float32
+ *           partials through a split-K workspace: caller-owned device memory
+ *           registered once with skinny_gemm_set_workspace (one stream) or
+ *           skinny_gemm_set_device_workspace (every stream of the device that
+ *           has none of its own).  skinny_gemm_workspace_bytes tells how much a
+ *           call needs; a call whose dispatch choice needs more than its
+ *           stream's workspace holds returns SKG_EUNSUPPORTED and launches
+ *           nothing.  GEMM calls never allocate, free or synchronise, and
+ *           which kernel runs does not depend on the workspace, on graph
+ *           capture or on earlier calls (no host sync in the decode step:
+ *           mstar PR #1102, "Verification"; every kernel served from graph
+ *           replay: mstar PR #1104, "Verification").  Calls that share one
+ *           workspace must be ordered (one stream, or synchronised streams):
+ *           calls that overlap in time on one workspace race on it and give
+ *           wrong results.
  */
 #ifndef SKINNY_GEMM_H
 #define SKINNY_GEMM_H
@@ -188,6 +196,39 @@ skg_status skinny_gemm_a8w8_block_quant_packed(const void* x, const void* W_pack
                                                const float* w_scales, float* x_scales_out, void* y,
                                                int M, int N, int K, hipStream_t stream);
 
+/* ---- Split-K workspace ---------------------------------------------------
+ * Layout: 256 KiB of arrival counters (65536 words, one per output tile of a
+ * launch, each left at zero by the launch that used it), then the float32
+ * partials [S][G][M][N] of the call (S = the variant's K split, G = 2 for the
+ * gated form).  The counters are the only part that must start at zero; the
+ * registration clears them. */
+
+/* Bytes of split-K workspace the call (op, M, N, K) needs under the current
+ * dispatch (table or default), or 0 when its kernel needs none (also 0 for an
+ * unknown op or sizes outside the contract).  Loads the table on first use,
+ * like a GEMM call. */
+size_t skinny_gemm_workspace_bytes(int op, int M, int N, int K);
+
+/* The same for one variant of op at M rows and N outputs. */
+size_t skinny_gemm_variant_workspace_bytes(int op, int variant, int M, int N);
+
+/* Register `workspace` (device memory of `bytes` bytes, 256-byte aligned,
+ * caller-owned) for the GEMM calls ordered on `stream` of the current device;
+ * NULL removes the stream's registration.  The call clears the counters with
+ * a kernel ordered on `stream` (so it must not run under graph capture:
+ * SKG_EINVAL) and allocates nothing.  The caller keeps the memory alive while
+ * it is registered and while a graph captured with it may still replay; a new
+ * registration applies to later calls only.  Errors: SKG_EINVAL (fewer than
+ * 256 KiB, host or short memory, capture), SKG_EUNSUPPORTED (alignment). */
+skg_status skinny_gemm_set_workspace(hipStream_t stream, void* workspace, size_t bytes);
+
+/* Register the current device's workspace, used by calls on any stream of the
+ * device that has no workspace of its own; the counters are cleared on
+ * `stream`, so calls on other streams must be ordered after that (for
+ * instance by synchronising `stream` once).  NULL removes it.  Otherwise as
+ * skinny_gemm_set_workspace. */
+skg_status skinny_gemm_set_device_workspace(void* workspace, size_t bytes, hipStream_t stream);
+
 /* Text of the calling thread's last non-OK status ("" if none). */
 const char* skinny_gemm_last_error(void);
 
@@ -197,9 +238,9 @@ const char* skinny_gemm_last_error(void);
  * dispatch override ($SKINNY_GEMM_FORCE) is set, is REFUSED: one line on
  * stderr, built-in defaults stay in effect, and the call returns SKG_OK.  A
  * missing or malformed file returns SKG_ETABLE (defaults stay in effect).
- * (Tuned solutions apply only on the stack they were tuned on: mstar PR #1104,
- * "What changed"; identity, stale and knob refusals: Strata PR #1297, "The
- * second commit: the seam rework", items 1-2.) */
+ * (A table is valid only for the software stack it was tuned on: mstar PR
+ * #1104, "What changed"; identity, stale and knob refusals: Strata PR #1297,
+ * "The second commit: the seam rework", items 1-2.) */
 skg_status skinny_gemm_load_table(const char* path);
 
 /* Same, with the identity string given instead of read from the device and
@@ -208,7 +249,10 @@ skg_status skinny_gemm_load_table_as(const char* path, const char* identity);
 
 /* Identity this build and device give a table:
  * "arch=<gfx>;hip=<runtime version>;cc=<compiler hash>;space=<selection token>".
- * Writes a NUL-terminated string into buf[len]. */
+ * Writes a NUL-terminated string into buf[len]; SKG_EINVAL if it does not fit,
+ * SKG_EUNSUPPORTED without a HIP device.  (The identity header a table carries
+ * and is checked against: Strata PR #1297, "The second commit: the seam
+ * rework", item 1.) */
 skg_status skinny_gemm_identity(char* buf, int len);
 
 /* 1 if a table is engaged, 0 if defaults are in effect. Also reports, in buf,
@@ -219,7 +263,11 @@ int skinny_gemm_table_status(char* buf, int len);
  * "<variant> <source>" where source is table|default|force. */
 skg_status skinny_gemm_query(int op, int M, int N, int K, char* buf, int len);
 
-/* Number of compiled variants for an op, and the name of variant i. */
+/* Number of compiled variants for an op (0 for an unknown op), and the name of
+ * variant i.  The variant list is one X-macro list from which the launch
+ * tables, the table parser and the selection-space token all derive (one
+ * rows and kernel list for every consumer: Strata PR #1297, "The second
+ * commit: the seam rework", item 3). */
 int skinny_gemm_num_variants(int op);
 skg_status skinny_gemm_variant_name(int op, int variant, char* buf, int len);
 
@@ -227,11 +275,14 @@ skg_status skinny_gemm_variant_name(int op, int variant, char* buf, int len);
  * that rows bucket), else 0. */
 int skinny_gemm_variant_supports(int op, int variant, int M);
 
-/* Run one named variant, bypassing the table (tuner and tests).  s0/s1 are the
- * op's scale arrays (fp8_tensor: s0 = w_scale; a8w8: s0 = x_scales,
- * s1 = w_scales; a8w8_quant: s0 = x_scales_out (written, may be NULL),
- * s1 = w_scales; others NULL); a packed op takes its form's arrays and the
- * packed weight as W.  knobs: reserved, pass NULL. */
+/* Run one named variant, bypassing the table: the tuner measures every
+ * candidate this way and checks it against the true default's output before
+ * it can be promoted (Strata PR #1297, "The second commit: the seam rework",
+ * item 4).  s0/s1 are the op's scale arrays (fp8_tensor: s0 = w_scale; a8w8:
+ * s0 = x_scales, s1 = w_scales; a8w8_quant: s0 = x_scales_out (written, may be
+ * NULL), s1 = w_scales; others NULL); a packed op takes its form's arrays and
+ * the packed weight as W.  knobs: reserved, pass NULL.  Arguments, errors and
+ * workspace as for the op's entry point. */
 skg_status skinny_gemm_run_variant(int op, int variant, const int* knobs,
                                    const void* x, const void* W, const float* s0,
                                    const float* s1, void* y, int M, int N, int K,

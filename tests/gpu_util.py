@@ -11,6 +11,19 @@ import gemv_skinny_gemm_02_amd as skg
 import oracle
 
 
+# Split-K workspace the GPU tests register for the device: enough for every
+# table entry they run (the largest, A8W8 32768 x 1024 at M = 512 with S = 4,
+# takes 256 MiB of partials).
+TEST_WORKSPACE_BYTES = 512 << 20
+_WS = []
+
+
+def ensure_workspace() -> None:
+    """Register the tests' device-wide split-K workspace once per process."""
+    if not _WS:
+        _WS.append(skg.skinny_gemm_set_device_workspace(TEST_WORKSPACE_BYTES))
+
+
 def say(*a) -> None:
     print(*a, flush=True)
     sys.stdout.flush()

@@ -120,8 +120,8 @@ assert not skg.skinny_gemm_table_status()[0]
 
 
 @pytest.mark.parametrize("case,needle", [
-    ("stale", "made before the kernel selection space was tracked"),
-    ("space", "made for kernel selection space"),
+    ("stale", "has no selection-space token"),
+    ("space", "selection-space token"),
     ("arch", "made for gfx942"),
     ("hip", "tuned on HIP runtime"),
     ("cc", "built by compiler"),

@@ -71,3 +71,27 @@ def test_bench_gpus_flag_refuses_more_than_one():
     r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_printed_line_is_short():
+    """The line the benchmark prints holds the headline fields, the roofline
+    and the CPU baseline, and stays under 2 KB, so that a reader of the last
+    few KB of the output gets all of it."""
+    import json
+    shapes = ["4096x4096", "6144x4096", "4096x12288", "2048x2048", "1024x1024"]
+    per_m = {str(M): {s: [123.45, 7654] for s in shapes} for M in (1, 8, 128)}
+    roofline = {"bound": "hbm", "achieved": 4486.3, "peak": 8000.0, "unit": "GB/s", "frac": 0.5608,
+                "traffic": 35190123, "kernel": "void skg::tlds_kernel<5, 1, 1, 1, 4, 4, 4, 1>(skg::Args)",
+                "launches_per_step": 26, "avg_launch_us": 7.812, "alg_bytes_per_launch": 34830494}
+    cpu = {"value": 1.3908, "unit": "GB/s", "cores": 16, "kind": "oracle",
+           "sample": "median of 3 runs of 5 s, each the step's 65 calls in order (170-180 calls), "
+                     "oracle.linear_bf16 in float64 on 16 BLAS threads of 128 host cores"}
+    line = bench.make_line(3859.2, 0.6654, 20, 5, 65, roofline, per_m, cpu)
+    text = json.dumps(line, separators=(",", ":"))
+    assert len(text) < 2048, len(text)
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+              "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert k in line
+    for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert k in line["roofline"]
+    assert line["metric"] == "achieved HBM GB/s and \u00b5s/call at M=1/8/128; fraction of MI355X roofline"

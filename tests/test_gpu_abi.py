@@ -9,7 +9,7 @@ import torch
 import gemv_skinny_gemm_02_amd as skg
 import oracle
 import synth
-from gpu_util import assert_parity, dev_bf16, dev_f32, dev_fp8, host_bits, reference, run, say, to_device
+from gpu_util import ensure_workspace, assert_parity, dev_bf16, dev_f32, dev_fp8, host_bits, reference, run, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -19,6 +19,7 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     skg.load()
+    ensure_workspace()
 
 
 def _raw(fn, *args):

@@ -9,8 +9,9 @@ import torch
 import gemv_skinny_gemm_02_amd as skg
 import oracle
 import synth
-from gpu_util import (assert_parity, dev_bf16, dev_fp8, host_bits, reference, run, run_packed, say, to_device,
-                      to_device_packed)
+from gpu_util import (ensure_workspace, assert_parity, dev_bf16, dev_f32, dev_fp8, host_bits, reference, run,
+                      run_packed, say, to_device, to_device_packed)
+from test_gpu_parity import VARIANT_M, head_cols
 
 pytestmark = pytest.mark.gpu
 
@@ -28,6 +29,7 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     skg.load()
+    ensure_workspace()
 
 
 def layout(w: np.ndarray, kind: str, N: int, K: int) -> np.ndarray:
@@ -70,7 +72,7 @@ def test_every_packed_variant_small(kind):
     N, K = _small_shape(kind)
     op = kind + "_packed"
     names = skg.variants(op)
-    for M in (1, 2, 3, 5, 8, 12, 16, 17, 40, 128):
+    for M in VARIANT_M:
         p = MAKE[kind](M, N, K, seed=1)
         dev = to_device_packed(p)
         ref = reference(p)
@@ -109,26 +111,29 @@ def test_packed_dispatch_ragged(kind):
 
 def test_packed_full_shapes():
     """The bf16 sweep shapes and both A8W8 shapes at full size through the packed
-    dispatch, sampled columns."""
+    dispatch, at every workload M, every output (the oracle at the largest M,
+    sliced: row m depends on row m of x only)."""
     for (N, K) in synth.SWEEP_NK:
-        base = synth.make_bf16(128, N, K, seed=0)
+        base = synth.make_bf16(max(synth.SWEEP_M), N, K, seed=0)
+        ref = oracle.linear_bf16(base.x, base.w)
         wp = skg.skinny_gemm_pack_weight("bf16", dev_bf16(base.w))
-        for M in (1, 4, 8, 16, 64, 128):
+        for M in synth.SWEEP_M:
             x = dev_bf16(base.x[:M])
             say(f"bf16_packed M={M} N={N} K={K} -> {skg.skinny_gemm_query('bf16_packed', M, N, K)}")
             y = skg.skinny_gemm_bf16_packed(x, wp)
             torch.cuda.synchronize()
-            cols = synth.rows_of(N, 64, seed=M)
-            ref = oracle.linear_bf16(base.x[:M], base.w, cols=cols)
-            assert_parity(host_bits(y)[:, cols], ref, f"bf16_packed M={M} N={N} K={K}")
+            assert_parity(host_bits(y), ref[:M], f"bf16_packed M={M} N={N} K={K}")
+        del wp
     for (N, K) in synth.A8W8_NK:
-        for M in (1, 16, 64):
-            p = synth.make_a8w8_block(M, N, K, seed=0)
-            say(f"a8w8_block_packed M={M} N={N} K={K}")
-            y = run_packed(p)
+        base = synth.make_a8w8_block(max(synth.A8W8_M), N, K, seed=0)
+        ref = oracle.linear_a8w8_block(base.x, base.s0, base.w, base.s1)
+        wp = skg.skinny_gemm_pack_weight("a8w8_block", dev_fp8(base.w))
+        ws = dev_f32(base.s1)
+        for M in synth.A8W8_M:
+            say(f"a8w8_block_packed M={M} N={N} K={K} -> {skg.skinny_gemm_query('a8w8_block_packed', M, N, K)}")
+            y = skg.skinny_gemm_a8w8_block_packed(dev_fp8(base.x[:M]), wp, dev_f32(base.s0[:M]), ws)
             torch.cuda.synchronize()
-            cols = synth.rows_of(N, 64, seed=M)
-            assert_parity(host_bits(y)[:, cols], reference(p, cols=cols), f"a8w8_block_packed M={M} N={N} K={K}")
+            assert_parity(host_bits(y), ref[:M], f"a8w8_block_packed M={M} N={N} K={K}")
 
 
 def test_pack_refusals():
@@ -148,39 +153,39 @@ def test_pack_refusals():
 def test_packed_other_forms_full_shapes():
     """The gate/up 12288 x 4096, the 248320 x 4096 fp8 head and A8W8 with x
     quantised in the call, at full size on packed weights through table
-    dispatch, as the benchmark times them; sampled columns (the quantising
-    form's x scales bit for bit)."""
+    dispatch, as the benchmark times them: every output (the head: one column
+    in every 16-row block), the quantising form's x scales bit for bit."""
     N, K = synth.GATED_NK
     base = synth.make_gated(max(synth.GATED_M), N, K, seed=0)
+    ref = oracle.linear_gated(base.x, base.w)
     wp = skg.skinny_gemm_pack_weight("gated", dev_bf16(base.w))
     for M in synth.GATED_M:
         say(f"gated_packed M={M} N={N} K={K} -> {skg.skinny_gemm_query('gated_packed', M, N, K)}")
         y = skg.skinny_gemm_gated_packed(dev_bf16(base.x[:M]), wp)
         torch.cuda.synchronize()
-        cols = synth.rows_of(N, 64, seed=M)
-        assert_parity(host_bits(y)[:, cols], oracle.linear_gated(base.x[:M], base.w, cols=cols),
-                      f"gated_packed M={M}")
+        assert_parity(host_bits(y), ref[:M], f"gated_packed M={M}")
     del wp
     N, K = synth.HEAD_NK
     head = synth.make_fp8_tensor(max(synth.HEAD_M), N, K, seed=0)
+    cols = head_cols(N, 0)
+    ref = oracle.linear_fp8_tensor(head.x, head.w, head.s0, cols=cols)
     wp = skg.skinny_gemm_pack_weight("fp8_tensor", dev_fp8(head.w))
-    s = torch.from_numpy(np.ascontiguousarray(head.s0, dtype=np.float32)).cuda()
+    s = dev_f32(head.s0)
     for M in synth.HEAD_M:
         say(f"fp8_tensor_packed M={M} N={N} K={K} -> {skg.skinny_gemm_query('fp8_tensor_packed', M, N, K)}")
         y = skg.skinny_gemm_fp8_tensor_packed(dev_bf16(head.x[:M]), wp, s)
         torch.cuda.synchronize()
-        cols = synth.rows_of(N, 256, seed=M)
-        assert_parity(host_bits(y)[:, cols], oracle.linear_fp8_tensor(head.x[:M], head.w, head.s0, cols=cols),
-                      f"fp8_tensor_packed M={M}")
+        assert_parity(host_bits(y)[:, cols], ref[:M], f"fp8_tensor_packed M={M}")
     del wp
     for (N, K) in synth.A8W8_NK:
+        base = synth.make_a8w8_quant(max(synth.A8W8_M), N, K, seed=0)
+        ref, _, want = oracle.linear_a8w8_quant(base.x, base.w, base.s1)
+        wp = skg.skinny_gemm_pack_weight("a8w8_quant", dev_fp8(base.w))
+        ws = dev_f32(base.s1)
         for M in synth.A8W8_M:
-            p = synth.make_a8w8_quant(M, N, K, seed=0)
             say(f"a8w8_quant_packed M={M} N={N} K={K} -> {skg.skinny_gemm_query('a8w8_quant_packed', M, N, K)}")
-            x, wpk, xs, ws = to_device_packed(p)
-            y = skg.skinny_gemm_a8w8_block_quant_packed(x, wpk, ws, x_scales=xs)
+            xs = torch.full((M, -(-K // 128)), -1.0, device="cuda")
+            y = skg.skinny_gemm_a8w8_block_quant_packed(dev_bf16(base.x[:M]), wp, ws, x_scales=xs)
             torch.cuda.synchronize()
-            cols = synth.rows_of(N, 64, seed=M)
-            assert_parity(host_bits(y)[:, cols], reference(p, cols=cols), f"a8w8_quant_packed M={M} N={N} K={K}")
-            _, want = oracle.quantize_a8w8_x(p.x)
-            assert np.array_equal(xs.cpu().numpy().view(np.uint32), want.view(np.uint32)), f"x scales M={M}"
+            assert_parity(host_bits(y), ref[:M], f"a8w8_quant_packed M={M} N={N} K={K}")
+            assert np.array_equal(xs.cpu().numpy().view(np.uint32), want[:M].view(np.uint32)), f"x scales M={M}"

@@ -2,8 +2,13 @@
 
 Small shapes span several workgroups and ragged tails in N, K and M and are
 compared element by element.  The full workload shapes run in the launch
-configuration the benchmark times (table dispatch) and are compared on a seeded
-sample of output columns, which the oracle computes one by one.
+configuration the benchmark times (table dispatch) and are compared on every
+output, except the 248320-row vocabulary head, which is compared on one
+seeded column in every 16-row block of its weight.
+
+Row m of the linear depends on row m of x only, so the oracle's result for the
+largest M of a shape, sliced to its first M rows, is the reference of every
+smaller M drawn from the same x stream.
 """
 import numpy as np
 import pytest
@@ -12,13 +17,18 @@ import torch
 import gemv_skinny_gemm_02_amd as skg
 import oracle
 import synth
-from gpu_util import assert_parity, dev_bf16, dev_f32, dev_fp8, host_bits, reference, run, say, to_device
+from gpu_util import ensure_workspace, assert_parity, dev_bf16, dev_f32, dev_fp8, host_bits, reference, run, say, to_device
 
 pytestmark = pytest.mark.gpu
 
 MAKE = {"bf16": synth.make_bf16, "gated": synth.make_gated,
         "fp8_tensor": synth.make_fp8_tensor, "a8w8_block": synth.make_a8w8_block,
         "a8w8_quant": synth.make_a8w8_quant}
+
+
+# Rows of the per-variant tests: every tile height (1, 2, 4, 6 and 8 fragments
+# of 16 rows) with a ragged last fragment, and each GEMV rows bucket.
+VARIANT_M = (1, 2, 3, 5, 8, 12, 16, 17, 40, 72, 96, 128)
 
 
 def _small_shape(kind):
@@ -31,6 +41,7 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     skg.load()
+    ensure_workspace()
     say("device:", torch.cuda.get_device_name(0), "identity:", skg.skinny_gemm_identity())
     say("table:", skg.skinny_gemm_table_status())
 
@@ -47,7 +58,7 @@ def test_config1_full():
 def test_every_variant_small(kind):
     N, K = _small_shape(kind)
     names = skg.variants(kind)
-    for M in (1, 2, 3, 5, 8, 12, 16, 17, 40, 128):
+    for M in VARIANT_M:
         p = MAKE[kind](M, N, K, seed=1)
         dev = to_device(p)
         ref = reference(p)
@@ -75,55 +86,61 @@ def test_dispatch_ragged(kind):
             assert_parity(host_bits(y), reference(p), f"{kind} dispatch M={M} N={N} K={K}")
 
 
-def _sampled(p, y, count=64):
-    cols = synth.rows_of(p.N, count, seed=p.M)
-    assert_parity(host_bits(y)[:, cols], reference(p, cols=cols), f"{p.kind} M={p.M} N={p.N} K={p.K} (sampled)")
+def _full(p, y, ref, what):
+    assert_parity(host_bits(y), ref[:p.M], f"{p.kind} M={p.M} N={p.N} K={p.K} {what}")
 
 
 def test_sweep_full_shapes():
-    """The bf16 decode-linear sweep at its full shapes, sampled columns."""
+    """The bf16 decode-linear sweep at its full shapes, every output."""
     for (N, K) in synth.SWEEP_NK:
+        base = synth.make_bf16(max(synth.SWEEP_M), N, K, seed=0)
+        ref = oracle.linear_bf16(base.x, base.w)
+        w = dev_bf16(base.w)
         for M in synth.SWEEP_M:
-            p = synth.make_bf16(M, N, K, seed=0)
             say(f"bf16 sweep M={M} N={N} K={K} -> {skg.skinny_gemm_query('bf16', M, N, K)}")
-            y = run(p)
+            y = skg.skinny_gemm_bf16(dev_bf16(base.x[:M]), w)
             torch.cuda.synchronize()
-            _sampled(p, y)
+            assert_parity(host_bits(y), ref[:M], f"bf16 sweep M={M} N={N} K={K}")
 
 
 def test_gated_full_shapes():
     N, K = synth.GATED_NK
+    base = synth.make_gated(max(synth.GATED_M), N, K, seed=0)
+    ref = oracle.linear_gated(base.x, base.w)
+    w = dev_bf16(base.w)
     for M in synth.GATED_M:
-        p = synth.make_gated(M, N, K, seed=0)
         say(f"gated M={M} N={N} K={K} -> {skg.skinny_gemm_query('gated', M, N, K)}")
-        y = run(p)
+        y = skg.skinny_gemm_gated(dev_bf16(base.x[:M]), w)
         torch.cuda.synchronize()
-        _sampled(p, y)
+        assert_parity(host_bits(y), ref[:M], f"gated M={M}")
 
 
 def test_a8w8_full_shapes():
     for (N, K) in synth.A8W8_NK:
+        base = synth.make_a8w8_block(max(synth.A8W8_M), N, K, seed=0)
+        ref = oracle.linear_a8w8_block(base.x, base.s0, base.w, base.s1)
+        w, ws = dev_fp8(base.w), dev_f32(base.s1)
         for M in synth.A8W8_M:
-            p = synth.make_a8w8_block(M, N, K, seed=0)
             say(f"a8w8 M={M} N={N} K={K} -> {skg.skinny_gemm_query('a8w8_block', M, N, K)}")
-            y = run(p)
+            y = skg.skinny_gemm_a8w8_block(dev_fp8(base.x[:M]), w, dev_f32(base.s0[:M]), ws)
             torch.cuda.synchronize()
-            _sampled(p, y)
+            assert_parity(host_bits(y), ref[:M], f"a8w8 M={M} N={N} K={K}")
 
 
 def test_a8w8_quant_full_shapes():
-    """A8W8 with x quantised in the call, at the A8W8 shapes; the x scales it
-    hands out equal the oracle's bit for bit."""
+    """A8W8 with x quantised in the call, at the A8W8 shapes, every output; the
+    x scales it hands out equal the oracle's bit for bit."""
     for (N, K) in synth.A8W8_NK:
+        base = synth.make_a8w8_quant(max(synth.A8W8_M), N, K, seed=0)
+        ref, _, want = oracle.linear_a8w8_quant(base.x, base.w, base.s1)
+        w, ws = dev_fp8(base.w), dev_f32(base.s1)
         for M in synth.A8W8_M:
-            p = synth.make_a8w8_quant(M, N, K, seed=0)
             say(f"a8w8_quant M={M} N={N} K={K} -> {skg.skinny_gemm_query('a8w8_quant', M, N, K)}")
-            x, w, xs, ws = to_device(p)
-            y = skg.skinny_gemm_a8w8_block_quant(x, w, ws, x_scales=xs)
+            xs = torch.full((M, -(-K // 128)), -1.0, device="cuda")
+            y = skg.skinny_gemm_a8w8_block_quant(dev_bf16(base.x[:M]), w, ws, x_scales=xs)
             torch.cuda.synchronize()
-            _sampled(p, y)
-            _, want = oracle.quantize_a8w8_x(p.x)
-            assert np.array_equal(xs.cpu().numpy().view(np.uint32), want.view(np.uint32)), f"x scales M={M}"
+            assert_parity(host_bits(y), ref[:M], f"a8w8_quant M={M} N={N} K={K}")
+            assert np.array_equal(xs.cpu().numpy().view(np.uint32), want[:M].view(np.uint32)), f"x scales M={M}"
 
 
 def test_a8w8_quant_codes_exact():
@@ -180,21 +197,27 @@ def test_a8w8_quant_codes_exact():
         assert np.array_equal(back, codes), f"codes ({variant}): {np.argwhere(back != codes)[:5]}"
 
 
+def head_cols(N: int, seed: int) -> np.ndarray:
+    """One seeded column in every 16-row block of an N-row weight."""
+    r = np.random.default_rng([seed, 16])
+    base = np.arange(0, N, 16)
+    return np.minimum(base + r.integers(0, 16, size=base.size), N - 1)
+
+
 def test_fp8_head_full_shape():
-    """The 248320 x 4096 fp8 vocabulary head, one weight copy for all M."""
+    """The 248320 x 4096 fp8 vocabulary head, one weight copy for all M, one
+    column in every 16-row block of the weight."""
     N, K = synth.HEAD_NK
     base = synth.make_fp8_tensor(max(synth.HEAD_M), N, K, seed=0)
     w = dev_fp8(base.w)
     s = dev_f32(base.s0)
+    cols = head_cols(N, 0)
+    ref = oracle.linear_fp8_tensor(base.x, base.w, base.s0, cols=cols)
     for M in synth.HEAD_M:
-        # x for M rows: the first M rows of the x stream (seed 0, tensor 1)
-        xM = synth.bf16_bits(synth.normal_f32(0, 1, (M, K)))
         say(f"fp8 head M={M} -> {skg.skinny_gemm_query('fp8_tensor', M, N, K)}")
-        y = skg.skinny_gemm_fp8_tensor(dev_bf16(xM), w, s)
+        y = skg.skinny_gemm_fp8_tensor(dev_bf16(base.x[:M]), w, s)
         torch.cuda.synchronize()
-        cols = synth.rows_of(N, 256, seed=M)
-        ref = oracle.linear_fp8_tensor(xM, base.w, base.s0, cols=cols)
-        assert_parity(host_bits(y)[:, cols], ref, f"fp8 head M={M}")
+        assert_parity(host_bits(y)[:, cols], ref[:M], f"fp8 head M={M}")
 
 
 def test_fp8_one_hot_exact():
