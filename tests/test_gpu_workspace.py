@@ -98,8 +98,9 @@ def test_registration_refusals():
     assert lib.skinny_gemm_set_workspace(s, buf.data_ptr(), 1000) == 1                 # under 256 KiB
     assert lib.skinny_gemm_set_workspace(s, buf.data_ptr() + 16, 512 << 10) == 2       # alignment
     assert lib.skinny_gemm_set_workspace(s, buf.data_ptr(), 4 << 20) == 1             # past the allocation
-    host = np.zeros(1 << 20, dtype=np.uint8)
-    assert lib.skinny_gemm_set_workspace(s, host.ctypes.data, 512 << 10) == 1        # host memory
+    host = np.zeros(2 << 20, dtype=np.uint8)
+    hp = (host.ctypes.data + 255) // 256 * 256                                         # aligned host address
+    assert lib.skinny_gemm_set_workspace(s, hp, 512 << 10) == 1                       # host memory
     g = torch.cuda.CUDAGraph()
     st = []
     with torch.cuda.graph(g):
