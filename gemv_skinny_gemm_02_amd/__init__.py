@@ -42,7 +42,7 @@ __all__ = [
     "skinny_gemm_variant_name", "skinny_gemm_variant_supports", "variants", "default_table_path",
     "skinny_gemm_calib_read", "skinny_gemm_calib_mfma", "CALIB_MFMA_FLOPS_PER_ITER_WG",
     "skinny_gemm_workspace_bytes", "skinny_gemm_variant_workspace_bytes", "skinny_gemm_set_workspace",
-    "skinny_gemm_set_device_workspace",
+    "skinny_gemm_set_device_workspace", "skinny_gemm_run_static", "skinny_gemm_static_scratch_bytes",
 ]
 
 # Rows buckets of dispatch (the library's list): M rounds up to the next one;
@@ -140,6 +140,10 @@ def load() -> ctypes.CDLL:
         lib.skinny_gemm_set_workspace.restype = i
         lib.skinny_gemm_set_device_workspace.argtypes = [vp, ctypes.c_size_t, vp]
         lib.skinny_gemm_set_device_workspace.restype = i
+        lib.skinny_gemm_run_static.argtypes = [i, vp, vp, fp, fp, vp, i, i, i, vp]
+        lib.skinny_gemm_run_static.restype = i
+        lib.skinny_gemm_static_scratch_bytes.argtypes = []
+        lib.skinny_gemm_static_scratch_bytes.restype = ctypes.c_size_t
         _LIB = lib
         return lib
 
@@ -482,6 +486,34 @@ def skinny_gemm_set_device_workspace(ws, stream=None) -> torch.Tensor | None:
         _HELD.append(t)
         torch.cuda.synchronize()
     return t
+
+
+def skinny_gemm_static_scratch_bytes() -> int:
+    """Bytes of split-K partials the library's static device scratch holds."""
+    return int(load().skinny_gemm_static_scratch_bytes())
+
+
+def skinny_gemm_run_static(op, x, W, s0=None, s1=None, y=None, stream=None) -> torch.Tensor:
+    """The op's entry point with its split-K partials in the library's static
+    device scratch: allocates nothing on the device and needs no workspace
+    (calls that overlap in time on one device race on the scratch).  Scale
+    arrays as skinny_gemm_run_variant; for a packed op W is its
+    PackedWeight."""
+    opi = _opi(op)
+    b = _base(opi)
+    xd = _FP8 if b == 3 else _BF16
+    wd = _FP8 if b in (2, 3, 4) else _BF16
+    if opi >= PACKED:
+        M, N, K, wp = _pk(x, W, _BASE_NAMES[b])
+    else:
+        M, N, K = _mk(x, W, 2 if b == 1 else 1)
+        wp = _dev(W, "W", wd, 2)
+    y = _out(y, M, N, x)
+    p0 = _dev(s0, "s0", (torch.float32,), s0.dim()) if s0 is not None else None
+    p1 = _dev(s1, "s1", (torch.float32,), s1.dim()) if s1 is not None else None
+    _check(load().skinny_gemm_run_static(opi, _dev(x, "x", xd, 2), wp, p0, p1, _dev(y, "y", _BF16, 2), M, N, K,
+                                         _stream(stream)))
+    return y
 
 
 # ------------------------------------------------------ measurement helpers

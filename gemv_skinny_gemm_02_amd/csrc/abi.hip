@@ -4,8 +4,9 @@
 //
 // A GEMM call allocates nothing, frees nothing and never synchronises: the
 // only device memory it touches beyond its arguments is the split-K workspace
-// that the caller registered (skinny_gemm_set_workspace).  Which kernel runs is
-// a pure function of (op, rows bucket, N, K, table).
+// that the caller registered (skinny_gemm_set_workspace) or, for
+// skinny_gemm_run_static, the library's static device scratch below.  Which
+// kernel runs is a pure function of (op, rows bucket, N, K, table).
 #include <dlfcn.h>
 
 #include <atomic>
@@ -27,10 +28,17 @@
 #include "skinny_gemm.h"
 #include "table.hpp"
 
-// Split-K workspace layout: kSplitCounters arrival
+// Split-K workspace layout (registered or static): kSplitCounters arrival
 // counters (one per output tile, zero between calls), then the fp32 partials
 // [S][G][M][N] of the call.
 constexpr size_t kCntBytes = (size_t)skg::kSplitCounters * sizeof(unsigned);
+// The static scratch of skinny_gemm_run_static: the counters and at most
+// kStaticPartialBytes of partials.  Each device that runs the library holds
+// its own copy until the process ends.  Host code never uses this name as an
+// address (in host code it is a stand-in, not device memory): it takes each
+// device's address from hipGetSymbolAddress once, with that device current.
+constexpr size_t kStaticPartialBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kCntBytes + kStaticPartialBytes];
 
 namespace skg {
 
@@ -410,8 +418,42 @@ std::pair<char*, size_t> find_ws(hipStream_t stream) {
   return anyr ? std::make_pair(anyr->p, anyr->bytes) : std::make_pair((char*)nullptr, (size_t)0);
 }
 
+// --------------------------------------------- the static scratch, per device
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices] = {};
+bool g_static_cleared[kMaxDevices] = {};   // counters cleared by a launch outside capture
+
+// This device's copy of `scratch`: its address is taken once per device with
+// that device current; the counters are cleared (stream-ordered, before the
+// call's kernel) until one clear has run outside graph capture, after which
+// every launch leaves them at zero.
+skg_status static_scratch(hipStream_t s, char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(SKG_EINVAL, "no current HIP device");
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(SKG_EUNSUPPORTED, "device %d beyond the static scratch table", dev);
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return fail(SKG_ELAUNCH, "hipGetSymbolAddress of the static scratch failed on device %d", dev);
+    }
+    g_static_ptr[dev] = ptr;
+  }
+  if (!g_static_cleared[dev]) {
+    if (skg_status st = clear_counters(g_static_ptr[dev], s)) return st;
+    if (!capturing(s)) g_static_cleared[dev] = true;
+  }
+  *out = static_cast<char*>(g_static_ptr[dev]);
+  return SKG_OK;
+}
+
 // ------------------------------------------------------------------ launch
-enum class WsFrom { kRegistered };
+enum class WsFrom { kRegistered, kStatic };
 
 skg_status launch(int op, int v, const Args& a_in, hipStream_t s, WsFrom from) {
   Args a = a_in;
@@ -430,14 +472,21 @@ skg_status launch(int op, int v, const Args& a_in, hipStream_t s, WsFrom from) {
     if (!tiles_fit(op, v, a.M, a.N))
       return fail(SKG_EUNSUPPORTED, "%s: more output tiles than split-K counters", kVariants[v].name);
     char* base = nullptr;
-    (void)from;
-    const auto ws = find_ws(s);
-    if (!ws.first || ws.second < need + kCntBytes)
-      return fail(SKG_EUNSUPPORTED,
-                  "%s at M=%d N=%d needs a split-K workspace of %zu bytes on this stream (registered: %zu); "
-                  "see skinny_gemm_set_workspace",
-                  kVariants[v].name, a.M, a.N, need + kCntBytes, ws.second);
-    base = ws.first;
+    if (from == WsFrom::kStatic) {
+      if (need > kStaticPartialBytes)
+        return fail(SKG_EUNSUPPORTED,
+                    "%s at M=%d N=%d needs %zu bytes of split-K partials; the static scratch holds %zu",
+                    kVariants[v].name, a.M, a.N, need, kStaticPartialBytes);
+      if (skg_status st = static_scratch(s, &base)) return st;
+    } else {
+      const auto ws = find_ws(s);
+      if (!ws.first || ws.second < need + kCntBytes)
+        return fail(SKG_EUNSUPPORTED,
+                    "%s at M=%d N=%d needs a split-K workspace of %zu bytes on this stream (registered: %zu); "
+                    "see skinny_gemm_set_workspace",
+                    kVariants[v].name, a.M, a.N, need + kCntBytes, ws.second);
+      base = ws.first;
+    }
     a.cnt = reinterpret_cast<unsigned*>(base);
     a.ws = reinterpret_cast<float*>(base + kCntBytes);
   }
@@ -551,6 +600,15 @@ skg_status skinny_gemm_set_workspace(hipStream_t stream, void* workspace, size_t
 skg_status skinny_gemm_set_device_workspace(void* workspace, size_t bytes, hipStream_t stream) {
   return register_ws(true, stream, workspace, bytes);
 }
+
+skg_status skinny_gemm_run_static(int op, const void* x, const void* W, const float* s0, const float* s1, void* y,
+                                  int M, int N, int K, hipStream_t stream) {
+  if (!op_name(op)) return fail(SKG_EINVAL, "unknown op %d", op);
+  float* xs_out = op_base(op) == OP_A8W8Q ? const_cast<float*>(s0) : nullptr;   // its s0 is the x-scale output
+  return run_op(op, x, W, s0, s1, y, M, N, K, stream, xs_out, WsFrom::kStatic);
+}
+
+size_t skinny_gemm_static_scratch_bytes(void) { return kStaticPartialBytes; }
 
 size_t skinny_gemm_packed_weight_bytes(int op, int N, int K) {
   if (!op_name(op) || N <= 0 || K <= 0 || K % op_k_multiple(op)) return 0;

@@ -229,6 +229,28 @@ skg_status skinny_gemm_set_workspace(hipStream_t stream, void* workspace, size_t
  * skinny_gemm_set_workspace. */
 skg_status skinny_gemm_set_device_workspace(void* workspace, size_t bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory or manage a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the entry point of form `op` (SKG_OP_*: any of the ten forms)
+ * with its split-K partials in the library's static device scratch instead
+ * of a registered workspace.  Arguments as skinny_gemm_run_variant (s0/s1 =
+ * the op's scale arrays, W = the packed weight for a packed op), result and
+ * dispatch as the op's own entry point; it allocates nothing and needs no
+ * registration.  The scratch is a static device array of the library, one
+ * copy per device, held until the process ends: 256 KiB of counters and
+ * skinny_gemm_static_scratch_bytes() (16 MiB) of partials.  A call whose
+ * dispatch choice needs more partials returns SKG_EUNSUPPORTED and launches
+ * nothing.  Every call on a device shares that device's scratch: calls that
+ * overlap in time (on different streams) race on it and give wrong results;
+ * calls ordered on one stream are safe.  The first call on a device clears
+ * the counters with a kernel ordered before its own. */
+skg_status skinny_gemm_run_static(int op, const void* x, const void* W, const float* s0,
+                                  const float* s1, void* y, int M, int N, int K,
+                                  hipStream_t stream);
+
+/* Bytes of split-K partials the static scratch holds (16 MiB). */
+size_t skinny_gemm_static_scratch_bytes(void);
+
 /* Text of the calling thread's last non-OK status ("" if none). */
 const char* skinny_gemm_last_error(void);
 
