@@ -172,8 +172,15 @@ def _dev(t: torch.Tensor, name: str, dtypes, ndim: int) -> int:
     return t.data_ptr() if t.numel() else 0
 
 
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream) -> int:
+    """The HIP stream handle of `stream`, default torch's current stream (read
+    without building a Stream object: this runs on every call)."""
     if stream is None:
+        if _RAW_STREAM is not None:
+            return _RAW_STREAM(torch.cuda.current_device())
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream

@@ -2,6 +2,7 @@
 
     python -m gemv_skinny_gemm_02_amd.tuner tune  --store STORE.jsonl [--ops bf16,gated,...] [--rows decode|mid|all] [--quick]
     python -m gemv_skinny_gemm_02_amd.tuner promote --store STORE.jsonl --out TABLE.json [--merge OLD_TABLE.json]
+    python -m gemv_skinny_gemm_02_amd.tuner check [--table TABLE.json]
 
 `tune` runs on the GPU.  For every key (op, rows bucket, N, K) of the workload
 set it runs every compiled variant that can serve the bucket, checks its
@@ -20,7 +21,7 @@ changed"; candidates are measured against the incumbent's own entry point as
 in Decode optimization round 3, "Rejected paths", and Strata PR #1297, item 4,
 the true-default baseline).  The table
 keeps every candidate's time beside the choice, so moving a size is a one-word
-edit.
+edit, and `check` re-derives every choice from the times the table carries.
 """
 from __future__ import annotations
 
@@ -235,6 +236,36 @@ def tune(store, ops, quick=False, rotation_gib=1.0, replays=5, only_m=None, rows
     return 0
 
 
+def choose(default, times):
+    """The promotion rule: `times` maps each measured variant to its µs.  The
+    fastest variant (ties: the first name) replaces the built-in default only
+    when it is at least KEEP_GAIN faster; a default that was not measured
+    gives way to the fastest."""
+    best = min(sorted(times), key=lambda v: times[v])
+    if default in times and best != default and times[best] > (1.0 - KEEP_GAIN) * times[default]:
+        return default
+    return best
+
+
+def check(table_path):
+    """Re-derive every entry's choice from the candidate times the table
+    carries (the store's per-variant medians) with the promotion rule; returns
+    the entries whose stored choice differs (an empty list: the table is what
+    promotion of its own measurements gives)."""
+    with open(table_path) as f:
+        t = json.load(f)
+    bad = []
+    for e in t["entries"]:
+        times = {v: c["us"] for v, c in e.get("candidates", {}).items()}
+        if not times:
+            bad.append((e["op"], e["rows"], e["N"], e["K"], "no candidates"))
+            continue
+        want = choose(e["default"], times)
+        if want != e["choice"] or abs(times[e["choice"]] - e["us"]) > 1e-9:
+            bad.append((e["op"], e["rows"], e["N"], e["K"], e["choice"], want))
+    return bad
+
+
 def promote(store, out, identity=None, merge=None):
     """Write the table from the store (pure function of the store).  merge: an
     existing table of the same identity whose entries for keys the store does
@@ -261,13 +292,7 @@ def promote(store, out, identity=None, merge=None):
         slot = by_key[k]
         default = next(iter(slot.values()))["default"]
         cands = sorted(slot.values(), key=lambda r: (r["us"], r["variant"]))
-        best = cands[0]
-        choice = default
-        if default in slot:
-            if best["variant"] != default and best["us"] <= (1.0 - KEEP_GAIN) * slot[default]["us"]:
-                choice = best["variant"]
-        else:
-            choice = best["variant"]
+        choice = choose(default, {r["variant"]: r["us"] for r in cands})
         entries.append({"op": k[0], "rows": k[1], "N": k[2], "K": k[3], "choice": choice, "default": default,
                         "measured_M": slot[choice]["M"], "us": round(slot[choice]["us"], 3),
                         "candidates": {r["variant"]: {"us": round(r["us"], 3)} for r in cands}})
@@ -309,7 +334,16 @@ def main(argv=None):
     p.add_argument("--out", required=True)
     p.add_argument("--identity", default=None)
     p.add_argument("--merge", default=None, help="existing table whose other entries are kept")
+    c = sub.add_parser("check")
+    c.add_argument("--table", default=None, help="table to check (default: the installed gfx950 table)")
     a = ap.parse_args(argv)
+    if a.mode == "check":
+        path = a.table or os.path.join(ROOT, "gemv_skinny_gemm_02_amd", "configs", "gfx950", "skinny_gemm.json")
+        bad = check(path)
+        for b in bad:
+            log("differs:", b)
+        log(f"{path}: {'every choice follows from its candidate times' if not bad else f'{len(bad)} entries differ'}")
+        return 1 if bad else 0
     if a.mode == "tune":
         os.environ.setdefault("SKINNY_GEMM_TABLE", "/nonexistent/skinny_gemm.json")  # measure the true defaults
         only = [int(v) for v in a.only_m.split(",") if v]
