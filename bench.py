@@ -64,12 +64,13 @@ def kernel_symbol(variant: str, M: int, op: int = 0) -> str:
     """The kernel template instance a variant runs for M rows, as rocprofv3
     prints it.  Variant names are the family followed by one-letter fields:
     gemv_r<R>_k<KS>_p<P>, tile_f<FN>_k<KS>_p<P>, and
-    tlds[_d][_w<NW>][_k<KW>]_f<FN>_s<S>_p<P>[_m<MC>] (d: direct x; NW waves,
+    tlds[_d|_x][_w<NW>][_k<KW>]_f<FN>_s<S>_p<P>[_m<MC>] (d: direct x; x: x copied
+    into LDS by DMA; NW waves,
     default 4, of which KW split K inside the workgroup, default 1; at most MC
     16-row fragments per workgroup, default 8)."""
     parts = variant.split("_")
-    xd = 1 if "d" in parts[1:] else 0
-    kv = {p[0]: int(p[1:]) for p in parts[1:] if p != "d"}
+    xd = 1 if "d" in parts[1:] else (2 if "x" in parts[1:] else 0)
+    kv = {p[0]: int(p[1:]) for p in parts[1:] if p not in ("d", "x")}
     if parts[0] == "gemv":
         mt = next(b for b in (1, 2, 3, 4, 6, 8, 12, 16) if M <= b)
         return f"void skg::gemv_kernel<{op}, {mt}, {kv['r']}, {kv['k']}, {kv['p']}>(skg::Args)"
@@ -532,19 +533,12 @@ def form_alg_bytes(form, M, N, K):
     return N * K + M * K + 4 * M * kb + 4 * nb * kb + 2 * M * N
 
 
-def measure_forms(args, torch, skg, synth, stream):
-    """The other forms at their workload shapes: gate/up 12288 x 4096, the
-    248320 x 4096 fp8 head, and A8W8 (and A8W8 with x quantised in the call) at
-    (32768, 1024) and (8192, 4096), A8W8 also at the mid-M rows 144 .. 512.  µs per call of the row-major and packed
-    weights through table dispatch, graph replay over >= 1 GiB of rotated
-    weight copies, against the read ceiling of the weight.  Inputs are drawn on
-    the device from torch's seeded generator with the workload distributions
-    (x ~ N(0,1), W ~ N(0,0.02), fp8 scales amax/448); the values do not change
-    the time of these kernels, and the oracle checks them in the tests."""
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(0)
-    sink = torch.empty(256, dtype=torch.int32, device="cuda")
-
+def form_operands(torch, gen, form, N, K, Mmax):
+    """Device operands (x [Mmax, K], the row-major weight, s0, s1) of one form
+    at one shape, drawn on the device from torch's seeded generator `gen` with
+    the workload distributions (x ~ N(0,1), W ~ N(0,0.02), fp8 scales
+    amax/448): the values do not change the time of these kernels, and the
+    oracle checks them in the tests."""
     def normal(shape, std):
         return torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32) * std
 
@@ -560,6 +554,58 @@ def measure_forms(args, torch, skg, synth, stream):
         q = (blk / sc[:, None, :, None]).clamp(-448, 448).view(pr, pc)[:R_, :C_]
         return q.to(torch.float8_e4m3fn).contiguous(), sc.float().contiguous()
 
+    s0 = s1 = None
+    if form == "bf16":
+        w0 = normal((N, K), 0.02).to(torch.bfloat16)
+    elif form == "gated":
+        w0 = normal((2 * N, K), 0.02).to(torch.bfloat16)
+    elif form == "fp8_tensor":
+        # drawn twice in the same row blocks from the same seed (the fp32
+        # weight would be 4 GB): once for amax, once to quantise
+        w0 = torch.empty((N, K), dtype=torch.float8_e4m3fn, device="cuda")
+        amax = torch.zeros((), device="cuda")
+        gen.manual_seed(1)
+        for r0 in range(0, N, 16384):
+            amax = torch.maximum(amax, normal((min(16384, N - r0), K), 0.02).abs().max())
+        sc = (amax / 448.0).reshape(1).float()
+        gen.manual_seed(1)
+        for r0 in range(0, N, 16384):
+            w0[r0:r0 + 16384] = (normal((min(16384, N - r0), K), 0.02) / sc).clamp(-448, 448).to(torch.float8_e4m3fn)
+        s0 = sc
+    else:
+        w0, s1 = e4m3(normal((N, K), 0.02), 128, 128)
+    xf = normal((Mmax, K), 1.0)
+    if form == "a8w8_block":
+        x, s0 = e4m3(xf, 1, 128)
+    else:
+        x = xf.to(torch.bfloat16)
+    return x, w0, s0, s1
+
+
+def form_call(skg, form, packed, xm, w, s0m, s1, y):
+    """One call of a form's entry point (row-major or packed weight)."""
+    sfx = "_packed" if packed else ""
+    if form == "bf16":
+        return getattr(skg, "skinny_gemm_bf16" + sfx)(xm, w, y=y)
+    if form == "gated":
+        return getattr(skg, "skinny_gemm_gated" + sfx)(xm, w, y=y)
+    if form == "fp8_tensor":
+        return getattr(skg, "skinny_gemm_fp8_tensor" + sfx)(xm, w, s0m, y=y)
+    if form == "a8w8_block":
+        return getattr(skg, "skinny_gemm_a8w8_block" + sfx)(xm, w, s0m, s1, y=y)
+    return getattr(skg, "skinny_gemm_a8w8_block_quant" + sfx)(xm, w, s1, y=y)
+
+
+def measure_forms(args, torch, skg, synth, stream):
+    """The other forms at their workload shapes: gate/up 12288 x 4096, the
+    248320 x 4096 fp8 head, and A8W8 (and A8W8 with x quantised in the call) at
+    (32768, 1024) and (8192, 4096), A8W8 also at the mid-M rows 144 .. 512.  µs per call of the row-major and packed
+    weights through table dispatch, graph replay over >= 1 GiB of rotated
+    weight copies, against the read ceiling of the weight (operands from
+    form_operands)."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    sink = torch.empty(256, dtype=torch.int32, device="cuda")
     cases = [("gated", synth.GATED_NK, synth.GATED_M), ("fp8_tensor", synth.HEAD_NK, synth.HEAD_M)]
     cases += [("a8w8_block", nk, tuple(synth.A8W8_M) + tuple(synth.MID_M)) for nk in synth.A8W8_NK]
     cases += [("a8w8_quant", nk, synth.A8W8_M) for nk in synth.A8W8_NK]
@@ -568,29 +614,7 @@ def measure_forms(args, torch, skg, synth, stream):
         Mmax = max(Ms)
         ensure_ws(skg, max(skg.skinny_gemm_workspace_bytes(op, M, N, K) for M in Ms
                            for op in (form, form + "_packed")))
-        s0 = s1 = None
-        if form == "gated":
-            w0 = normal((2 * N, K), 0.02).to(torch.bfloat16)
-        elif form == "fp8_tensor":
-            # drawn twice in the same row blocks from the same seed (the fp32
-            # weight would be 4 GB): once for amax, once to quantise
-            w0 = torch.empty((N, K), dtype=torch.float8_e4m3fn, device="cuda")
-            amax = torch.zeros((), device="cuda")
-            gen.manual_seed(1)
-            for r0 in range(0, N, 16384):
-                amax = torch.maximum(amax, normal((min(16384, N - r0), K), 0.02).abs().max())
-            sc = (amax / 448.0).reshape(1).float()
-            gen.manual_seed(1)
-            for r0 in range(0, N, 16384):
-                w0[r0:r0 + 16384] = (normal((min(16384, N - r0), K), 0.02) / sc).clamp(-448, 448).to(torch.float8_e4m3fn)
-            s0 = sc
-        else:
-            w0, s1 = e4m3(normal((N, K), 0.02), 128, 128)
-        xf = normal((Mmax, K), 1.0)
-        if form == "a8w8_block":
-            x, s0 = e4m3(xf, 1, 128)
-        else:
-            x = xf.to(torch.bfloat16)
+        x, w0, s0, s1 = form_operands(torch, gen, form, N, K, Mmax)
         wbytes = w0.numel() * w0.element_size()
         R = max(2, math.ceil(args.rotation_gib * 2**30 / wbytes))
         ws = [w0] + [w0.clone() for _ in range(R - 1)]
@@ -603,18 +627,8 @@ def measure_forms(args, torch, skg, synth, stream):
             xm = x[:M]
             s0m = s0[:M] if form == "a8w8_block" else s0
             y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-            if form == "gated":
-                f_rm = lambda i: skg.skinny_gemm_gated(xm, ws[i % R], y=y)
-                f_pk = lambda i: skg.skinny_gemm_gated_packed(xm, wps[i % R], y=y)
-            elif form == "fp8_tensor":
-                f_rm = lambda i: skg.skinny_gemm_fp8_tensor(xm, ws[i % R], s0m, y=y)
-                f_pk = lambda i: skg.skinny_gemm_fp8_tensor_packed(xm, wps[i % R], s0m, y=y)
-            elif form == "a8w8_block":
-                f_rm = lambda i: skg.skinny_gemm_a8w8_block(xm, ws[i % R], s0m, s1, y=y)
-                f_pk = lambda i: skg.skinny_gemm_a8w8_block_packed(xm, wps[i % R], s0m, s1, y=y)
-            else:
-                f_rm = lambda i: skg.skinny_gemm_a8w8_block_quant(xm, ws[i % R], s1, y=y)
-                f_pk = lambda i: skg.skinny_gemm_a8w8_block_quant_packed(xm, wps[i % R], s1, y=y)
+            f_rm = lambda i: form_call(skg, form, False, xm, ws[i % R], s0m, s1, y)
+            f_pk = lambda i: form_call(skg, form, True, xm, wps[i % R], s0m, s1, y)
             rm = _graph_us(torch, stream, n, f_rm, args.per_call_replays)
             pk = _graph_us(torch, stream, n, f_pk, args.per_call_replays)
             best = min(rm, pk)
@@ -624,9 +638,70 @@ def measure_forms(args, torch, skg, synth, stream):
         key = f"{form} {N}x{K}"
         out[key] = {"weight_bytes": wbytes, "read_ceiling_us": round(ceil_us, 3), "rows": rows}
         log(f"{key}: ceiling {ceil_us:.2f} us,", {m: (v["row_major_us"], v["packed_us"]) for m, v in rows.items()})
-        del ws, wps, w0, x, xf
+        del ws, wps, w0, x
         torch.cuda.empty_cache()
     return {"dispatch": "table", "GB/s": "algorithmic bytes / the faster layout's µs", "shapes": out}
+
+
+PROFILE_FORMS = ("bf16", "gated", "fp8_tensor", "a8w8_block", "a8w8_quant", "mid_m", "small_n")
+
+
+def profile_form(args, torch, skg, synth) -> int:
+    """A run for the profiler: the workload calls of one form on packed weights
+    through table dispatch, launched eagerly one after another (no graphs), so
+    that every dispatch a profiler records is one call of the list written to
+    --calls-out in launch order (with its algorithmic bytes; the first launch of
+    each call is marked as a warm-up).  Each shape cycles through >= 1 GiB of
+    packed weight copies.  Ends with the 256 MiB device copy the counter
+    summaries calibrate on."""
+    import json as _json
+    form = args.profile_form
+    if form == "mid_m":
+        groups = [("bf16", nk, synth.MID_M) for nk in synth.SWEEP_NK]
+        groups += [("a8w8_block", nk, synth.MID_M) for nk in synth.A8W8_NK]
+    elif form == "small_n":
+        groups = [("bf16", nk, synth.SMALLN_M) for nk in synth.SMALLN_NK]
+    elif form == "bf16":
+        groups = [("bf16", nk, synth.SWEEP_M) for nk in synth.SWEEP_NK]
+    elif form == "gated":
+        groups = [("gated", synth.GATED_NK, synth.GATED_M)]
+    elif form == "fp8_tensor":
+        groups = [("fp8_tensor", synth.HEAD_NK, synth.HEAD_M)]
+    else:
+        groups = [(form, nk, synth.A8W8_M) for nk in synth.A8W8_NK]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    launches = []
+    for f, (N, K), Ms in groups:
+        ensure_ws(skg, max(skg.skinny_gemm_workspace_bytes(f + "_packed", M, N, K) for M in Ms))
+        x, w0, s0, s1 = form_operands(torch, gen, f, N, K, max(Ms))
+        wbytes = w0.numel() * w0.element_size()
+        R = max(2, math.ceil(args.rotation_gib * 2**30 / wbytes))
+        wps = [skg.skinny_gemm_pack_weight(f, w0) for _ in range(R)]
+        del w0
+        ys = {M: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for M in Ms}
+        torch.cuda.synchronize()
+        i = 0
+        for p in range(args.steps + 1):
+            for M in Ms:
+                form_call(skg, f, True, x[:M], wps[i % R], s0[:M] if f == "a8w8_block" else s0, s1, ys[M])
+                i += 1
+                nb = alg_bytes(M, N, K) if f == "bf16" else form_alg_bytes(f, M, N, K)
+                launches.append({"op": f + "_packed", "M": M, "N": N, "K": K, "alg_bytes": nb, "warm": p == 0,
+                                 "variant": skg.skinny_gemm_query(f + "_packed", M, N, K)[0]})
+        torch.cuda.synchronize()
+        del wps, x, ys
+        torch.cuda.empty_cache()
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    if args.calls_out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.calls_out)), exist_ok=True)
+        with open(args.calls_out, "w") as fh:
+            _json.dump({"form": form, "launches": launches}, fh)
+    print(_json.dumps({"profile_form": form, "launches": len(launches), "passes": args.steps + 1}), flush=True)
+    return 0
 
 
 def main() -> int:
@@ -648,6 +723,9 @@ def main() -> int:
     ap.add_argument("--no-row-major", action="store_true",
                     help="skip the row-major step (profiling runs of the packed layout)")
     ap.add_argument("--detail", default=None, help="write the full report (JSON) to this file")
+    ap.add_argument("--profile-form", choices=PROFILE_FORMS, default=None,
+                    help="profiler run: one form's workload calls, eager, in a recorded order (see --calls-out)")
+    ap.add_argument("--calls-out", default=None, help="with --profile-form: where to write the launch list")
     ap.add_argument("--verbose", action="store_true", help="progress on stderr")
     args = ap.parse_args()
     global VERBOSE
@@ -668,6 +746,8 @@ def main() -> int:
         return 1
     torch.cuda.set_device(0)
     skg.load()
+    if args.profile_form:
+        return profile_form(args, torch, skg, synth)
     props = torch.cuda.get_device_properties(0)
     dev_name = f"{props.gcnArchName.split(':')[0]} ({props.multi_processor_count} CUs)"
     log("device", dev_name, "| identity", skg.skinny_gemm_identity())

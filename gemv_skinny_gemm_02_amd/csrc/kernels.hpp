@@ -663,7 +663,7 @@ struct LdsRound {
   static constexpr int XPIECES = KW * 16 * FM * tlds_xg_bytes(OP) / 16;    // 16-byte pieces of the round's x chunks
   static constexpr int XPT = tlds_xpt(OP, FM, NW, KW, XD);              // pieces per thread (direct x: FM * XV)
   u32x4 w[op_groups(OP)][FN][WPF];
-  u32x4 x[XPT];
+  u32x4 x[XPT > 0 ? XPT : 1];
   float sx[BO == OP_A8W8 ? FM : 1];
   float sw[BO == OP_A8W8 || BO == OP_A8W8Q ? FN : 1];
 };
@@ -730,6 +730,41 @@ __device__ __forceinline__ uint2 quant8_e4m3fn(const u32x4 xv, float amax, float
   return make_uint2((unsigned)lo, (unsigned)hi);
 }
 
+// One wave instruction that copies 16 bytes per lane from global memory
+// straight into LDS: lane l's bytes land at d + 16*l (d wave-uniform).  It has
+// no register result; the copy is complete once the wave's vector-memory
+// counter has passed it (the callers wait for that explicitly).  Written as
+// a bare instruction so that the compiler's own counter bookkeeping for the
+// weight loads is not made to wait for the copies as well.
+__device__ __forceinline__ void copy16_to_lds(const void* g, unsigned char* d) {
+  const unsigned lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)d;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+}
+
+// s_waitcnt on the vector-memory counter alone: wait until at most V of this
+// wave's vector memory instructions are outstanding (V above the counter's
+// 6-bit range waits for 63, which is stricter).
+template <int V>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int C = V < 0 ? 0 : (V > 63 ? 63 : V);
+  __builtin_amdgcn_s_waitcnt((C & 15) | ((C >> 4) << 14) | 0x0F70);
+}
+// Wait for the x copies of the round whose loads were followed by n more
+// rounds of loads (n < N, wave-uniform): each round issues DPW copies and then
+// WLD weight loads, and a wave's vector loads complete in issue order.
+template <int WLD, int DPW, int N>
+__device__ __forceinline__ void wait_round_copies(int n) {
+  if constexpr (N > 1) {
+    if (n >= N - 1) {
+      wait_vmcnt<WLD + (N - 1) * (DPW + WLD)>();
+      return;
+    }
+    wait_round_copies<WLD, DPW, N - 1>(n);
+  } else {
+    wait_vmcnt<WLD>();
+  }
+}
+
 // W rows move as 128-byte row segments (8 rows per wave instruction, whole
 // cache lines) and pass through a per-wave LDS stage into the MFMA fragment
 // layout: the fragment layout itself would read 16 rows x 64 bytes per
@@ -757,9 +792,13 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   constexpr bool QX = BO == OP_A8W8Q;             // x quantised here: bf16 in, fp8 codes + scales in LDS
   constexpr int XS = tlds_xl_stride(OP);          // LDS x row stride
   constexpr int PPR = tlds_xg_bytes(OP) / 16;     // 16-byte x pieces per chunk row (as loaded)
-  constexpr int SUBB = tlds_sub_bytes(OP, FM);    // bytes of one x chunk in LDS
+  constexpr bool XDMA = XD == 2;                  // x copied by DMA into swizzled stages
+  constexpr int NSTG = XDMA ? P + 1 : 2;          // LDS x buffers (rounds) in use at once
+  constexpr int SUBB = XDMA ? tlds_dma_chunk_bytes(OP, FM) : tlds_sub_bytes(OP, FM);   // one x chunk in LDS
   constexpr int BUFB = KW * SUBB;                 // bytes of one LDS x buffer (a round's KW chunks)
-  constexpr int XTB = XD ? 0 : 2 * BUFB;           // bytes of the x tile
+  constexpr int XTB = XD == 1 ? 0 : NSTG * BUFB + (XDMA ? 1024 : 0);   // the x tile (+ the DMA spare block)
+  constexpr int DPW = XDMA ? tlds_dma_per_wave(OP, FM, NW, KW) : 0;     // DMA copies per wave per round
+  constexpr int WLD = 2 * G * FN;                 // weight loads per wave per round
   constexpr int XBUF = XTB > tlds_red_bytes(OP, FM, FN, NW, KW) ? XTB : tlds_red_bytes(OP, FM, FN, NW, KW);
   constexpr int XV = tlds_xv(OP);                 // direct x: 16-byte pieces per fragment per chunk
   constexpr int WSTB = tlds_wstage_bytes(OP, FN);  // bytes of one wave's W stage
@@ -814,9 +853,10 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   // clamped to M-1), byte column 16*(p%PPR)
   // (x quantised here: the 8 codes of a piece land at byte 8*(p%PPR) of the
   // LDS row, and the 16 lanes of a row, lanes 16q..16q+15, share its scale)
-  const char* xrowp[XPT];
-  int xcolb[XPT], xdst[XPT], xsub[XPT], xrr[XPT];
-  bool xmine[XPT];
+  constexpr int XPA = XPT > 0 ? XPT : 1;          // (no pieces when x is copied by DMA)
+  const char* xrowp[XPA];
+  int xcolb[XPA], xdst[XPA], xsub[XPA], xrr[XPA];
+  bool xmine[XPA];
 #pragma unroll
   for (int i = 0; i < (XD ? 0 : XPT); ++i) {
     const int p = min((int)threadIdx.x + NT * i, XPIECES - 1);
@@ -855,11 +895,37 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   // which every wave must finish before the chunk's barrier, waits only for
   // L2-resident x and never for the wave's own HBM weight stream.
   auto load = [&](Round& b, int c) {
+    const int stage = c % NSTG;     // x copied by DMA: the round's LDS buffer (from the unclamped round)
     c = min(c, max(rounds - 1, 0));
     const int chunk = min(chunk_of(c, kw), NC - 1);
     // x: 16-byte pieces of the round's chunk rows; a piece of a chunk past the
     // split or past K re-reads in-range data (finite, against zeroed weights)
-    if constexpr (XD) {
+    if constexpr (XDMA) {
+      // copy the round's KW chunks straight into LDS, 1 KiB (8 rows of 128
+      // bytes) per wave instruction: lane l fills row 8*block + l/8, 16-byte
+      // column l%8, with the x piece of logical column (l%8) ^ ((row/2)%8), so
+      // that the sixteen rows a fragment read touches fall in distinct bank
+      // groups.  A wave without a block of its own this round copies into the
+      // spare block, so every wave issues DPW copies per round.
+      constexpr int BPC = SUBB / 1024;            // blocks per chunk
+      unsigned char* sbase = xl + stage * BUFB;
+#pragma unroll
+      for (int i = 0; i < DPW; ++i) {
+        const int blk = wave + NW * i;             // wave-uniform
+        const bool real = blk < KW * BPC;
+        const int q = real ? blk / BPC : 0, rb = real ? blk - (blk / BPC) * BPC : 0;
+        const int r = rb * 8 + (lane >> 3);
+        const int lc = (lane & 7) ^ ((r >> 1) & 7);
+        const int ck = min(chunk_of(c, q), NC - 1);
+        const char* g = static_cast<const char*>(a.x) + (size_t)min(m_base + r, M - 1) * K * XB +
+                        min(ck * KCH * XB + lc * 16, K * XB - 16);
+        unsigned char* d = real ? sbase + q * SUBB + rb * 1024 : xl + NSTG * BUFB;
+        copy16_to_lds(g, d);
+      }
+      // the weight loads of the round follow the copies, so that the copy
+      // wait below can count them
+      __builtin_amdgcn_sched_barrier(0);
+    } else if constexpr (XD == 1) {
       // direct x: piece v of fragment j holds the bytes this lane's MFMA
       // operand takes (the weight's K permutation), from row xm[j]
 #pragma unroll
@@ -909,7 +975,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
 
   auto compute = [&](const Round& b0, int c, auto tail) {
     Round b = b0;
-    unsigned char* buf = xl + (c & 1) * BUFB;
+    unsigned char* buf = xl + (c % NSTG) * BUFB;
     if constexpr (QX) {
       // quantise each 16-byte piece (8 bf16): the row's scale is the maximum
       // magnitude over its 16 lanes over 448 (bf16 magnitudes compare as
@@ -939,12 +1005,29 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
           }
         }
       }
-    } else if constexpr (!XD) {
+    } else if constexpr (XD == 0) {
 #pragma unroll
       for (int i = 0; i < XPT; ++i)
         if (XPIECES % NT == 0 || xmine[i]) *reinterpret_cast<u32x4*>(buf + xdst[i]) = b.x[i];
     }
-    if constexpr (!XD) __syncthreads();
+    if constexpr (XDMA) {
+      // this wave's copies of round c have landed once at most the loads of
+      // the rounds issued after it are outstanding; the barrier then makes
+      // every wave's copies visible (and frees the buffer of round c - 1)
+      if constexpr (decltype(tail)::value) wait_round_copies<WLD, DPW, P>(min(P - 1, max(rounds - 1 - c, 0)));
+      else wait_round_copies<WLD, DPW, P>(P - 1);
+      // a bare barrier: __syncthreads' release fence would wait for every
+      // outstanding vector load (the copies write LDS), draining the weight
+      // ring; the copy wait above is the ordering the x data needs, and the
+      // compiler fences keep the fragment reads below the barrier
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    } else if constexpr (XD == 0) {
+      __syncthreads();
+    }
     if constexpr (!PK) {
       // the wave's own W stage needs no barrier (a wave's LDS accesses run in
       // order): stage the 128-byte segments (row 8h + lane/8, column lane%8) ...
@@ -989,8 +1072,10 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
-          B[u][j] = XD ? b.x[j * XV + u]
-                       : *reinterpret_cast<const u32x4*>(buf + kw * SUBB + (j * 16 + lr) * XS + u * 64 + lq * 16);
+          B[u][j] = XD == 1 ? b.x[j * XV + u]
+                    : XDMA ? *reinterpret_cast<const u32x4*>(buf + kw * SUBB + (j * 16 + lr) * 128 +
+                                                             (((u * 4 + lq) ^ (((j * 16 + lr) >> 1) & 7)) * 16))
+                           : *reinterpret_cast<const u32x4*>(buf + kw * SUBB + (j * 16 + lr) * XS + u * 64 + lq * 16);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -1010,8 +1095,8 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
-          B[u][j] = XD ? b.x[j * XV + u]
-                       : *reinterpret_cast<const u32x4*>(buf + kw * SUBB + (j * 16 + lr) * XS + lq * 64 + u * 16);
+          B[u][j] = XD == 1 ? b.x[j * XV + u]
+                            : *reinterpret_cast<const u32x4*>(buf + kw * SUBB + (j * 16 + lr) * XS + lq * 64 + u * 16);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -1039,8 +1124,8 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
         u32x4 B16[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          B16[h] = XD ? b.x[j * XV + h]
-                      : *reinterpret_cast<const u32x4*>(buf + kw * SUBB + (j * 16 + lr) * XS + h * 64 + lq * 16);
+          B16[h] = XD == 1 ? b.x[j * XV + h]
+                           : *reinterpret_cast<const u32x4*>(buf + kw * SUBB + (j * 16 + lr) * XS + h * 64 + lq * 16);
         float sxj;
         if constexpr (QX) sxj = *reinterpret_cast<const float*>(buf + kw * SUBB + 16 * FM * XS + (j * 16 + lr) * 4);
         else sxj = b.sx[j];
@@ -1065,6 +1150,8 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
 
   Round ring[P];
   ring_pipeline<P>(ring, rounds, load, compute);
+  // no x copy may still be writing LDS when it is reused or released
+  if constexpr (XDMA) wait_vmcnt<0>();
 
   // ---- K groups: waves kw > 0 hand their sums to wave kw = 0 of the same N
   // group through LDS (the x buffers are free once every wave is past its
@@ -1259,7 +1346,7 @@ hipError_t launch_tlds(const Args& a, hipStream_t s) {
   constexpr int TW = 16 * FN * (NW / KW);
   const unsigned gx = (unsigned)((a.N + TW - 1) / TW);
   const unsigned gy = (unsigned)((a.M + 16 * FM - 1) / (16 * FM));
-  const size_t smem = (size_t)tlds_smem(OP, FM, FN, NW, KW, XD);
+  const size_t smem = (size_t)tlds_smem(OP, FM, FN, NW, KW, XD, P);
   hipLaunchKernelGGL((tlds_kernel<OP, FM, FN, S, P, NW, KW, XD>), dim3(gx, gy, S), dim3(64 * NW), smem, s, a);
   return hipGetLastError();
 }

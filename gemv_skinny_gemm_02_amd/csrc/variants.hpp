@@ -112,15 +112,25 @@ constexpr int tlds_wstage_bytes(int op, int FN) { return op_groups(op) * FN * 16
 constexpr int tlds_red_bytes(int op, int FM, int FN, int NW, int KW) {   // K-group partials after the loop
   return (KW - 1) * (NW / KW) * 64 * op_groups(op) * FN * FM * 4 * 4;
 }
-// LDS bytes of a workgroup: the double-buffered x chunks (KW per round; none
-// with direct x), reused after the loop for the K-group partials, then one W
-// stage per wave (none with a packed weight, which arrives in fragment layout).
-constexpr int tlds_smem(int op, int FM, int FN, int NW, int KW, int XD) {
-  const int xb = XD ? 0 : 2 * KW * tlds_sub_bytes(op, FM), rb = tlds_red_bytes(op, FM, FN, NW, KW);
+// x copied by DMA (XD = 2): each round's KW chunks land unpadded, 16-byte
+// columns swizzled per row, in one of P + 1 LDS stages; one more 1 KiB block
+// takes the copies of waves that have no block of their own in a round.
+constexpr int tlds_dma_chunk_bytes(int op, int FM) { return 16 * FM * tlds_xg_bytes(op); }
+constexpr int tlds_dma_blocks(int op, int FM, int KW) { return KW * tlds_dma_chunk_bytes(op, FM) / 1024; }
+constexpr int tlds_dma_per_wave(int op, int FM, int NW, int KW) { return (tlds_dma_blocks(op, FM, KW) + NW - 1) / NW; }
+// LDS bytes of a workgroup: the x chunks (double-buffered and padded, or P + 1
+// DMA stages; none with direct x), reused after the loop for the K-group
+// partials, then one W stage per wave (none with a packed weight, which
+// arrives in fragment layout).
+constexpr int tlds_smem(int op, int FM, int FN, int NW, int KW, int XD, int P) {
+  const int xb = XD == 1 ? 0
+                 : XD == 2 ? (P + 1) * KW * tlds_dma_chunk_bytes(op, FM) + 1024
+                           : 2 * KW * tlds_sub_bytes(op, FM);
+  const int rb = tlds_red_bytes(op, FM, FN, NW, KW);
   return (xb > rb ? xb : rb) + (op_packed(op) ? 0 : NW * tlds_wstage_bytes(op, FN));
 }
 constexpr int tlds_xpt(int op, int FM, int NW, int KW, int XD) {   // 16-byte x pieces per thread per round
-  return XD ? FM * tlds_xv(op) : (KW * 16 * FM * (tlds_xg_bytes(op) / 16) + 64 * NW - 1) / (64 * NW);
+  return XD == 2 ? 0 : XD ? FM * tlds_xv(op) : (KW * 16 * FM * (tlds_xg_bytes(op) / 16) + 64 * NW - 1) / (64 * NW);
 }
 constexpr int tlds_regs(int op, int FM, int FN, int P, int NW, int KW, int XD) {
   const int G = op_groups(op), b = op_base(op);
@@ -135,9 +145,12 @@ constexpr bool tlds_valid(int op, int FM, int FN, int S, int P, int NW, int KW, 
   const int G = op_groups(op);
   const bool q = op_base(op) == OP_A8W8Q;
   return (S == 1 || S == 2 || S == 4 || S == 8) && (NW == 4 || NW == 8) && (KW == 1 || KW == 2 || KW == 4 || KW == 8) &&
-         NW % KW == 0 && P >= 1 && G * FN * FM * 4 <= 128 && (XD == 0 || (XD == 1 && !q && FM <= 2)) &&
+         NW % KW == 0 && P >= 1 && G * FN * FM * 4 <= 128 &&
+         (XD == 0 || (XD == 1 && !q && FM <= 2) ||
+          (XD == 2 && (op_base(op) == OP_BF16 || op_base(op) == OP_GATED) && P <= 8 &&
+           tlds_dma_chunk_bytes(op, FM) % 1024 == 0)) &&
          tlds_regs(op, FM, FN, P, NW, KW, XD) <= (q && NW == 8 ? 160 : 224) &&
-         tlds_smem(op, FM, FN, NW, KW, XD) <= 64 * 1024 && (128 % (64 * FN)) == 0;
+         tlds_smem(op, FM, FN, NW, KW, XD, P) <= 64 * 1024 && (128 % (64 * FN)) == 0;
 }
 // Bytes of split-K partials a tlds launch with S > 1 needs, and the number of
 // output tiles (one arrival counter each) its grid has.

@@ -5,6 +5,8 @@
         --code-hash HASH [--cmd CMD]
     python -m gemv_skinny_gemm_02_amd.profsum mfma COUNTERS.csv [--cmd CMD]
     python -m gemv_skinny_gemm_02_amd.profsum pmc COUNTERS.csv [MORE.csv ...] [--cmd CMD]
+    python -m gemv_skinny_gemm_02_amd.profsum form CALLS.json --trace KERNEL_TRACE.csv \
+        [--fetch FETCH.csv --write WRITE.csv] [--pmc MORE.csv ...] [--cmd CMD]
 
 `trace` prints the per-kernel call count and average/min/max duration from a
 `--kernel-trace --stats` run.  `counters` turns two `--pmc FETCH_SIZE` and
@@ -14,7 +16,12 @@ reads and writes 262144 KiB): the factor is what the counter reads for that
 copy divided by 262144.  HBM bytes per launch = FETCH/fetch_factor +
 WRITE/write_factor, in KiB.  `mfma` summarises a `--pmc MfmaUtil
 SQ_INSTS_VALU_MFMA_MOPS_BF16` run: MFMA utilisation and issued bf16 MFMA flops
-per kernel.
+per kernel.  `form` pairs the GEMM dispatches of a `bench.py --profile-form`
+run, in launch order, with the call list that run wrote, and prints per call
+shape (op, M, N, K, variant): the median device duration, the algorithmic
+GB/s, and with the two counter runs the measured HBM bytes per launch and
+their ratio to the algorithmic bytes, and the mean per launch of every
+counter of any further `--pmc` runs (warm-up launches left out).
 """
 from __future__ import annotations
 
@@ -130,6 +137,94 @@ def pmc_summary(paths, cmd: str | None) -> str:
     return "\n".join(out) + "\n"
 
 
+GEMM_KERNELS = ("void skg::gemv_kernel", "void skg::tile_kernel", "void skg::tlds_kernel")
+
+
+def _gemm_dispatches(path: str, counter: str | None = None):
+    """The GEMM dispatches of one run in dispatch order: (kernel, value), the
+    value being the duration in ns (trace file) or the counter (pmc file)."""
+    rows = []
+    for r in csv.DictReader(open(path)):
+        if not r["Kernel_Name"].startswith(GEMM_KERNELS):
+            continue
+        if counter is None:
+            v = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+        elif r["Counter_Name"] == counter:
+            v = float(r["Counter_Value"])
+        else:
+            continue
+        rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], v))
+    rows.sort()
+    return [(k, v) for _, k, v in rows]
+
+
+def _pair(launches, disp, what):
+    if len(disp) != len(launches):
+        raise SystemExit(f"{what}: {len(disp)} GEMM dispatches for {len(launches)} calls")
+    return list(zip(launches, disp))
+
+
+def form_summary(calls: str, trace: str, fetch: str | None, write: str | None, cmd: str | None,
+                 pmc=()) -> str:
+    import json
+    info = json.load(open(calls))
+    launches = info["launches"]
+    t = _pair(launches, _gemm_dispatches(trace), "trace")
+    groups = defaultdict(lambda: defaultdict(list))
+    order = []
+    for c, (k, ns) in t:
+        key = (c["op"], c["M"], c["N"], c["K"], c["variant"], k, c["alg_bytes"])
+        if key not in order:
+            order.append(key)
+        if not c["warm"]:
+            groups[key]["ns"].append(ns)
+    ff = wf = None
+    if fetch and write:
+        ff = _copy_factor(_per_kernel(fetch, "FETCH_SIZE"))
+        wf = _copy_factor(_per_kernel(write, "WRITE_SIZE"))
+        for col, path, ctr in (("f", fetch, "FETCH_SIZE"), ("w", write, "WRITE_SIZE")):
+            for c, (k, v) in _pair(launches, _gemm_dispatches(path, ctr), ctr):
+                if not c["warm"]:
+                    groups[(c["op"], c["M"], c["N"], c["K"], c["variant"], k, c["alg_bytes"])][col].append(v)
+    extra = []
+    for path in pmc:
+        names = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] not in names:
+                names.append(r["Counter_Name"])
+        for ctr in names:
+            extra.append(ctr)
+            for c, (k, v) in _pair(launches, _gemm_dispatches(path, ctr), ctr):
+                if not c["warm"]:
+                    groups[(c["op"], c["M"], c["N"], c["K"], c["variant"], k, c["alg_bytes"])][ctr].append(v)
+    out = []
+    if cmd:
+        out.append(f"# command: {cmd}")
+    out.append(f"# form {info['form']}: {len(launches)} calls in launch order, paired one to one with the GEMM "
+               "dispatches; warm-up launches dropped")
+    if ff is not None:
+        out.append(f"# copy_fetch_factor={ff:.6f} copy_write_factor={wf:.6f} (the run's 256 MiB device copy); "
+                   "hbm_MB = (FETCH/fetch_factor + WRITE/write_factor) KiB per launch")
+    out.append("# op | M | N | K | variant | launches | median_us | alg_MB | alg_GB/s | hbm_MB | hbm/alg | "
+               + "".join(f"{e} | " for e in extra) + "kernel" + ("   (counters: mean per launch)" if extra else ""))
+    for key in order:
+        op, M, N, K, var, k, nb = key
+        g = groups[key]
+        if not g["ns"]:
+            continue
+        us = statistics.median(g["ns"]) / 1e3
+        line = f"{op} | {M} | {N} | {K} | {var} | {len(g['ns'])} | {us:.3f} | {nb / 1e6:.3f} | {nb / (us * 1e3):.1f}"
+        if ff is not None and g["f"] and g["w"]:
+            hb = (statistics.fmean(g["f"]) / ff + statistics.fmean(g["w"]) / wf) * 1024
+            line += f" | {hb / 1e6:.3f} | {hb / nb:.3f}"
+        else:
+            line += " | nan | nan"
+        for e in extra:
+            line += f" | {statistics.fmean(g[e]):.6g}" if g[e] else " | nan"
+        out.append(line + f" | {k}")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -148,8 +243,17 @@ def main(argv=None) -> int:
     m = sub.add_parser("mfma")
     m.add_argument("counters")
     m.add_argument("--cmd")
+    f = sub.add_parser("form")
+    f.add_argument("calls")
+    f.add_argument("--trace", required=True, help="the per-dispatch kernel trace csv")
+    f.add_argument("--fetch")
+    f.add_argument("--write")
+    f.add_argument("--pmc", action="append", default=[], help="a further counter run (repeatable)")
+    f.add_argument("--cmd")
     a = ap.parse_args(argv)
-    if a.mode == "trace":
+    if a.mode == "form":
+        sys.stdout.write(form_summary(a.calls, a.trace, a.fetch, a.write, a.cmd, a.pmc))
+    elif a.mode == "trace":
         sys.stdout.write(trace_summary(a.stats, a.cmd, a.dispatches))
     elif a.mode == "pmc":
         sys.stdout.write(pmc_summary(a.counters, a.cmd))

@@ -21,6 +21,7 @@ import gemv_skinny_gemm_02_amd as skg
     ("tlds_f1_s4_p4", 40, "void skg::tlds_kernel<0, 4, 1, 4, 4, 4, 1, 0>(skg::Args)"),   # 3 fragments -> the 4 build
     ("tlds_d_k4_f1_s1_p4_m1", 4, "void skg::tlds_kernel<0, 1, 1, 1, 4, 4, 4, 1>(skg::Args)"),
     ("tlds_d_w8_k8_f1_s1_p4_m2", 32, "void skg::tlds_kernel<0, 2, 1, 1, 4, 8, 8, 1>(skg::Args)"),
+    ("tlds_x_w8_k2_f2_s4_p2_m4", 128, "void skg::tlds_kernel<0, 4, 2, 4, 2, 8, 2, 2>(skg::Args)"),
 ])
 def test_kernel_symbol(variant, M, symbol):
     assert bench.kernel_symbol(variant, M) == symbol
@@ -35,7 +36,8 @@ def test_every_variant_name_parses():
                 sym = bench.kernel_symbol(name, M, skg.OPS[op])
                 assert sym.startswith("void skg::") and sym.endswith("(skg::Args)")
                 if name.startswith("tlds"):
-                    assert sym.endswith(f", {1 if name.startswith('tlds_d_') else 0}>(skg::Args)"), (name, sym)
+                    xd = 1 if name.startswith("tlds_d_") else (2 if name.startswith("tlds_x_") else 0)
+                    assert sym.endswith(f", {xd}>(skg::Args)"), (name, sym)
 
 
 def test_read_counters(tmp_path, monkeypatch):
@@ -95,3 +97,44 @@ def test_printed_line_is_short():
     for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert k in line["roofline"]
     assert line["metric"] == "achieved HBM GB/s and \u00b5s/call at M=1/8/128; fraction of MI355X roofline"
+
+
+def test_profsum_form_pairs_dispatches_with_calls(tmp_path):
+    """The form summary pairs GEMM dispatches with the call list in dispatch
+    order, skips non-GEMM kernels and warm-up launches, and calibrates the
+    counters on the 256 MiB copy."""
+    import csv
+    import json
+
+    from gemv_skinny_gemm_02_amd import profsum
+
+    gemm = "void skg::tlds_kernel<5, 1, 1, 1, 4, 4, 4, 0>(skg::Args)"
+    other = "void skg::(anonymous namespace)::pack_kernel<false>(char const*)"
+    calls = [{"op": "bf16_packed", "M": 8, "N": 1024, "K": 1024, "alg_bytes": 2_000_000, "warm": w,
+              "variant": "tlds_f1_s1_p4_m4"} for w in (True, False, False)]
+    (tmp_path / "calls.json").write_text(json.dumps({"form": "bf16", "launches": calls}))
+    # dispatch ids out of file order on purpose; a pack dispatch in between
+    trace = [(3, gemm, 0, 1000), (1, gemm, 0, 9000), (2, other, 0, 5), (4, gemm, 0, 3000)]
+    with open(tmp_path / "trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writerows(trace)
+    for name, ctr, copy_v, v in (("fetch", "FETCH_SIZE", 131072.0, 1000.0), ("write", "WRITE_SIZE", 262144.0, 16.0)):
+        with open(tmp_path / f"{name}.csv", "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writerow([1, gemm, ctr, 99999.0])
+            w.writerow([3, gemm, ctr, v])
+            w.writerow([4, gemm, ctr, v])
+            w.writerow([5, profsum.COPY_KERNEL, ctr, copy_v])
+    out = profsum.form_summary(str(tmp_path / "calls.json"), str(tmp_path / "trace.csv"),
+                               str(tmp_path / "fetch.csv"), str(tmp_path / "write.csv"), "cmd")
+    row = [l for l in out.splitlines() if l.startswith("bf16_packed")]
+    assert len(row) == 1
+    cells = [c.strip() for c in row[0].split("|")]
+    assert cells[5] == "2"                      # two timed launches, the warm one dropped
+    assert cells[6] == "2.000"                  # median of 1 us and 3 us
+    assert cells[8] == "1000.0"                 # 2 MB / 2 us
+    assert abs(float(cells[9]) - (1000 / 0.5 + 16) * 1024 / 1e6) < 1e-3
+    with pytest.raises(SystemExit):             # a count mismatch is refused, not paired loosely
+        profsum._pair(calls, [("k", 1.0)], "trace")
