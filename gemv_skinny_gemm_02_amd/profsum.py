@@ -164,6 +164,28 @@ def _pair(launches, disp, what):
     return list(zip(launches, disp))
 
 
+# Ratios printed beside the raw counters when a run holds what they need.
+DERIVED_NEEDS = {
+    "wait_frac": ("SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
+    "lds_conflict_frac": ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"),
+    "l2_read_latency_cyc": ("TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum"),
+    "ta_stalled_by_tc_frac": ("TA_ADDR_STALLED_BY_TC_CYCLES_sum", "TA_BUSY_avr"),
+}
+DERIVED_DOC = {
+    "wait_frac": "SQ_WAIT_ANY / SQ_WAVE_CYCLES: share of wave cycles spent waiting on a counter (memory, LDS)",
+    "lds_conflict_frac": "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE: share of LDS cycles lost to bank conflicts",
+    "l2_read_latency_cyc": "TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum: mean L1->L2 read latency, cycles",
+    "ta_stalled_by_tc_frac": "TA_ADDR_STALLED_BY_TC_CYCLES_sum / (TA_BUSY_avr x 16 TA units): address unit stalled "
+                             "on the L1 (approximate normalisation)",
+}
+DERIVED = [
+    ("wait_frac", lambda v: v["SQ_WAIT_ANY"] / v["SQ_WAVE_CYCLES"]),
+    ("lds_conflict_frac", lambda v: v["SQ_LDS_BANK_CONFLICT"] / v["SQ_LDS_IDX_ACTIVE"]),
+    ("l2_read_latency_cyc", lambda v: v["TCP_TCC_READ_REQ_LATENCY_sum"] / v["TCP_TCC_READ_REQ_sum"]),
+    ("ta_stalled_by_tc_frac", lambda v: v["TA_ADDR_STALLED_BY_TC_CYCLES_sum"] / (v["TA_BUSY_avr"] * 16)),
+]
+
+
 def form_summary(calls: str, trace: str, fetch: str | None, write: str | None, cmd: str | None,
                  pmc=()) -> str:
     import json
@@ -197,16 +219,20 @@ def form_summary(calls: str, trace: str, fetch: str | None, write: str | None, c
             for c, (k, v) in _pair(launches, _gemm_dispatches(path, ctr), ctr):
                 if not c["warm"]:
                     groups[(c["op"], c["M"], c["N"], c["K"], c["variant"], k, c["alg_bytes"])][ctr].append(v)
+    derived = [(name, f) for name, f in DERIVED if all(c in extra for c in DERIVED_NEEDS[name])]
     out = []
     if cmd:
         out.append(f"# command: {cmd}")
+    for name, _ in derived:
+        out.append(f"# {name} = {DERIVED_DOC[name]}")
     out.append(f"# form {info['form']}: {len(launches)} calls in launch order, paired one to one with the GEMM "
                "dispatches; warm-up launches dropped")
     if ff is not None:
         out.append(f"# copy_fetch_factor={ff:.6f} copy_write_factor={wf:.6f} (the run's 256 MiB device copy); "
                    "hbm_MB = (FETCH/fetch_factor + WRITE/write_factor) KiB per launch")
     out.append("# op | M | N | K | variant | launches | median_us | alg_MB | alg_GB/s | hbm_MB | hbm/alg | "
-               + "".join(f"{e} | " for e in extra) + "kernel" + ("   (counters: mean per launch)" if extra else ""))
+               + "".join(f"{e} | " for e in extra) + "".join(f"{n} | " for n, _ in derived) + "kernel"
+               + ("   (counters: mean per launch)" if extra else ""))
     for key in order:
         op, M, N, K, var, k, nb = key
         g = groups[key]
@@ -221,6 +247,11 @@ def form_summary(calls: str, trace: str, fetch: str | None, write: str | None, c
             line += " | nan | nan"
         for e in extra:
             line += f" | {statistics.fmean(g[e]):.6g}" if g[e] else " | nan"
+        for _, fn in derived:
+            try:
+                line += f" | {fn({c: statistics.fmean(g[c]) for c in extra if g[c]}):.3f}"
+            except (KeyError, ZeroDivisionError):
+                line += " | nan"
         out.append(line + f" | {k}")
     return "\n".join(out) + "\n"
 
