@@ -67,8 +67,13 @@ def kernel_symbol(variant: str, M: int, op: int = 0) -> str:
     tlds[_d|_x][_w<NW>][_k<KW>]_f<FN>_s<S>_p<P>[_m<MC>] (d: direct x; x: x copied
     into LDS by DMA; NW waves,
     default 4, of which KW split K inside the workgroup, default 1; at most MC
-    16-row fragments per workgroup, default 8)."""
+    16-row fragments per workgroup, default 8), and the two-operand tile
+    mt_m<FM>_f<FN>_a<WM>_b<WN>_s<S>_p<P>."""
     parts = variant.split("_")
+    if parts[0] == "mt":                      # mt_m<FM>_f<FN>_a<WM>_b<WN>_s<S>_p<P>
+        kv = {p[0]: int(p[1:]) for p in parts[1:]}
+        return (f"void skg::mt_kernel<{op}, {kv['m']}, {kv['f']}, {kv['a']}, {kv['b']}, {kv['s']}, "
+                f"{kv['p']}>(skg::Args)")
     xd = 1 if "d" in parts[1:] else (2 if "x" in parts[1:] else 0)
     kv = {p[0]: int(p[1:]) for p in parts[1:] if p not in ("d", "x")}
     if parts[0] == "gemv":

@@ -24,7 +24,7 @@
 #include <unordered_map>
 #include <vector>
 
-#include "kernels.hpp"
+#include "kernels_mt.hpp"
 #include "skinny_gemm.h"
 #include "table.hpp"
 
@@ -304,6 +304,16 @@ skg_status validate(int op, const Args& a) {
 LaunchFn variant_fn(int op, int v, int M) {
   const VariantDesc& d = kVariants[v];
   const int fi = family_index(v);
+  if (d.family == FAM_MT) {
+    const LaunchFn* t = nullptr;
+    switch (op) {
+      case OP_BF16: t = mt_table<OP_BF16>(); break;
+      case OP_A8W8: t = mt_table<OP_A8W8>(); break;
+      case OP_PACKED + OP_BF16: t = mt_table<OP_PACKED + OP_BF16>(); break;
+      case OP_PACKED + OP_A8W8: t = mt_table<OP_PACKED + OP_A8W8>(); break;
+    }
+    return t ? t[fi] : nullptr;
+  }
   if (d.family == FAM_GEMV) {
     const int mi = gemv_mt_index(M);
     if (mi < 0) return nullptr;
@@ -338,11 +348,17 @@ LaunchFn variant_fn(int op, int v, int M) {
 // Bytes of split-K partials variant v of op needs for M rows (0: none), and
 // whether its output tiles fit the arrival counters.
 size_t partial_bytes(int op, int v, int M, int N) {
-  if (v < 0 || kVariants[v].family != FAM_TLDS) return 0;
+  if (v < 0) return 0;
+  if (kVariants[v].family == FAM_MT) return (size_t)tlds_ws_bytes(op, kVariants[v].p4, M, N);
+  if (kVariants[v].family != FAM_TLDS) return 0;
   return (size_t)tlds_ws_bytes(op, kVariants[v].p1, M, N);
 }
 bool tiles_fit(int op, int v, int M, int N) {
   (void)op;
+  if (kVariants[v].family == FAM_MT) {
+    const VariantDesc& d = kVariants[v];
+    return mt_tiles(d.p0, d.p1, d.p2, d.p3, M, N) <= (unsigned long long)kSplitCounters;
+  }
   const int fm = M > kMaxBucket ? kNumTileFM - 1 : tile_fm_index(M);
   const VariantDesc& d = kVariants[v];
   return tlds_tiles(d.p0, d.p4 / d.p5, tlds_fm(kTileFM[fm], d.p3), M, N) <= (unsigned long long)kSplitCounters;

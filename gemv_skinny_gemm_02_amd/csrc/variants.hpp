@@ -12,7 +12,7 @@ namespace skg {
 enum Op : int { OP_BF16 = 0, OP_GATED = 1, OP_FP8T = 2, OP_A8W8 = 3, OP_A8W8Q = 4, OP_PACKED = 5, NUM_OPS = 10 };
 constexpr int op_base(int op) { return op >= OP_PACKED ? op - OP_PACKED : op; }
 constexpr bool op_packed(int op) { return op >= OP_PACKED; }
-enum Family : int { FAM_GEMV = 0, FAM_TILE = 1, FAM_TLDS = 2 };
+enum Family : int { FAM_GEMV = 0, FAM_TILE = 1, FAM_TLDS = 2, FAM_MT = 3 };
 
 // Rows buckets: M is rounded up to the next one (padded-M lookup with no
 // nearest fallback: Decode optimization round 3, "Retained change 2";
@@ -171,6 +171,32 @@ constexpr unsigned long long packed_weight_bytes(int op, int N, int K) {
 constexpr int tlds_fm(int FM, int MC) { return FM < MC ? FM : MC; }
 constexpr int kSplitCounters = 65536;   // arrival counters kept in the workspace
 
+// Two-operand LDS tile (mt): a workgroup of WM x WN waves owns BM = 16*FM*WM x
+// rows by BN = 16*FN*WN weight rows; each chunk (128 bytes of every row) of
+// both operands is copied by DMA into one of P + 1 LDS stages.  Served forms:
+// bf16 and A8W8, row-major or fragment-packed weights.
+constexpr bool mt_op(int op) { return op_base(op) == OP_BF16 || op_base(op) == OP_A8W8; }
+constexpr int mt_stage_bytes(int op, int FM, int FN, int WM, int WN) {
+  return 128 * (16 * FM * WM + 16 * FN * WN) + (op_base(op) == OP_A8W8 ? 16 * FM * WM * 4 + 256 : 0);
+}
+constexpr int mt_lds_bytes(int op, int FM, int FN, int WM, int WN, int P) {
+  return (P + 1) * mt_stage_bytes(op, FM, FN, WM, WN) + 1024;
+}
+constexpr int mt_copies_per_wave(int op, int FM, int FN, int WM, int WN) {
+  const int blocks = 2 * FN * WN + 2 * FM * WM + (op_base(op) == OP_A8W8 ? FM * WM / 4 + 1 : 0);
+  return (blocks + WM * WN - 1) / (WM * WN);
+}
+constexpr bool mt_valid(int op, int FM, int FN, int WM, int WN, int S, int P) {
+  return mt_op(op) && FM >= 1 && FN >= 1 && FM * FN <= 32 && (WM * WN == 4 || WM * WN == 8) &&
+         (FM * WM) % 4 == 0 && (S == 1 || S == 2 || S == 4 || S == 8) && P >= 1 && P <= 4 &&
+         mt_lds_bytes(op, FM, FN, WM, WN, P) <= 160 * 1024 &&
+         (P - 1) * mt_copies_per_wave(op, FM, FN, WM, WN) <= 63;
+}
+constexpr unsigned long long mt_tiles(int FM, int FN, int WM, int WN, int M, int N) {
+  return (unsigned long long)((N + 16 * FN * WN - 1) / (16 * FN * WN)) *
+         (unsigned long long)((M + 16 * FM * WM - 1) / (16 * FM * WM));
+}
+
 // The MFMA tile path serves every rows bucket: rows past M inside a 16-row
 // fragment re-read row M-1 and are never stored, so a table may pick it
 // wherever it streams the weight faster than the VALU path, even for one row.
@@ -179,6 +205,7 @@ struct VariantDesc {
   const char* name;
   int family;
   int p0, p1, p2, p3, p4, p5, p6;  // GEMV: R, KS, U.  TILE: FN, KS, U.  TLDS: FN, S, P, MC, NW, KW, XD.
+                                   // MT: FM, FN, WM, WN, S, P.
 };
 
 constexpr VariantDesc kVariants[] = {
@@ -189,6 +216,9 @@ constexpr VariantDesc kVariants[] = {
 #undef SKG_GEMV
 #undef SKG_TILE
 #undef SKG_TLDS
+#define SKG_MT(name, FM, FN, WM, WN, S, P) {#name, FAM_MT, FM, FN, WM, WN, S, P, 0},
+#include "variants_mt.def"
+#undef SKG_MT
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -200,6 +230,7 @@ constexpr int count_family(int fam) {
 constexpr int kNumGemv = count_family(FAM_GEMV);
 constexpr int kNumTile = count_family(FAM_TILE);
 constexpr int kNumTlds = count_family(FAM_TLDS);
+constexpr int kNumMt = count_family(FAM_MT);
 // index of variant i inside its family's launch table
 constexpr int family_index(int i) {
   int n = 0;
@@ -214,6 +245,7 @@ constexpr bool variant_supports(int op, int i, int M) {
     const int mi = gemv_mt_index(M);
     return mi >= 0 && gemv_valid(op, kGemvMT[mi], v.p0, v.p1, v.p2);
   }
+  if (v.family == FAM_MT) return mt_valid(op, v.p0, v.p1, v.p2, v.p3, v.p4, v.p5);
   const int fm = M > kMaxBucket ? kNumTileFM - 1 : tile_fm_index(M);
   if (v.family == FAM_TLDS) return tlds_valid(op, tlds_fm(kTileFM[fm], v.p3), v.p0, v.p1, v.p2, v.p4, v.p5, v.p6);
   return tile_valid(op, kTileFM[fm], v.p0, v.p1, v.p2);
@@ -234,7 +266,10 @@ constexpr const char kSpaceText[] =
 #undef SKG_GEMV
 #undef SKG_TILE
 #undef SKG_TLDS
-    "kernels=15";  // bump when a kernel's arithmetic or indexing changes
+#define SKG_MT(name, FM, FN, WM, WN, S, P) "X:" #name "," #FM "," #FN "," #WM "," #WN "," #S "," #P ";"
+#include "variants_mt.def"
+#undef SKG_MT
+    "kernels=16";  // bump when a kernel's arithmetic or indexing changes
 constexpr uint32_t kSpaceToken = fnv1a(kSpaceText);
 
 }  // namespace skg

@@ -292,7 +292,9 @@ def promote(store, out, identity=None, merge=None):
         slot = by_key[k]
         default = next(iter(slot.values()))["default"]
         cands = sorted(slot.values(), key=lambda r: (r["us"], r["variant"]))
-        choice = choose(default, {r["variant"]: r["us"] for r in cands})
+        # the rule sees the times the table stores (rounded to the ns), so that
+        # `check` re-derives exactly this choice
+        choice = choose(default, {r["variant"]: round(r["us"], 3) for r in cands})
         entries.append({"op": k[0], "rows": k[1], "N": k[2], "K": k[3], "choice": choice, "default": default,
                         "measured_M": slot[choice]["M"], "us": round(slot[choice]["us"], 3),
                         "candidates": {r["variant"]: {"us": round(r["us"], 3)} for r in cands}})

@@ -22,19 +22,23 @@ import gemv_skinny_gemm_02_amd as skg
     ("tlds_d_k4_f1_s1_p4_m1", 4, "void skg::tlds_kernel<0, 1, 1, 1, 4, 4, 4, 1>(skg::Args)"),
     ("tlds_d_w8_k8_f1_s1_p4_m2", 32, "void skg::tlds_kernel<0, 2, 1, 1, 4, 8, 8, 1>(skg::Args)"),
     ("tlds_x_w8_k2_f2_s4_p2_m4", 128, "void skg::tlds_kernel<0, 4, 2, 4, 2, 8, 2, 2>(skg::Args)"),
+    ("mt_m4_f2_a2_b4_s2_p3", 512, "void skg::mt_kernel<0, 4, 2, 2, 4, 2, 3>(skg::Args)"),   # any M: one build
 ])
 def test_kernel_symbol(variant, M, symbol):
     assert bench.kernel_symbol(variant, M) == symbol
 
 
 def test_every_variant_name_parses():
-    for op in ("bf16", "bf16_packed"):
+    for op in ("bf16", "bf16_packed", "a8w8_block_packed"):
         for i, name in enumerate(skg.variants(op)):
             for M in (1, 16, 128):
                 if not skg.skinny_gemm_variant_supports(op, i, M):
                     continue
                 sym = bench.kernel_symbol(name, M, skg.OPS[op])
                 assert sym.startswith("void skg::") and sym.endswith("(skg::Args)")
+                if name.startswith("mt_"):
+                    v = [int(p[1:]) for p in name.split("_")[1:]]
+                    assert sym == f"void skg::mt_kernel<{skg.OPS[op]}, {', '.join(map(str, v))}>(skg::Args)", (name, sym)
                 if name.startswith("tlds"):
                     xd = 1 if name.startswith("tlds_d_") else (2 if name.startswith("tlds_x_") else 0)
                     assert sym.endswith(f", {xd}>(skg::Args)"), (name, sym)
