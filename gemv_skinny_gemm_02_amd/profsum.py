@@ -169,20 +169,21 @@ DERIVED_NEEDS = {
     "wait_frac": ("SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
     "lds_conflict_frac": ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"),
     "l2_read_latency_cyc": ("TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum"),
-    "ta_stalled_by_tc_frac": ("TA_ADDR_STALLED_BY_TC_CYCLES_sum", "TA_BUSY_avr"),
+    "ta_units_stalled": ("TA_ADDR_STALLED_BY_TC_CYCLES_sum", "TA_BUSY_avr"),
 }
 DERIVED_DOC = {
     "wait_frac": "SQ_WAIT_ANY / SQ_WAVE_CYCLES: share of wave cycles spent waiting on a counter (memory, LDS)",
     "lds_conflict_frac": "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE: share of LDS cycles lost to bank conflicts",
     "l2_read_latency_cyc": "TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum: mean L1->L2 read latency, cycles",
-    "ta_stalled_by_tc_frac": "TA_ADDR_STALLED_BY_TC_CYCLES_sum / (TA_BUSY_avr x 16 TA units): address unit stalled "
-                             "on the L1 (approximate normalisation)",
+    "ta_units_stalled": "TA_ADDR_STALLED_BY_TC_CYCLES_sum / TA_BUSY_avr: address-stall cycles (waiting on the "
+                        "vector L1) summed over the TA units per busy cycle of the average unit, i.e. how many "
+                        "units are stalled at once on average",
 }
 DERIVED = [
     ("wait_frac", lambda v: v["SQ_WAIT_ANY"] / v["SQ_WAVE_CYCLES"]),
     ("lds_conflict_frac", lambda v: v["SQ_LDS_BANK_CONFLICT"] / v["SQ_LDS_IDX_ACTIVE"]),
     ("l2_read_latency_cyc", lambda v: v["TCP_TCC_READ_REQ_LATENCY_sum"] / v["TCP_TCC_READ_REQ_sum"]),
-    ("ta_stalled_by_tc_frac", lambda v: v["TA_ADDR_STALLED_BY_TC_CYCLES_sum"] / (v["TA_BUSY_avr"] * 16)),
+    ("ta_units_stalled", lambda v: v["TA_ADDR_STALLED_BY_TC_CYCLES_sum"] / v["TA_BUSY_avr"]),
 ]
 
 
