@@ -68,8 +68,13 @@ def kernel_symbol(variant: str, M: int, op: int = 0) -> str:
     into LDS by DMA; NW waves,
     default 4, of which KW split K inside the workgroup, default 1; at most MC
     16-row fragments per workgroup, default 8), and the two-operand tile
-    mt_m<FM>_f<FN>_a<WM>_b<WN>_s<S>_p<P>."""
+    mt_m<FM>_f<FN>_a<WM>_b<WN>_s<S>_p<P>, and the packed-weight stream
+    pg_r<RW>_k<KS>_p<P>."""
     parts = variant.split("_")
+    if parts[0] == "pg":                      # pg_r<RW>_k<KS>_p<P>
+        kv = {p[0]: int(p[1:]) for p in parts[1:]}
+        mt = next(b for b in (1, 2, 3, 4, 6, 8, 12, 16) if M <= b)
+        return f"void skg::pg_kernel<{op}, {mt}, {kv['r']}, {kv['k']}, {kv['p']}>(skg::Args)"
     if parts[0] == "mt":                      # mt_m<FM>_f<FN>_a<WM>_b<WN>_s<S>_p<P>
         kv = {p[0]: int(p[1:]) for p in parts[1:]}
         return (f"void skg::mt_kernel<{op}, {kv['m']}, {kv['f']}, {kv['a']}, {kv['b']}, {kv['s']}, "

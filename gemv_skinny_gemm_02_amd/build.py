@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libskinny_gemm.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["abi.hip", "pack.hip", "calib.hip", "ops_bf16.hip", "ops_gated.hip", "ops_fp8t.hip", "ops_a8w8.hip", "ops_a8w8q.hip",
-               "ops_bf16p.hip", "ops_gatedp.hip", "ops_fp8tp.hip", "ops_a8w8p.hip", "ops_a8w8qp.hip", "ops_mt.hip"]
+               "ops_bf16p.hip", "ops_gatedp.hip", "ops_fp8tp.hip", "ops_a8w8p.hip", "ops_a8w8qp.hip", "ops_mt.hip", "ops_pg.hip"]
 CXX_SOURCES = ["table.cpp"]
 
 # Packed fp32 VALU ops are kept out of the device code: hipcc -O3 would form

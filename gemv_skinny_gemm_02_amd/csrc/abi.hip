@@ -25,6 +25,7 @@
 #include <vector>
 
 #include "kernels_mt.hpp"
+#include "kernels_pg.hpp"
 #include "skinny_gemm.h"
 #include "table.hpp"
 
@@ -304,6 +305,13 @@ skg_status validate(int op, const Args& a) {
 LaunchFn variant_fn(int op, int v, int M) {
   const VariantDesc& d = kVariants[v];
   const int fi = family_index(v);
+  if (d.family == FAM_PG) {
+    const int mi = gemv_mt_index(M);
+    const GemvRow* t = op == OP_PACKED + OP_BF16   ? pg_table<OP_PACKED + OP_BF16>()
+                       : op == OP_PACKED + OP_GATED ? pg_table<OP_PACKED + OP_GATED>()
+                                                    : nullptr;
+    return t && mi >= 0 ? t[fi].f[mi] : nullptr;
+  }
   if (d.family == FAM_MT) {
     const LaunchFn* t = nullptr;
     switch (op) {
@@ -506,7 +514,7 @@ skg_status launch(int op, int v, const Args& a_in, hipStream_t s, WsFrom from) {
     a.cnt = reinterpret_cast<unsigned*>(base);
     a.ws = reinterpret_cast<float*>(base + kCntBytes);
   }
-  if (op == OP_A8W8 && kVariants[v].family == FAM_GEMV) {
+  if (op_base(op) == OP_A8W8 && kVariants[v].family == FAM_GEMV) {
     const size_t smem = (size_t)(kGemvMT[gemv_mt_index(a.M)] + 1) * a.kb * sizeof(float);
     if (smem > 64 * 1024)
       return fail(SKG_EUNSUPPORTED, "K=%d needs %zu bytes of A8W8 scale staging (limit 65536)", a.K, smem);

@@ -12,7 +12,7 @@ namespace skg {
 enum Op : int { OP_BF16 = 0, OP_GATED = 1, OP_FP8T = 2, OP_A8W8 = 3, OP_A8W8Q = 4, OP_PACKED = 5, NUM_OPS = 10 };
 constexpr int op_base(int op) { return op >= OP_PACKED ? op - OP_PACKED : op; }
 constexpr bool op_packed(int op) { return op >= OP_PACKED; }
-enum Family : int { FAM_GEMV = 0, FAM_TILE = 1, FAM_TLDS = 2, FAM_MT = 3 };
+enum Family : int { FAM_GEMV = 0, FAM_TILE = 1, FAM_TLDS = 2, FAM_MT = 3, FAM_PG = 4 };
 
 // Rows buckets: M is rounded up to the next one (padded-M lookup with no
 // nearest fallback: Decode optimization round 3, "Retained change 2";
@@ -188,13 +188,21 @@ constexpr int mt_copies_per_wave(int op, int FM, int FN, int WM, int WN) {
 }
 constexpr bool mt_valid(int op, int FM, int FN, int WM, int WN, int S, int P) {
   return mt_op(op) && FM >= 1 && FN >= 1 && FM * FN <= 32 && (WM * WN == 4 || WM * WN == 8) &&
-         (FM * WM) % 4 == 0 && (S == 1 || S == 2 || S == 4 || S == 8) && P >= 1 && P <= 4 &&
+         (FM * WM) % 4 == 0 && S >= 1 && S <= 8 && P >= 1 && P <= 4 &&
          mt_lds_bytes(op, FM, FN, WM, WN, P) <= 160 * 1024 &&
          (P - 1) * mt_copies_per_wave(op, FM, FN, WM, WN) <= 63;
 }
 constexpr unsigned long long mt_tiles(int FM, int FN, int WM, int WN, int M, int N) {
   return (unsigned long long)((N + 16 * FN * WN - 1) / (16 * FN * WN)) *
          (unsigned long long)((M + 16 * FM * WM - 1) / (16 * FM * WM));
+}
+
+// Packed-weight stream (pg): RW weight rows per workgroup of KS waves, for
+// the packed bf16 and gated forms at the rows buckets up to 8.
+constexpr int kPgMaxM = 8;
+constexpr bool pg_valid(int op, int MT, int RW, int KS, int P) {
+  return op_packed(op) && (op_base(op) == OP_BF16 || op_base(op) == OP_GATED) && MT >= 1 && MT <= kPgMaxM &&
+         (RW == 2 || RW == 4 || RW == 8) && (KS == 4 || KS == 8 || KS == 16) && P >= 1 && P <= 4;
 }
 
 // The MFMA tile path serves every rows bucket: rows past M inside a 16-row
@@ -205,7 +213,7 @@ struct VariantDesc {
   const char* name;
   int family;
   int p0, p1, p2, p3, p4, p5, p6;  // GEMV: R, KS, U.  TILE: FN, KS, U.  TLDS: FN, S, P, MC, NW, KW, XD.
-                                   // MT: FM, FN, WM, WN, S, P.
+                                   // MT: FM, FN, WM, WN, S, P.  PG: RW, KS, P.
 };
 
 constexpr VariantDesc kVariants[] = {
@@ -219,6 +227,9 @@ constexpr VariantDesc kVariants[] = {
 #define SKG_MT(name, FM, FN, WM, WN, S, P) {#name, FAM_MT, FM, FN, WM, WN, S, P, 0},
 #include "variants_mt.def"
 #undef SKG_MT
+#define SKG_PG(name, RW, KS, P) {#name, FAM_PG, RW, KS, P, 0, 0, 0, 0},
+#include "variants_pg.def"
+#undef SKG_PG
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -231,6 +242,7 @@ constexpr int kNumGemv = count_family(FAM_GEMV);
 constexpr int kNumTile = count_family(FAM_TILE);
 constexpr int kNumTlds = count_family(FAM_TLDS);
 constexpr int kNumMt = count_family(FAM_MT);
+constexpr int kNumPg = count_family(FAM_PG);
 // index of variant i inside its family's launch table
 constexpr int family_index(int i) {
   int n = 0;
@@ -246,6 +258,10 @@ constexpr bool variant_supports(int op, int i, int M) {
     return mi >= 0 && gemv_valid(op, kGemvMT[mi], v.p0, v.p1, v.p2);
   }
   if (v.family == FAM_MT) return mt_valid(op, v.p0, v.p1, v.p2, v.p3, v.p4, v.p5);
+  if (v.family == FAM_PG) {
+    const int mi = gemv_mt_index(M);
+    return mi >= 0 && pg_valid(op, kGemvMT[mi], v.p0, v.p1, v.p2);
+  }
   const int fm = M > kMaxBucket ? kNumTileFM - 1 : tile_fm_index(M);
   if (v.family == FAM_TLDS) return tlds_valid(op, tlds_fm(kTileFM[fm], v.p3), v.p0, v.p1, v.p2, v.p4, v.p5, v.p6);
   return tile_valid(op, kTileFM[fm], v.p0, v.p1, v.p2);
@@ -269,7 +285,10 @@ constexpr const char kSpaceText[] =
 #define SKG_MT(name, FM, FN, WM, WN, S, P) "X:" #name "," #FM "," #FN "," #WM "," #WN "," #S "," #P ";"
 #include "variants_mt.def"
 #undef SKG_MT
-    "kernels=16";  // bump when a kernel's arithmetic or indexing changes
+#define SKG_PG(name, RW, KS, P) "Q:" #name "," #RW "," #KS "," #P ";"
+#include "variants_pg.def"
+#undef SKG_PG
+    "kernels=18";  // bump when a kernel's arithmetic or indexing changes
 constexpr uint32_t kSpaceToken = fnv1a(kSpaceText);
 
 }  // namespace skg

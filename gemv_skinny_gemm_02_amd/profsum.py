@@ -137,7 +137,8 @@ def pmc_summary(paths, cmd: str | None) -> str:
     return "\n".join(out) + "\n"
 
 
-GEMM_KERNELS = ("void skg::gemv_kernel", "void skg::tile_kernel", "void skg::tlds_kernel", "void skg::mt_kernel")
+GEMM_KERNELS = ("void skg::gemv_kernel", "void skg::tile_kernel", "void skg::tlds_kernel", "void skg::mt_kernel",
+                "void skg::pg_kernel")
 
 
 def _gemm_dispatches(path: str, counter: str | None = None):

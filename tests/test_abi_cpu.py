@@ -66,11 +66,18 @@ def test_variants_and_buckets():
     for op in skg.OPS:
         for M in range(1, 601):
             assert any(skg.skinny_gemm_variant_supports(op, i, M) for i in range(len(names))), (op, M)
-    # GEMV variants never claim rows above 16; the bf16 tile variants serve
-    # every bucket from one row
+    # GEMV variants never claim rows above 16; the packed-weight stream serves
+    # only the packed bf16 and gated forms, up to 8 rows; the bf16 tile
+    # variants serve every bucket from one row
     for i, n in enumerate(names):
         if n.startswith("gemv_"):
             assert not skg.skinny_gemm_variant_supports("bf16", i, 17)
+        elif n.startswith("pg_"):
+            assert not skg.skinny_gemm_variant_supports("bf16", i, 1)
+            assert skg.skinny_gemm_variant_supports("bf16_packed", i, 8)
+            assert skg.skinny_gemm_variant_supports("gated_packed", i, 1)
+            assert not skg.skinny_gemm_variant_supports("bf16_packed", i, 9)
+            assert not skg.skinny_gemm_variant_supports("a8w8_block_packed", i, 1)
         else:
             assert skg.skinny_gemm_variant_supports("bf16", i, 1)
 
