@@ -495,6 +495,10 @@ skg_status launch(int op, int v, const Args& a_in, hipStream_t s, WsFrom from) {
   if (const size_t need = partial_bytes(op, v, a.M, a.N)) {
     if (!tiles_fit(op, v, a.M, a.N))
       return fail(SKG_EUNSUPPORTED, "%s: more output tiles than split-K counters", kVariants[v].name);
+    // the kernels address the partials through a 32-bit buffer range
+    if (need >= (size_t)1 << 32)
+      return fail(SKG_EUNSUPPORTED, "%s at M=%d N=%d: %zu bytes of split-K partials exceed the 4 GiB the kernels address",
+                  kVariants[v].name, a.M, a.N, need);
     char* base = nullptr;
     if (from == WsFrom::kStatic) {
       if (need > kStaticPartialBytes)

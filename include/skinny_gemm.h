@@ -59,7 +59,8 @@
  *           #1104, "What changed": one per-device table).  A miss, an absent
  *           table or a refused table uses the built-in default for the op and
  *           bucket; M above 512 uses the untuned default.  Rows above 128 run
- *           on the MFMA tile path in launch rows of at most 128.
+ *           on the MFMA tile paths (launch rows of at most 128 x rows, or the
+ *           two-operand tile's own row tiles).
  * Threads.  GEMM calls are reentrant.  skinny_gemm_load_table must not run
  *           concurrently with other calls.
  * Workspace. Some variants split K across workgroups and pass float32
@@ -68,8 +69,9 @@
  *           skinny_gemm_set_device_workspace (every stream of the device that
  *           has none of its own).  skinny_gemm_workspace_bytes tells how much a
  *           call needs; a call whose dispatch choice needs more than its
- *           stream's workspace holds returns SKG_EUNSUPPORTED and launches
- *           nothing.  GEMM calls never allocate, free or synchronise, and
+ *           stream's workspace holds, or 4 GiB or more of partials, returns
+ *           SKG_EUNSUPPORTED and launches nothing.  GEMM calls never
+ *           allocate, free or synchronise, and
  *           which kernel runs does not depend on the workspace, on graph
  *           capture or on earlier calls (no host sync in the decode step:
  *           mstar PR #1102, "Verification"; every kernel served from graph
