@@ -74,6 +74,29 @@ __device__ __forceinline__ unsigned short f32_to_bf16(float f) {
   return static_cast<unsigned short>(u >> 16);
 }
 
+// Whether y takes 8-byte stores of four outputs: rows of a multiple of 4
+// outputs and an 8-byte aligned base (y itself needs only 2-byte alignment).
+__device__ __forceinline__ bool y_vec4(const void* y, int N) {
+  return (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
+}
+
+// y[row, n .. n+3] = bf16(v[0 .. 3]) for n a multiple of 4, each value rounded
+// once: a single 8-byte store when yvec and the row holds all four (a tile's
+// output fragment gives each lane four consecutive outputs of one row), else
+// one 2-byte store per output inside the row.
+__device__ __forceinline__ void store_y4(unsigned short* y, size_t row, int n, int N, bool yvec, const float (&v)[4]) {
+  if (yvec && n + 3 < N) {
+    uint2 pk;
+    pk.x = (unsigned)f32_to_bf16(v[0]) | ((unsigned)f32_to_bf16(v[1]) << 16);
+    pk.y = (unsigned)f32_to_bf16(v[2]) | ((unsigned)f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<uint2*>(y + row * N + n) = pk;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (n + e < N) y[row * N + n + e] = f32_to_bf16(v[e]);
+  }
+}
+
 __device__ __forceinline__ float silu_f32(float g) {
   // g * sigmoid(g) = g / (1 + e^-g); for very negative g, e^-g overflows to
   // +inf and the quotient is -0, the correctly signed limit.
@@ -603,21 +626,22 @@ __global__ __launch_bounds__(256) void tile_kernel(const Args a) {
   float scale = 1.0f;
   if constexpr (OP == OP_FP8T) scale = a.s0[0];
   unsigned short* y = static_cast<unsigned short*>(a.y);
+  const bool yvec = y_vec4(a.y, N);
 #pragma unroll
   for (int f = 0; f < FN; ++f)
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const int m = m_base + j * 16 + lr;
-      if (m >= M) continue;
+      const int n = nb + f * 16 + lq * 4;
+      if (m >= M || n >= N) continue;
+      float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int n = nb + f * 16 + lq * 4 + e;
-        if (n >= N) continue;
-        float v = acc[0][f][j][e];
-        if constexpr (OP == OP_GATED) v = silu_f32(v) * acc[G - 1][f][j][e];
-        if constexpr (OP == OP_FP8T) v *= scale;
-        y[(size_t)m * N + n] = f32_to_bf16(v);
+        v[e] = acc[0][f][j][e];
+        if constexpr (OP == OP_GATED) v[e] = silu_f32(v[e]) * acc[G - 1][f][j][e];
+        if constexpr (OP == OP_FP8T) v[e] *= scale;
       }
+      store_y4(y, (size_t)m, n, N, yvec, v);
     }
 }
 
@@ -1192,6 +1216,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
   }
 
   unsigned short* y = static_cast<unsigned short*>(a.y);
+  const bool yvec = y_vec4(a.y, N);
   float scale = 1.0f;
   if constexpr (BO == OP_FP8T) scale = a.s0[0];
   if constexpr (S == 1) {
@@ -1200,16 +1225,16 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
         const int m = m_base + j * 16 + lr;
-        if (!owner || m >= M) continue;
+        const int n = nb + f * 16 + lq * 4;
+        if (!owner || m >= M || n >= N) continue;
+        float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int n = nb + f * 16 + lq * 4 + e;
-          if (n >= N) continue;
-          float v = acc[0][f][j][e];
-          if constexpr (BO == OP_GATED) v = silu_f32(v) * acc[G - 1][f][j][e];
-          if constexpr (BO == OP_FP8T) v *= scale;
-          y[(size_t)m * N + n] = f32_to_bf16(v);
+          v[e] = acc[0][f][j][e];
+          if constexpr (BO == OP_GATED) v[e] = silu_f32(v[e]) * acc[G - 1][f][j][e];
+          if constexpr (BO == OP_FP8T) v[e] *= scale;
         }
+        store_y4(y, (size_t)m, n, N, yvec, v);
       }
   } else {
     // ---- split-K: store this split's partials (device-coherent), count in,
@@ -1278,6 +1303,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
             const int q = threadIdx.x + NT * (t0 + tb);
             const int m = m_base + q / QPR, n = n0 + 4 * (q % QPR);
             if (q >= Q || m >= M || n >= N) continue;
+            float o[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               float v = 0.0f, u = 0.0f;
@@ -1288,8 +1314,9 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
               }
               if constexpr (BO == OP_GATED) v = silu_f32(v) * u;
               if constexpr (BO == OP_FP8T) v *= scale;
-              y[(size_t)m * N + n + e] = f32_to_bf16(v);
+              o[e] = v;
             }
+            store_y4(y, (size_t)m, n, N, yvec, o);
           }
         }
       } else {

@@ -254,19 +254,8 @@ __global__ __launch_bounds__(64 * WM * WN) void mt_kernel(const Args a) {
 
   // ---- epilogue
   unsigned short* y = static_cast<unsigned short*>(a.y);
-  const bool yvec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(a.y) & 7) == 0;
-  auto store_y = [&](int m, int n, const float (&v)[4]) {
-    if (yvec && n + 3 < N) {
-      uint2 pk;
-      pk.x = (unsigned)f32_to_bf16(v[0]) | ((unsigned)f32_to_bf16(v[1]) << 16);
-      pk.y = (unsigned)f32_to_bf16(v[2]) | ((unsigned)f32_to_bf16(v[3]) << 16);
-      *reinterpret_cast<uint2*>(y + (size_t)m * N + n) = pk;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (n + e < N) y[(size_t)m * N + n + e] = f32_to_bf16(v[e]);
-    }
-  };
+  const bool yvec = y_vec4(a.y, N);
+  auto store_y = [&](int m, int n, const float (&v)[4]) { store_y4(y, (size_t)m, n, N, yvec, v); };
 
   if constexpr (S == 1) {
 #pragma unroll
