@@ -181,20 +181,26 @@ def test_a8w8_quant_codes_exact():
     wq[np.arange(N), np.arange(K)] = 0x38                     # identity in e4m3fn
     ws = np.ones((3, 3), np.float32)
     M = xb.shape[0]
-    xs = torch.full((M, 3), -1.0, device="cuda")
-    for variant in [None] + [n for i, n in enumerate(skg.variants("a8w8_quant"))
-                             if skg.skinny_gemm_variant_supports("a8w8_quant", i, M)][:6]:
-        say(f"a8w8_quant codes variant={variant}")
-        if variant is None:
-            y = skg.skinny_gemm_a8w8_block_quant(dev_bf16(xb), dev_fp8(wq), dev_f32(ws), x_scales=xs)
-        else:
-            y = skg.skinny_gemm_run_variant("a8w8_quant", variant, dev_bf16(xb), dev_fp8(wq), xs, dev_f32(ws))
-        torch.cuda.synchronize()
-        s = xs.cpu().numpy()
-        assert np.array_equal(s.view(np.uint32), scales.view(np.uint32)), f"scales ({variant})"
-        yv = oracle.dec_bf16(host_bits(y)) / np.repeat(s.astype(np.float64), 128, axis=1)
-        back = oracle.e4m3fn_rne_bits(yv)                     # the nearest grid point to y / s
-        assert np.array_equal(back, codes), f"codes ({variant}): {np.argwhere(back != codes)[:5]}"
+    w_rm = dev_fp8(wq)
+    w_pk = skg.skinny_gemm_pack_weight("a8w8_quant", w_rm)
+    # table dispatch and every variant, both weight layouts: the tiles that
+    # quantise through LDS and those that quantise each lane's x in registers
+    for op, w in (("a8w8_quant", w_rm), ("a8w8_quant_packed", w_pk)):
+        for variant in [None] + [n for i, n in enumerate(skg.variants(op)) if skg.skinny_gemm_variant_supports(op, i, M)]:
+            say(f"{op} codes variant={variant}")
+            xs = torch.full((M, 3), -1.0, device="cuda")
+            if variant is None and op == "a8w8_quant":
+                y = skg.skinny_gemm_a8w8_block_quant(dev_bf16(xb), w, dev_f32(ws), x_scales=xs)
+            elif variant is None:
+                y = skg.skinny_gemm_a8w8_block_quant_packed(dev_bf16(xb), w, dev_f32(ws), x_scales=xs)
+            else:
+                y = skg.skinny_gemm_run_variant(op, variant, dev_bf16(xb), w, xs, dev_f32(ws))
+            torch.cuda.synchronize()
+            s = xs.cpu().numpy()
+            assert np.array_equal(s.view(np.uint32), scales.view(np.uint32)), f"scales ({op} {variant})"
+            yv = oracle.dec_bf16(host_bits(y)) / np.repeat(s.astype(np.float64), 128, axis=1)
+            back = oracle.e4m3fn_rne_bits(yv)                     # the nearest grid point to y / s
+            assert np.array_equal(back, codes), f"codes ({op} {variant}): {np.argwhere(back != codes)[:5]}"
 
 
 def head_cols(N: int, seed: int) -> np.ndarray:
