@@ -200,9 +200,14 @@ constexpr unsigned long long mt_tiles(int FM, int FN, int WM, int WN, int M, int
 // Packed-weight stream (pg): RW weight rows per workgroup of KS waves, for
 // the packed bf16 and gated forms at the rows buckets up to 8.
 constexpr int kPgMaxM = 8;
+// VGPRs a lane needs (estimate): P rounds of the weight pieces and the x of
+// each row, the sums, and ~44 more.  With KS waves a SIMD holds KS/4 of them,
+// so the budget is 512 / (KS/4); past it the compiler spills.
+constexpr int pg_regs(int op, int MT, int P) { return 4 * P * (op_groups(op) + MT) + op_groups(op) * MT + 44; }
 constexpr bool pg_valid(int op, int MT, int RW, int KS, int P) {
   return op_packed(op) && (op_base(op) == OP_BF16 || op_base(op) == OP_GATED) && MT >= 1 && MT <= kPgMaxM &&
-         (RW == 2 || RW == 4 || RW == 8) && (KS == 4 || KS == 8 || KS == 16) && P >= 1 && P <= 4;
+         (RW == 2 || RW == 4 || RW == 8) && (KS == 4 || KS == 8 || KS == 16) && P >= 1 && P <= 4 &&
+         pg_regs(op, MT, P) <= 512 / (KS / 4);
 }
 
 // The MFMA tile path serves every rows bucket: rows past M inside a 16-row
