@@ -29,9 +29,9 @@
 #include "skinny_gemm.h"
 #include "table.hpp"
 
-// Split-K workspace layout (registered or static): kSplitCounters arrival
-// counters (one per output tile, zero between calls), then the fp32 partials
-// [S][G][M][N] of the call.
+// Split-K workspace layout (registered or static): kSplitCounters words of
+// split-K tile state (three per output tile, split_tile_state in
+// kernels.hpp), then the fp32 partials [S][G][M][N] of the call.
 constexpr size_t kCntBytes = (size_t)skg::kSplitCounters * sizeof(unsigned);
 // The static scratch of skinny_gemm_run_static: the counters and at most
 // kStaticPartialBytes of partials.  Each device that runs the library holds
@@ -48,7 +48,7 @@ __global__ void zero_kernel(unsigned short* y, size_t n) {
     y[i] = 0;
 }
 
-// Clears n words (the arrival counters of a workspace).  A kernel, not
+// Clears n words (the split-K tile state of a workspace).  A kernel, not
 // hipMemsetAsync, so that it is an ordinary node if a caller captures it.
 __global__ void zero_words_kernel(unsigned* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
@@ -354,7 +354,7 @@ LaunchFn variant_fn(int op, int v, int M) {
 }
 
 // Bytes of split-K partials variant v of op needs for M rows (0: none), and
-// whether its output tiles fit the arrival counters.
+// whether its output tiles fit the split-K tile state.
 size_t partial_bytes(int op, int v, int M, int N) {
   if (v < 0) return 0;
   if (kVariants[v].family == FAM_MT) return (size_t)tlds_ws_bytes(op, kVariants[v].p4, M, N);
@@ -365,11 +365,11 @@ bool tiles_fit(int op, int v, int M, int N) {
   (void)op;
   if (kVariants[v].family == FAM_MT) {
     const VariantDesc& d = kVariants[v];
-    return mt_tiles(d.p0, d.p1, d.p2, d.p3, M, N) <= (unsigned long long)kSplitCounters;
+    return mt_tiles(d.p0, d.p1, d.p2, d.p3, M, N) <= (unsigned long long)kSplitMaxTiles;
   }
   const int fm = M > kMaxBucket ? kNumTileFM - 1 : tile_fm_index(M);
   const VariantDesc& d = kVariants[v];
-  return tlds_tiles(d.p0, d.p4 / d.p5, tlds_fm(kTileFM[fm], d.p3), M, N) <= (unsigned long long)kSplitCounters;
+  return tlds_tiles(d.p0, d.p4 / d.p5, tlds_fm(kTileFM[fm], d.p3), M, N) <= (unsigned long long)kSplitMaxTiles;
 }
 
 // ------------------------------------------------- registered workspaces
@@ -451,7 +451,7 @@ bool g_static_cleared[kMaxDevices] = {};   // counters cleared by a launch outsi
 // This device's copy of `scratch`: its address is taken once per device with
 // that device current; the counters are cleared (stream-ordered, before the
 // call's kernel) until one clear has run outside graph capture, after which
-// every launch leaves them at zero.
+// every launch leaves them consistent for the next.
 skg_status static_scratch(hipStream_t s, char** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {

@@ -43,6 +43,8 @@ struct Args {
   float* ws;        // split-K partials [S][G][M][N] fp32 (tlds variants with S > 1)
   unsigned* cnt;    // split-K arrival counters, one per output tile, zero between calls
   float* xs_out;    // a8w8 with x quantised here: the x scales [M, kb] it computes, or NULL
+  int split_wait;   // split-K tiles: the whole grid fits on the device at once, so a
+                    // split's workgroup may wait (bounded) for the tile's other splits
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -104,6 +106,49 @@ __device__ __forceinline__ float silu_f32(float g) {
 }
 
 __device__ __forceinline__ u32x4 load_nt(const u32x4* p) { return __builtin_nontemporal_load(p); }
+
+// Split-K tile state (3 words of the workspace counters, laid out as
+// kSplitLines describes).  Word 0 counts arrivals over all launches: each
+// launch adds exactly 8 to it (its S arrivals, then 8 - S from the last to
+// arrive), so it is a multiple of 8 between launches, a launch's epoch is the
+// value over 8, and a workgroup's arrival rank is the value's low 3 bits.
+// Words 1 and 2 hold the slice claims of even and odd epochs; the last to
+// arrive clears the other one for the next launch.  Nothing needs a reset.
+__device__ __forceinline__ unsigned* split_tile_state(unsigned* cnt, unsigned tile) {
+  return cnt + (tile % kSplitLines) * 32 + (tile / kSplitLines) * 3;
+}
+
+// Arrive at a split-K tile (one thread of the workgroup, after its partials
+// are stored and complete): returns the tile's arrival word before this
+// arrival.  The last of the S arrivals also makes the launch's total 8 and
+// clears the claim word of the next epoch.
+template <int S>
+__device__ __forceinline__ unsigned split_arrive(unsigned* st) {
+  const unsigned old = __hip_atomic_fetch_add(st, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((old & 7u) == (unsigned)(S - 1)) {
+    if constexpr (S < 8) __hip_atomic_fetch_add(st, (unsigned)(8 - S), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(st + 1 + (((old >> 3) + 1u) & 1u), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return old;
+}
+
+// The longest a split-K workgroup waits for the other splits of its tile, in
+// ticks of the 100 MHz real-time counter (20 us): past it the last split to
+// arrive adds the slice instead.
+constexpr unsigned long long kSplitWaitTicks = 2000;
+
+// Workgroups of `kernel` (block threads, smem bytes of dynamic LDS) that the
+// current device holds at once: its occupancy per CU times the CUs, or 0 when
+// the runtime cannot tell.  A host query, no stream work.
+inline unsigned long long resident_workgroups(const void* kernel, int block, size_t smem) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, smem) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return (unsigned long long)cus * (unsigned long long)per_cu;
+}
 
 // Buffer resource over [p, p + bytes) for raw buffer loads/stores; cache
 // policy bit 4 (sc1) makes an access device-coherent across the XCDs' L2s.
@@ -1263,31 +1308,61 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
           }
         }
       }
-    __shared__ unsigned last;
     __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0): this thread's partial stores are done
     __syncthreads();
-    const unsigned tile = blockIdx.y * gridDim.x + blockIdx.x;
-    if (threadIdx.x == 0)
-      last = __hip_atomic_fetch_add(a.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (unsigned)(S - 1);
+    // Combine.  With S = 2 the last split to arrive adds the whole tile.  With
+    // S >= 4 the tile's outputs are cut into S slices; slice sl is added, all
+    // S partials in split order, by exactly one workgroup: split sl's own
+    // once it has seen all S arrivals (it waits for them at most
+    // kSplitWaitTicks, and only when the whole grid is resident at once),
+    // claiming the slice with an atomic OR on the epoch's claim word; the last
+    // to arrive adds its own slice and then claims, in one atomic OR, every
+    // slice not yet claimed.
+    constexpr bool DIST = S >= 4;
+    unsigned* const st = split_tile_state(a.cnt, blockIdx.y * gridDim.x + blockIdx.x);
+    __shared__ int comb_last, comb_mine, comb_rest;
+    if (threadIdx.x == 0) {
+      const unsigned old = split_arrive<S>(st);
+      const bool lst = (old & 7u) == (unsigned)(S - 1);
+      bool mine = lst;
+      if (DIST && !lst) {
+        bool ready = false;
+        if (a.split_wait) {
+          const unsigned base = old & ~7u;
+          const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+          do {
+            __builtin_amdgcn_s_sleep(1);
+            ready = __hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - base >= (unsigned)S;
+          } while (!ready && __builtin_amdgcn_s_memrealtime() - t0 < kSplitWaitTicks);
+        }
+        const unsigned bit = 1u << split;
+        mine = ready && !(__hip_atomic_fetch_or(st + 1 + ((old >> 3) & 1u), bit, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT) & bit);
+      }
+      comb_last = lst;
+      comb_mine = mine;
+      comb_rest = (int)((old >> 3) & 1u);       // the epoch's claim word
+    }
     __syncthreads();
-    if (last) {                                   // workgroup-uniform
-      constexpr int TW = 16 * FN * NG, TH = 16 * FM;
-      const int n0 = blockIdx.x * TW;
+    constexpr int TW = 16 * FN * NG, TH = 16 * FM;
+    constexpr int NSL = DIST ? S : 1;               // slices of the tile
+    const int n0 = blockIdx.x * TW;
+    // add slice sl: quads (4 outputs) [sl*QS, (sl+1)*QS) of the tile, thread t
+    // taking quads t, t + NT, ...; every load of a batch is issued before its sums
+    auto add_slice = [&](int sl) {
       if (vec) {
-        // quads of 4 outputs: thread t takes quads t, t + NT, ...; every load
-        // is issued before the sums
         constexpr int QPR = TW / 4;               // quads per tile row
-        constexpr int Q = TH * QPR;               // quads of the tile
-        constexpr int T = (Q + NT - 1) / NT;      // quads per thread
+        constexpr int QS = TH * QPR / NSL;        // quads of a slice (NSL divides 64 * FM * FN * NG)
+        constexpr int T = (QS + NT - 1) / NT;     // quads per thread
         constexpr int TB0 = 32 / (S * G);         // quads per batch: at most 128 registers in flight
         constexpr int TB = TB0 < 1 ? 1 : (TB0 > T ? T : TB0);
+        const int q0 = sl * QS;
 #pragma unroll
         for (int t0 = 0; t0 < T; t0 += TB) {
           f32x4 pv[TB][S][G];
 #pragma unroll
           for (int tb = 0; tb < TB; ++tb) {
-            const int q = min((int)threadIdx.x + NT * min(t0 + tb, T - 1), Q - 1);
+            const int q = q0 + min((int)threadIdx.x + NT * min(t0 + tb, T - 1), QS - 1);
             const int m = min(m_base + q / QPR, M - 1), n = min(n0 + 4 * (q % QPR), N - 4);
 #pragma unroll
             for (int sp = 0; sp < S; ++sp)
@@ -1300,9 +1375,10 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
 #pragma unroll
           for (int tb = 0; tb < TB; ++tb) {
             if (t0 + tb >= T) continue;
-            const int q = threadIdx.x + NT * (t0 + tb);
+            const int qi = threadIdx.x + NT * (t0 + tb);
+            const int q = q0 + qi;
             const int m = m_base + q / QPR, n = n0 + 4 * (q % QPR);
-            if (q >= Q || m >= M || n >= N) continue;
+            if (qi >= QS || m >= M || n >= N) continue;
             float o[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1320,8 +1396,10 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
           }
         }
       } else {
-        for (int e = threadIdx.x; e < TW * TH; e += NT) {
-          const int r = e / TW, cc = e - (e / TW) * TW;
+        constexpr int ES = TW * TH / NSL;         // outputs of a slice
+        for (int e = threadIdx.x; e < ES; e += NT) {
+          const int eo = sl * ES + e;
+          const int r = eo / TW, cc = eo - (eo / TW) * TW;
           const int m = m_base + r, n = n0 + cc;
           if (m >= M || n >= N) continue;
           const size_t i = (size_t)m * N + n;
@@ -1338,7 +1416,23 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
           y[i] = f32_to_bf16(v);
         }
       }
-      if (threadIdx.x == 0) __hip_atomic_store(a.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    if constexpr (!DIST) {
+      if (comb_last) add_slice(0);                // workgroup-uniform
+    } else {
+      if (comb_mine) add_slice(split);            // workgroup-uniform
+      if (comb_last) {
+        __syncthreads();                          // every thread has read comb_mine
+        if (threadIdx.x == 0) {
+          const unsigned others = ((1u << S) - 1u) & ~(1u << split);
+          comb_mine = (int)(others & ~__hip_atomic_fetch_or(st + 1 + comb_rest, others, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT));
+        }
+        __syncthreads();
+        const unsigned got = (unsigned)comb_mine;
+        for (int sl = 0; sl < S; ++sl)
+          if ((got >> sl) & 1u) add_slice(sl);
+      }
     }
   }
 }
@@ -1374,7 +1468,14 @@ hipError_t launch_tlds(const Args& a, hipStream_t s) {
   const unsigned gx = (unsigned)((a.N + TW - 1) / TW);
   const unsigned gy = (unsigned)((a.M + 16 * FM - 1) / (16 * FM));
   const size_t smem = (size_t)tlds_smem(OP, FM, FN, NW, KW, XD, P);
-  hipLaunchKernelGGL((tlds_kernel<OP, FM, FN, S, P, NW, KW, XD>), dim3(gx, gy, S), dim3(64 * NW), smem, s, a);
+  Args b = a;
+  if constexpr (S > 1) {
+    // the resident capacity of this kernel, taken once (all devices are gfx950)
+    static const unsigned long long cap =
+        resident_workgroups((const void*)&tlds_kernel<OP, FM, FN, S, P, NW, KW, XD>, 64 * NW, smem);
+    b.split_wait = (unsigned long long)gx * gy * S <= cap;
+  }
+  hipLaunchKernelGGL((tlds_kernel<OP, FM, FN, S, P, NW, KW, XD>), dim3(gx, gy, S), dim3(64 * NW), smem, s, b);
   return hipGetLastError();
 }
 

@@ -292,9 +292,8 @@ __global__ __launch_bounds__(64 * WM * WN) void mt_kernel(const Args a) {
     __shared__ unsigned last;
     __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): this thread's partial stores are done
     __syncthreads();
-    const unsigned tile = blockIdx.y * gridDim.x + blockIdx.x;
     if (threadIdx.x == 0)
-      last = __hip_atomic_fetch_add(a.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(S - 1);
+      last = (split_arrive<S>(split_tile_state(a.cnt, blockIdx.y * gridDim.x + blockIdx.x)) & 7u) == (unsigned)(S - 1);
     __syncthreads();
     if (last) {                                  // workgroup-uniform
       // the other splits' partials of FB fragments of W rows at a time (at
@@ -343,7 +342,6 @@ __global__ __launch_bounds__(64 * WM * WN) void mt_kernel(const Args a) {
             store_y(m, n, v);
           }
       }
-      if (threadIdx.x == 0) __hip_atomic_store(a.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

@@ -169,7 +169,12 @@ constexpr unsigned long long packed_weight_bytes(int op, int N, int K) {
 }
 // M fragments a tlds workgroup takes: the bucket's count, capped at MC.
 constexpr int tlds_fm(int FM, int MC) { return FM < MC ? FM : MC; }
-constexpr int kSplitCounters = 65536;   // arrival counters kept in the workspace
+constexpr int kSplitCounters = 65536;   // words of split-K tile state kept in the workspace
+// A split-K output tile's state is 3 words (arrivals, two claim words); tile t
+// sits in the 128-byte line t % kSplitLines, at word 3 * (t / kSplitLines) of
+// it, so tiles that run together queue their atomics on different lines.
+constexpr int kSplitLines = kSplitCounters / 32;
+constexpr int kSplitMaxTiles = kSplitLines * 10;
 
 // Two-operand LDS tile (mt): a workgroup of WM x WN waves owns BM = 16*FM*WM x
 // rows by BN = 16*FN*WN weight rows; each chunk (128 bytes of every row) of
@@ -293,7 +298,7 @@ constexpr const char kSpaceText[] =
 #define SKG_PG(name, RW, KS, P) "Q:" #name "," #RW "," #KS "," #P ";"
 #include "variants_pg.def"
 #undef SKG_PG
-    "kernels=18";  // bump when a kernel's arithmetic or indexing changes
+    "kernels=19";  // bump when a kernel's arithmetic or indexing changes
 constexpr uint32_t kSpaceToken = fnv1a(kSpaceText);
 
 }  // namespace skg

@@ -199,11 +199,11 @@ skg_status skinny_gemm_a8w8_block_quant_packed(const void* x, const void* W_pack
                                                int M, int N, int K, hipStream_t stream);
 
 /* ---- Split-K workspace ---------------------------------------------------
- * Layout: 256 KiB of arrival counters (65536 words, one per output tile of a
- * launch, each left at zero by the launch that used it), then the float32
- * partials [S][G][M][N] of the call (S = the variant's K split, G = 2 for the
- * gated form).  The counters are the only part that must start at zero; the
- * registration clears them. */
+ * Layout: 256 KiB of split-K tile state (65536 words: three per output tile
+ * of a launch, at most 20480 tiles; a launch leaves them consistent for the
+ * next), then the float32 partials [S][G][M][N] of the call (S = the
+ * variant's K split, G = 2 for the gated form).  The tile state is the only
+ * part that must start at zero; the registration clears it. */
 
 /* Bytes of split-K workspace the call (op, M, N, K) needs under the current
  * dispatch (table or default), or 0 when its kernel needs none (also 0 for an
@@ -239,7 +239,7 @@ skg_status skinny_gemm_set_device_workspace(void* workspace, size_t bytes, hipSt
  * the op's scale arrays, W = the packed weight for a packed op), result and
  * dispatch as the op's own entry point; it allocates nothing and needs no
  * registration.  The scratch is a static device array of the library, one
- * copy per device, held until the process ends: 256 KiB of counters and
+ * copy per device, held until the process ends: 256 KiB of split-K tile state and
  * skinny_gemm_static_scratch_bytes() (16 MiB) of partials.  A call whose
  * dispatch choice needs more partials returns SKG_EUNSUPPORTED and launches
  * nothing.  Every call on a device shares that device's scratch: calls that
