@@ -72,8 +72,10 @@ skg_status fail(skg_status st, const char* fmt, ...) {
 // ------------------------------------------------- process-wide settings
 // Read once: the dispatch override and the dispatch log.
 struct Settings {
-  int force = -1;    // $SKINNY_GEMM_FORCE as a variant index, or -1
-  bool log = false;  // $SKINNY_GEMM_LOG set and not "0"
+  int force = -1;          // $SKINNY_GEMM_FORCE as a variant index, or -1
+  bool log = false;        // $SKINNY_GEMM_LOG set and not "0"
+  bool split_wait = true;  // $SKINNY_GEMM_SPLIT_WAIT not "0": split-K workgroups may wait for
+                           // the tile's other splits (else the last to arrive adds every slice)
 };
 const Settings& settings() {
   static const Settings s = [] {
@@ -81,6 +83,8 @@ const Settings& settings() {
     t.force = forced_variant();
     const char* lg = std::getenv("SKINNY_GEMM_LOG");
     t.log = lg && *lg && *lg != '0';
+    const char* sw = std::getenv("SKINNY_GEMM_SPLIT_WAIT");
+    t.split_wait = !(sw && sw[0] == '0' && sw[1] == '\0');
     return t;
   }();
   return s;
@@ -533,6 +537,7 @@ Args make_args(int op, const void* x, const void* w, const float* s0, const floa
                int K, float* xs_out) {
   const int base = op_base(op);
   Args a{x, w, s0, s1, y, M, N, K, (K + 127) / 128, nullptr, nullptr, base == OP_A8W8Q ? xs_out : nullptr};
+  a.split_wait = settings().split_wait ? 0 : -1;   // the launch decides 1 or 0 unless waits are off
   if (base != OP_FP8T && base != OP_A8W8) a.s0 = nullptr;
   if (base != OP_A8W8 && base != OP_A8W8Q) a.s1 = nullptr;
   return a;

@@ -43,8 +43,9 @@ struct Args {
   float* ws;        // split-K partials [S][G][M][N] fp32 (tlds variants with S > 1)
   unsigned* cnt;    // split-K arrival counters, one per output tile, zero between calls
   float* xs_out;    // a8w8 with x quantised here: the x scales [M, kb] it computes, or NULL
-  int split_wait;   // split-K tiles: the whole grid fits on the device at once, so a
-                    // split's workgroup may wait (bounded) for the tile's other splits
+  int split_wait;   // split-K tiles: 1 when a split's workgroup may wait (bounded) for the
+                    // tile's other splits, i.e. the whole grid fits on the device at once;
+                    // set by the launch from 0, kept at -1 (never wait) when waits are off
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -1283,7 +1284,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
       }
   } else {
     // ---- split-K: store this split's partials (device-coherent), count in,
-    // and let the last workgroup of the tile combine them
+    // and combine them (below)
     const size_t MN = (size_t)M * N;
     const auto ws = buffer_rsrc(a.ws, (unsigned)((size_t)S * G * MN * 4));
     const bool vec = (N & 3) == 0;                // 16-byte partial rows
@@ -1327,7 +1328,7 @@ __global__ __launch_bounds__(64 * NW) void tlds_kernel(const Args a) {
       bool mine = lst;
       if (DIST && !lst) {
         bool ready = false;
-        if (a.split_wait) {
+        if (a.split_wait > 0) {
           const unsigned base = old & ~7u;
           const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
           do {
@@ -1473,7 +1474,7 @@ hipError_t launch_tlds(const Args& a, hipStream_t s) {
     // the resident capacity of this kernel, taken once (all devices are gfx950)
     static const unsigned long long cap =
         resident_workgroups((const void*)&tlds_kernel<OP, FM, FN, S, P, NW, KW, XD>, 64 * NW, smem);
-    b.split_wait = (unsigned long long)gx * gy * S <= cap;
+    b.split_wait = a.split_wait >= 0 && (unsigned long long)gx * gy * S <= cap;
   }
   hipLaunchKernelGGL((tlds_kernel<OP, FM, FN, S, P, NW, KW, XD>), dim3(gx, gy, S), dim3(64 * NW), smem, s, b);
   return hipGetLastError();

@@ -15,7 +15,7 @@ import torch
 
 import gemv_skinny_gemm_02_amd as skg
 import synth
-from gpu_util import _WS, assert_parity, ensure_workspace, host_bits, reference, run, say, to_device
+from gpu_util import _WS, assert_parity, ensure_workspace, host_bits, reference, run, run_packed, say, to_device, to_device_packed
 
 pytestmark = pytest.mark.gpu
 
@@ -225,3 +225,51 @@ def test_first_call_captured_in_a_fresh_process(tmp_path):
     assert "SAME" in r.stdout, r.stdout
     p = synth.make_bf16(M, N, K, seed=16)
     assert_parity(np.load(out), reference(p), f"captured first call M={M} N={N} K={K}")
+
+
+def test_split_slices_without_waits(tmp_path):
+    """Tiles that split K four or eight ways add each slice of a tile in the
+    split that owns it, after a bounded wait for the tile's other splits.
+    With the waits switched off ($SKINNY_GEMM_SPLIT_WAIT=0, read once per
+    process, so in a fresh one) the last split to arrive adds every slice
+    itself.  Both ways give the same bits, for every such variant of the
+    packed bf16 and gated forms, on N divisible by 4 (16-byte partial rows)
+    and not, and they pass the oracle."""
+    M = 64
+    shapes = [("bf16", 1024, 4096), ("bf16", 1030, 2048), ("gated", 512, 4096)]
+    cases = []
+    for kind, N, K in shapes:
+        op = kind + "_packed"
+        for i, n in enumerate(skg.variants(op)):
+            if n.startswith("tlds_") and ("_s4_" in n or "_s8_" in n) and skg.skinny_gemm_variant_supports(op, i, M):
+                cases.append((kind, N, K, n))
+    assert len(cases) >= 6
+    out = tmp_path / "nowait.npz"
+    script = textwrap.dedent(f"""
+        import sys
+        sys.path.insert(0, {ROOT!r}); sys.path.insert(0, {os.path.join(ROOT, 'tests')!r})
+        import numpy as np, torch
+        import gemv_skinny_gemm_02_amd as skg, synth
+        from gpu_util import to_device_packed, run_packed, host_bits
+        torch.cuda.set_device(0)
+        skg.skinny_gemm_set_device_workspace(64 << 20)
+        res = {{}}
+        for i, (kind, N, K, v) in enumerate({cases!r}):
+            p = getattr(synth, "make_" + kind)({M}, N, K, seed=21)
+            y = run_packed(p, to_device_packed(p), variant=v)
+            torch.cuda.synchronize()
+            res["c%d" % i] = host_bits(y)
+        np.savez({str(out)!r}, **res)
+        print("DONE", flush=True)
+    """)
+    say(f"split slices without waits: {len(cases)} cases in a fresh process")
+    env = dict(os.environ, SKINNY_GEMM_SPLIT_WAIT="0")
+    r = subprocess.run([sys.executable, "-c", script], capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "DONE" in r.stdout, r.stdout
+    nowait = np.load(out)
+    for i, (kind, N, K, v) in enumerate(cases):
+        p = getattr(synth, "make_" + kind)(M, N, K, seed=21)
+        y = host_bits(run_packed(p, to_device_packed(p), variant=v))
+        assert np.array_equal(y, nowait[f"c{i}"]), f"{kind} N={N} K={K} {v}: waits on/off differ"
+        assert_parity(y, reference(p), f"{kind} N={N} K={K} {v}")
