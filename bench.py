@@ -421,7 +421,6 @@ def measure_host_cost(torch, skg, x_dev, wp_dev, y_dev, stream, n=2000):
     MFMA measurement kernel) and for the packed bf16 call on 1024 x 1024 at
     M = 1, each through the Python binding and through the bare C entry
     point with its arguments prepared once."""
-    import ctypes
     lib = skg.load()
     sink = torch.zeros(256, dtype=torch.int32, device="cuda")
     M, N, K = 1, 1024, 1024

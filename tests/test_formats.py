@@ -6,7 +6,6 @@ import os
 from fractions import Fraction
 
 import numpy as np
-import pytest
 import torch
 
 from oracle import E4M3FN_TABLE, bf16_rne_bits, dec_bf16, dec_e4m3fn

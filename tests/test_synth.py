@@ -3,7 +3,6 @@ quantisation rules, and the sizes the pages print."""
 import os
 
 import numpy as np
-import torch
 
 import oracle
 import synth
