@@ -709,13 +709,15 @@ __global__ __launch_bounds__(256) void tile_kernel(const Args a) {
 //
 // Split-K (S > 1): every workgroup stores its fp32 partial tile with device-
 // coherent stores, waits for them to complete, and counts itself in the
-// tile's arrival counter.  The workgroup that arrives last reads the S
-// partials of the tile with device-coherent loads, adds them in split order
-// 0..S-1 -- the same order whichever workgroup is last, so the result is
-// reproducible -- applies the epilogue, stores y and resets the counter for the
-// next call.  Nothing waits on another workgroup.  (Device-coherent accesses
-// pass the per-XCD L2 coherently; a device-scope fence would instead write back
-// and invalidate the whole L2 under every co-resident workgroup.)
+// tile's arrival word (split_arrive).  With S = 2 the workgroup that arrives
+// last reads the S partials of the tile with device-coherent loads and adds
+// them in split order 0..S-1 -- the same order whichever workgroup adds, so
+// the result is reproducible -- applies the epilogue and stores y.  With S >= 4
+// each split adds one slice of the tile the same way, after a bounded wait
+// for the other arrivals, and the last to arrive adds any slice left
+// unclaimed.  (Device-coherent accesses pass the per-XCD L2 coherently; a
+// device-scope fence would instead write back and invalidate the whole L2
+// under every co-resident workgroup.)
 // A chunk is 128 bytes of every W row: 64 K for bf16 weights, 128 K for fp8
 // weights (for A8W8 also one 128-K scale group).  Its x rows are 128 bytes
 // (bf16 and fp8 x with 128-byte W rows) or 256 bytes (bf16 x with fp8 W).

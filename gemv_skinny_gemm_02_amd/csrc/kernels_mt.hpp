@@ -20,9 +20,9 @@
 //
 // Split-K (S > 1): as in the LDS tile path, each workgroup stores its fp32
 // partial tile with device-coherent stores, waits for them, counts itself in
-// the tile's arrival counter with a relaxed device-scope add, and the last
-// arriver adds the S partials in split order 0..S-1 (its own from registers),
-// stores y and resets the counter.
+// the tile's arrival word with a relaxed device-scope add (split_arrive), and
+// the last arriver adds the S partials in split order 0..S-1 (its own from
+// registers) and stores y.
 #pragma once
 
 #include "kernels.hpp"
