@@ -6,7 +6,8 @@
 // only device memory it touches beyond its arguments is the split-K workspace
 // that the caller registered (skinny_gemm_set_workspace) or, for
 // skinny_gemm_run_static, the library's static device scratch below.  Which
-// kernel runs is a pure function of (op, rows bucket, N, K, table).
+// kernel runs is a pure function of (op, rows bucket, N, K, table), and of M
+// past the last bucket.
 #include <dlfcn.h>
 
 #include <atomic>
@@ -188,14 +189,17 @@ const Snapshot* snapshot() {
 
 // The dispatch decision: the override, else the table entry of the rows
 // bucket, else the built-in default.  Every M of one rows bucket compiles to
-// the same kernels, so a decision depends on (op, bucket, N, K) only.
+// the same kernels, so a decision depends on (op, bucket, N, K) only; past
+// the last bucket it depends on M as well.
 Decision decide(int op, int M, int N, int K) {
   const Snapshot* snap = snapshot();
   const Settings& cfg = settings();
   const int b = bucket_of(M);                              // 0: above the last bucket
   const uint64_t key = ((uint64_t)(unsigned)op << 58) ^ ((uint64_t)(unsigned)b << 48) ^
                        ((uint64_t)(unsigned)N << 24) ^ (uint64_t)(unsigned)K;
-  const bool keyable = N < (1 << 24) && K < (1 << 24);
+  // (rows past the last bucket are not cached: there the default also
+  // depends on M, through the split-K tile limit)
+  const bool keyable = b != 0 && N < (1 << 24) && K < (1 << 24);
   {
     std::lock_guard<std::mutex> lk(snap->mu);
     if (keyable) {
@@ -367,13 +371,7 @@ size_t partial_bytes(int op, int v, int M, int N) {
 }
 bool tiles_fit(int op, int v, int M, int N) {
   (void)op;
-  if (kVariants[v].family == FAM_MT) {
-    const VariantDesc& d = kVariants[v];
-    return mt_tiles(d.p0, d.p1, d.p2, d.p3, M, N) <= (unsigned long long)kSplitMaxTiles;
-  }
-  const int fm = M > kMaxBucket ? kNumTileFM - 1 : tile_fm_index(M);
-  const VariantDesc& d = kVariants[v];
-  return tlds_tiles(d.p0, d.p4 / d.p5, tlds_fm(kTileFM[fm], d.p3), M, N) <= (unsigned long long)kSplitMaxTiles;
+  return split_tiles_fit(v, M, N);
 }
 
 // ------------------------------------------------- registered workspaces

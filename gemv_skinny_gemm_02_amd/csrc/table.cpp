@@ -470,6 +470,12 @@ int default_pick(int op, int M, int N, int K, bool allow_ws) {
 
 }  // namespace
 
-int default_variant(int op, int M, int N, int K) { return default_pick(op, M, N, K, true); }
+// A split-K choice whose output tiles would not fit the split-K tile state
+// (only at M far beyond the skinny range) gives way to the rule's no-split
+// choice, so the default always launches.
+int default_variant(int op, int M, int N, int K) {
+  const int v = default_pick(op, M, N, K, true);
+  return v >= 0 && !split_tiles_fit(v, M, N) ? default_pick(op, M, N, K, false) : v;
+}
 
 }  // namespace skg

@@ -277,6 +277,17 @@ constexpr bool variant_supports(int op, int i, int M) {
   return tile_valid(op, kTileFM[fm], v.p0, v.p1, v.p2);
 }
 
+// Whether variant i's output tiles at M rows and N outputs fit the split-K
+// tile state (kSplitMaxTiles); variants that do not split K always fit.
+constexpr bool split_tiles_fit(int i, int M, int N) {
+  const VariantDesc& d = kVariants[i];
+  if (d.family == FAM_MT)
+    return d.p4 == 1 || mt_tiles(d.p0, d.p1, d.p2, d.p3, M, N) <= (unsigned long long)kSplitMaxTiles;
+  if (d.family != FAM_TLDS || d.p1 == 1) return true;
+  const int fm = M > kMaxBucket ? kNumTileFM - 1 : tile_fm_index(M);
+  return tlds_tiles(d.p0, d.p4 / d.p5, tlds_fm(kTileFM[fm], d.p3), M, N) <= (unsigned long long)kSplitMaxTiles;
+}
+
 // FNV-1a over the list's text: the kernel-selection-space token.
 constexpr uint32_t fnv1a(const char* s, uint32_t h = 2166136261u) {
   for (; *s; ++s) h = (h ^ static_cast<uint8_t>(*s)) * 16777619u;

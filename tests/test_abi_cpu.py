@@ -270,3 +270,13 @@ def test_selection_token_names_the_buckets():
     buckets = tuple(int(v) for v in arr.replace("\n", " ").split(",") if v.strip())
     text = re.search(r'"buckets=([0-9,]+);', src).group(1)
     assert tuple(int(v) for v in text.split(",")) == buckets == skg.BUCKETS
+
+
+def test_default_split_falls_back_when_tiles_do_not_fit():
+    """The built-in default splits K across workgroups for mid-sized weights;
+    at M far beyond the skinny range its output tiles would outgrow the
+    split-K tile state (20480 tiles), and the default then takes the rule's
+    no-split choice instead of one the launch would refuse."""
+    for op in ("bf16", "bf16_packed", "gated", "a8w8_block"):
+        assert skg.skinny_gemm_workspace_bytes(op, 1024, 8192, 4096) > 0, op      # splits K
+        assert skg.skinny_gemm_workspace_bytes(op, 65536, 8192, 4096) == 0, op    # too many tiles to split
