@@ -191,9 +191,11 @@ constexpr int mt_copies_per_wave(int op, int FM, int FN, int WM, int WN) {
   const int blocks = 2 * FN * WN + 2 * FM * WM + (op_base(op) == OP_A8W8 ? FM * WM / 4 + 1 : 0);
   return (blocks + WM * WN - 1) / (WM * WN);
 }
+// A8W8 copies its x scales in blocks of 64 rows, so its x tile is a multiple
+// of 64 rows; the bf16 tile takes any number of 16-row fragments.
 constexpr bool mt_valid(int op, int FM, int FN, int WM, int WN, int S, int P) {
   return mt_op(op) && FM >= 1 && FN >= 1 && FM * FN <= 32 && (WM * WN == 4 || WM * WN == 8) &&
-         (FM * WM) % 4 == 0 && S >= 1 && S <= 8 && P >= 1 && P <= 4 &&
+         (op_base(op) != OP_A8W8 || (FM * WM) % 4 == 0) && S >= 1 && S <= 8 && P >= 1 && P <= 4 &&
          mt_lds_bytes(op, FM, FN, WM, WN, P) <= 160 * 1024 &&
          (P - 1) * mt_copies_per_wave(op, FM, FN, WM, WN) <= 63;
 }
