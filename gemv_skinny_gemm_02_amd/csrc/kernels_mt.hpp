@@ -11,12 +11,12 @@
 // both operands from LDS (v_mfma_f32_16x16x32_bf16 for bf16; for A8W8 one
 // v_mfma_f32_16x16x128_f8f6f4 per 128-K scale group, scaled into fp32).
 //
-// LDS stage: [W: BN rows x 128 B][x: BM rows x 128 B][A8W8: x scales BM x 4 B,
-// W block scales 64 x 4 B].  A fragment-packed W arrives as its 2 KiB units
-// (already in MFMA operand order: lane l reads 16 contiguous bytes); a
-// row-major operand arrives as 128-byte row segments whose 16-byte columns
-// are XOR-swizzled by (row / 2) % 8, so the 16 rows of a fragment read fall in
-// distinct bank groups.
+// LDS stage: [W: BN rows x 128 B][x: BM rows x 128 B][A8W8: x scales, 4 B per
+// row in blocks of 64 rows, then W block scales 64 x 4 B].  A fragment-packed
+// W arrives as its 2 KiB units (already in MFMA operand order: lane l reads 16
+// contiguous bytes); a row-major operand arrives as 128-byte row segments
+// whose 16-byte columns are XOR-swizzled by (row / 2) % 8, so the 16 rows of a
+// fragment read fall in distinct bank groups.
 //
 // Split-K (S > 1): as in the LDS tile path, each workgroup stores its fp32
 // partial tile with device-coherent stores, waits for them, counts itself in
@@ -77,7 +77,8 @@ __global__ __launch_bounds__(64 * WM * WN) void mt_kernel(const Args a) {
   constexpr int NSTG = P + 1;
   constexpr int WBLK = BN / 8;                   // 1 KiB copy blocks of W per chunk
   constexpr int XBLK = BM / 8;                   // 1 KiB copy blocks of x per chunk
-  constexpr int SBLK = A8 ? BM / 64 + 1 : 0;     // 256 B copy blocks of scales per chunk
+  constexpr int XSB = (BM + 63) / 64;            // 256 B blocks of x scales (64 rows each) per chunk
+  constexpr int SBLK = A8 ? XSB + 1 : 0;         // 256 B copy blocks of scales per chunk
   constexpr int NBLK = WBLK + XBLK + SBLK;
   constexpr int DPW = (NBLK + NW - 1) / NW;      // copies per wave per chunk
   constexpr int XOFF = BN * 128, SOFF = (BN + BM) * 128;
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mt_kernel(const Args a) {
         const int sbk = blk - WBLK - XBLK;       // x scales of rows 64*sbk + lane
         copy4_to_lds(a.s0 + (size_t)min(m0 + sbk * 64 + lane, M - 1) * kb + ck, sb + SOFF + sbk * 256);
       } else if (A8 && blk == NBLK - 1) {        // W block scales of 128-row blocks n0/128 + lane
-        copy4_to_lds(a.s1 + (size_t)min((n0 >> 7) + lane, ((N + 127) >> 7) - 1) * kb + ck, sb + SOFF + BM * 4);
+        copy4_to_lds(a.s1 + (size_t)min((n0 >> 7) + lane, ((N + 127) >> 7) - 1) * kb + ck, sb + SOFF + XSB * 256);
       } else {
         copy16_to_lds(static_cast<const char*>(a.x), lds + NSTG * STB);
       }
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mt_kernel(const Args a) {
         sx[j] = *reinterpret_cast<const float*>(sb + SOFF + ((wm * FM + j) * 16 + lr) * 4);
 #pragma unroll
       for (int f = 0; f < FN; ++f)
-        sw[f] = *reinterpret_cast<const float*>(sb + SOFF + BM * 4 +
+        sw[f] = *reinterpret_cast<const float*>(sb + SOFF + XSB * 256 +
                                                 (((n0 + (wn * FN + f) * 16) >> 7) - (n0 >> 7)) * 4);
       if (tail) {
 #pragma unroll

@@ -182,20 +182,18 @@ constexpr int kSplitMaxTiles = kSplitLines * 10;
 // bf16 and A8W8, row-major or fragment-packed weights.
 constexpr bool mt_op(int op) { return op_base(op) == OP_BF16 || op_base(op) == OP_A8W8; }
 constexpr int mt_stage_bytes(int op, int FM, int FN, int WM, int WN) {
-  return 128 * (16 * FM * WM + 16 * FN * WN) + (op_base(op) == OP_A8W8 ? 16 * FM * WM * 4 + 256 : 0);
+  return 128 * (16 * FM * WM + 16 * FN * WN) + (op_base(op) == OP_A8W8 ? (16 * FM * WM + 63) / 64 * 256 + 256 : 0);
 }
 constexpr int mt_lds_bytes(int op, int FM, int FN, int WM, int WN, int P) {
   return (P + 1) * mt_stage_bytes(op, FM, FN, WM, WN) + 1024;
 }
 constexpr int mt_copies_per_wave(int op, int FM, int FN, int WM, int WN) {
-  const int blocks = 2 * FN * WN + 2 * FM * WM + (op_base(op) == OP_A8W8 ? FM * WM / 4 + 1 : 0);
+  const int blocks = 2 * FN * WN + 2 * FM * WM + (op_base(op) == OP_A8W8 ? (FM * WM + 3) / 4 + 1 : 0);
   return (blocks + WM * WN - 1) / (WM * WN);
 }
-// A8W8 copies its x scales in blocks of 64 rows, so its x tile is a multiple
-// of 64 rows; the bf16 tile takes any number of 16-row fragments.
 constexpr bool mt_valid(int op, int FM, int FN, int WM, int WN, int S, int P) {
   return mt_op(op) && FM >= 1 && FN >= 1 && FM * FN <= 32 && (WM * WN == 4 || WM * WN == 8) &&
-         (op_base(op) != OP_A8W8 || (FM * WM) % 4 == 0) && S >= 1 && S <= 8 && P >= 1 && P <= 4 &&
+         S >= 1 && S <= 8 && P >= 1 && P <= 4 &&
          mt_lds_bytes(op, FM, FN, WM, WN, P) <= 160 * 1024 &&
          (P - 1) * mt_copies_per_wave(op, FM, FN, WM, WN) <= 63;
 }
