@@ -280,3 +280,22 @@ def test_default_split_falls_back_when_tiles_do_not_fit():
     for op in ("bf16", "bf16_packed", "gated", "a8w8_block"):
         assert skg.skinny_gemm_workspace_bytes(op, 1024, 8192, 4096) > 0, op      # splits K
         assert skg.skinny_gemm_workspace_bytes(op, 65536, 8192, 4096) == 0, op    # too many tiles to split
+
+
+def test_two_operand_tile_heights():
+    """The two-operand tile serves bf16 and A8W8 (both layouts) at every tile
+    height of whole 16-row fragments, 96-row tiles included (the A8W8 x
+    scales sit in LDS in blocks of 64 rows); the other forms never get it."""
+    names = skg.variants("bf16")
+    heights = set()
+    for i, n in enumerate(names):
+        m = re.fullmatch(r"mt_m(\d+)_f(\d+)_a(\d+)_b(\d+)_s(\d+)_p(\d+)", n)
+        if not m:
+            continue
+        fm, fn, wm, wn = (int(v) for v in m.groups()[:4])
+        heights.add(16 * fm * wm)
+        for op in ("bf16", "bf16_packed", "a8w8_block", "a8w8_block_packed"):
+            assert skg.skinny_gemm_variant_supports(op, i, 144), (op, n)
+        for op in ("gated", "gated_packed", "fp8_tensor", "fp8_tensor_packed", "a8w8_quant", "a8w8_quant_packed"):
+            assert not skg.skinny_gemm_variant_supports(op, i, 144), (op, n)
+    assert 96 in heights and 384 in heights and 128 in heights, sorted(heights)
