@@ -436,7 +436,11 @@ def variants(op=0) -> list:
 
 
 # ------------------------------------------------------ split-K workspace
-_HELD = []            # every workspace tensor registered through the binding
+# Every workspace tensor registered through the binding stays alive until the
+# process ends, also after another one replaces it: a graph captured while it
+# was registered keeps its address.  Register a workspace once per stream (or
+# device) and reuse it, rather than registering a new one per call.
+_HELD = []
 
 
 def _opi(op) -> int:
